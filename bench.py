@@ -1,0 +1,222 @@
+"""Benchmark one MoE-layer forward (route -> SERE -> capacity -> dispatch ->
+expert FFN -> combine) through the C ABI on one MI355X.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Default workload: the Qwen3-30B-A3B-shaped decode step at batch 128 with
+SERE K'=2, rho=0.5 (T=128, H=2048, N=128, top-8, I=768, bf16).  A step is one
+pass of the whole path over one batch; inputs are resident in HBM before the
+timed region.  Two copies of the expert weights alternate between steps so
+the weight stream is not served from the 256 MB Infinity Cache.
+
+Prints one JSON line: whole-layer tokens/s (value), ms per step, the
+roofline of the dominant kernel (HBM-bound gate-up GEMM for decode,
+MFMA-bound for prefill) timed with HIP events on the launch stream, and the
+CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+FP32_VALU_PEAK_TFLOPS = 157.3
+METRIC = ("MoE-layer tokens/s (prefill) + decode-step µs at B=128; "
+          "% of HBM/MFMA peak")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="qwen3_decode_b128")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--copies", type=int, default=2,
+                   help="weight copies rotated between steps")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def cpu_baseline(inp, budget_s):
+    """The oracle, untuned, over whole steps of the same workload until the
+    time budget is used (at least one step)."""
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    t0 = time.perf_counter()
+    n = 0
+    t_route = t_ffn = 0.0
+    while True:
+        a = time.perf_counter()
+        rt = O.layer_routing(inp)
+        b = time.perf_counter()
+        O.layer_outputs(inp, rt)
+        c = time.perf_counter()
+        t_route += b - a
+        t_ffn += c - b
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return dict(value=round(n * inp["T"] / el, 3), unit="tokens/s",
+                cores=int(cores), kind="oracle",
+                sample=(f"{n} full layer step(s) of the same workload "
+                        f"(T={inp['T']}): routing {t_route / n:.3f} s/step "
+                        f"single-threaded Python, FFN+combine "
+                        f"{t_ffn / n:.3f} s/step fp64 numpy"))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    from mixture_experts_layer_macs_amd import build as _build
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    from mixture_experts_layer_macs_amd import binding as B
+    from mixture_experts_layer_macs_amd import configs, synth
+    from mixture_experts_layer_macs_amd.staging import (elem_tensor, to_device,
+                                                        torch_elem_dtype)
+
+    wl = configs.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating inputs for {wl.name}", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(wl, args.seed)
+    d = to_device(inp, dev)
+    w13s = [d["w13"]] + [d["w13"].clone() for _ in range(args.copies - 1)]
+    w2s = [d["w2"]] + [d["w2"].clone() for _ in range(args.copies - 1)]
+    T, H, N, k, I, R = wl.T, wl.H, wl.N, wl.k, wl.I, wl.R
+    lay = B.Layer(T, H, N, k, I, R, torch_elem_dtype(wl.dtype), dev)
+    h = torch.empty((T * k, I), dtype=torch_elem_dtype(wl.dtype), device=dev)
+    decode = wl.kprime > 0 or T * k <= 32 * N
+
+    def step(i, ev=None):
+        w13, w2 = w13s[i % len(w13s)], w2s[i % len(w2s)]
+        B.moe_route(d["logits"], k, R, lay.topk_ids, lay.topk_gates, lay.fallback_ids)
+        slot_in = lay.topk_ids
+        if wl.kprime:
+            B.moe_sere_reroute(lay.topk_ids, N, wl.kprime, wl.rho, d["sim"],
+                               d["prot"], lay.slot_sere, lay.flags_sere)
+            slot_in = lay.slot_sere
+        B.moe_capacity_assign(lay.topk_ids, slot_in, lay.fallback_ids,
+                              d["is_visual"], d["entropy_w"], d["modality"], N,
+                              R, wl.group, wl.gamma, wl.lam, lay.ws_cap, lay.cap)
+        B.moe_dispatch(lay.cap["slot_out"], N, lay.ws_disp, lay.disp)
+        if ev is not None:
+            ev[0].record()
+        B.moe_ffn_gate_up(d["x"], lay.disp["row_token"],
+                          lay.disp["expert_offsets"], w13, k, h)
+        if ev is not None:
+            ev[1].record()
+        B.moe_ffn_down(h, lay.disp["expert_offsets"], w2, T, k, lay.out_rows)
+        if ev is not None:
+            ev[2].record()
+        B.moe_combine(lay.out_rows, lay.disp["slot_row"], lay.topk_gates, lay.y)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+           for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    print("[bench] timed steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(i, evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = start.elapsed_time(stop) / args.steps
+    gu_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    dn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+
+    off = lay.disp["expert_offsets"].cpu().numpy()
+    counts = np.diff(off)
+    M = int(off[-1])
+    U = int((counts > 0).sum())
+    el = 2 if wl.dtype == "bf16" else 4
+    stats = lay.cap["stats"].cpu().numpy()
+    topk = lay.topk_ids.cpu().numpy()
+    slot_sere = (lay.slot_sere if wl.kprime else lay.topk_ids).cpu().numpy()
+
+    if decode:
+        # gate-up kernel: every active expert's W13 once, its x rows, its h rows
+        gu_bytes = U * 2 * I * H * el + M * H * el + M * I * el
+        achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
+                    unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
+                    traffic=None, kernel="gate_up_swiglu",
+                    kernel_ms=round(gu_ms, 4), bytes_per_launch=int(gu_bytes))
+    else:
+        gu_flops = 2.0 * M * H * 2 * I
+        achieved = gu_flops / (gu_ms * 1e-3) / 1e12
+        peak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_VALU_PEAK_TFLOPS
+        roof = dict(bound="mfma" if wl.dtype == "bf16" else "alu",
+                    achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
+                    frac=round(achieved / peak, 4), traffic=None,
+                    kernel="gate_up_swiglu", kernel_ms=round(gu_ms, 4),
+                    flops_per_launch=gu_flops)
+
+    res = {
+        "metric": METRIC,
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "step_us": round(ms * 1e3, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded; random-init weights of the stated shape)",
+        "config": {
+            "workload": wl.name, "T": T, "H": H, "N": N, "k": k, "I": I,
+            "kprime": wl.kprime, "rho": wl.rho,
+            "gamma": "inf" if math.isinf(wl.gamma) else wl.gamma, "R": R,
+            "union_baseline": int(len(np.unique(topk))),
+            "union_sere": int(len(np.unique(slot_sere))),
+            "union_final": U, "kept_rows": M,
+            "dropped": int(stats[2]), "macs_rerouted": int(stats[3]),
+            "weight_copies": args.copies, "mode": "eager",
+        },
+        "roofline": roof,
+        "kernels_ms": {"gate_up_swiglu": round(gu_ms, 4),
+                       "down": round(dn_ms, 4)},
+        "wall_s": round(t_wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

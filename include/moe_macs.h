@@ -1,0 +1,236 @@
+/*
+ * moe_macs.h -- C ABI of the MI355X (gfx950) MoE-layer forward library.
+ *
+ * One mixture-of-experts layer, y(x) = sum_{j in Top-k(G(x))} G(x)_j E_j(x)
+ * ("MACS: Modality-Aware Capacity Scaling for Efficient Multimodal MoE
+ * Inference", §3.1 Eq. 1), wrapped in
+ *   - MACS capacity routing: entropy-weighted expert load (§3.2 Eq. 5-6),
+ *     modality-adaptive capacity from the effective visual ratio (§3.3
+ *     Eq. 7 and the expert modality indicator m_j), and re-route-else-drop
+ *     of overflowing tokens (§1 and Fig. 1);
+ *   - SERE re-routing (multi-image QA inference write-up, §4.1-§4.3): the
+ *     batch union of every token's top-K' primaries, secondary experts moved
+ *     onto the most similar primary above a threshold, gated by a per-layer
+ *     0/1 protection matrix.
+ *
+ * Call order on one stream (prefill skips moe_sere_reroute, since prefill
+ * keeps the original top-K):
+ *   moe_route -> moe_sere_reroute -> moe_capacity_assign -> moe_dispatch
+ *   -> moe_expert_ffn -> moe_combine
+ *
+ * Conventions shared by every entry point
+ *   - Every array argument is a DEVICE pointer owned by the caller; the
+ *     library never allocates, frees or keeps pointers after returning.
+ *   - Arrays are dense and row-major; "[T,k]" means T rows of k elements.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *     void*; NULL = the default stream).  No entry point synchronises with
+ *     the host or reads device memory from the host, so the sequence can be
+ *     captured in a HIP graph.
+ *   - Arguments are checked on the host before anything is enqueued.  On an
+ *     error nothing is enqueued and the call returns:
+ *        MOE_EINVAL  a required pointer is NULL or a size is out of range,
+ *        MOE_EUNSUP  unsupported element type,
+ *        MOE_EHIP    the HIP runtime reported a launch error.
+ *   - T == 0 is valid and enqueues nothing.
+ *   - Limits: 1 <= N <= 1024 experts, 1 <= k <= N, 0 <= R <= N - k,
+ *     T <= 2^20 tokens.
+ *   - Device data are not validated: router logits must be finite, expert
+ *     ids must lie in [0, N).
+ *   - Results are deterministic: no floating-point atomics; integer
+ *     reductions only where order cannot matter.
+ *
+ * Workspaces
+ *   moe_capacity_assign, moe_dispatch and moe_expert_ffn take a workspace of
+ *   at least the size their *_workspace_size() query returns.  The capacity
+ *   and dispatch workspaces hold a few control words: they must be filled
+ *   with zero bytes once, before their first use (e.g. allocated zeroed);
+ *   every call leaves those words zero again.  A workspace must not be
+ *   shared by calls that may run concurrently.
+ */
+#ifndef MOE_MACS_H
+#define MOE_MACS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { MOE_OK = 0, MOE_EINVAL = -1, MOE_EUNSUP = -2, MOE_EHIP = -3 };
+
+/* element type of x, expert weights, intermediates, out_rows and y */
+enum { MOE_F32 = 0, MOE_BF16 = 1 };
+
+/* flags[t,s] bits written by moe_sere_reroute / moe_capacity_assign */
+enum { MOE_FLAG_SERE = 1, MOE_FLAG_MACS = 2, MOE_FLAG_DROP = 4 };
+
+/* Fixed-point unit of token weights, loads and capacities: one full token. */
+#define MOE_WEIGHT_ONE 65536
+
+/*
+ * moe_route -- router softmax and top-k (MACS §3.1 Eq. 1).
+ *
+ * logits        f32[T,N]  router scores.
+ * topk_ids      i32[T,k]  out: experts ranked by logit descending; equal
+ *                         logits rank the lower expert index first, and
+ *                         -0.0 equals +0.0.
+ * topk_gates    f32[T,k]  out: G(x)_j = softmax over all N logits of the
+ *                         ranked expert (no renormalisation over the top-k).
+ * fallback_ids  i32[T,R]  out: ranks k+1..k+R, the overflow re-route
+ *                         candidates of moe_capacity_assign; may be NULL
+ *                         when R == 0.
+ */
+int moe_route(const float* logits, int T, int N, int k, int R,
+              int32_t* topk_ids, float* topk_gates, int32_t* fallback_ids,
+              void* stream);
+
+/*
+ * moe_sere_reroute -- SERE similarity-guided re-routing (multi-image QA
+ * write-up §4.1-§4.3), for decode batches.
+ *
+ * P is the union over the whole batch of every token's ranks 1..kprime.
+ * For each secondary slot (rank > kprime) whose expert e is not in P, let
+ * p* be the expert of P with the largest sim[e][p] (ties: lowest index).
+ * The slot moves to p* iff sim[e][p*] > rho (fp32 compare) and
+ * prot[e][p*] == 0; otherwise it keeps e.  Experts already in P never move.
+ * Gates are not touched: a moved slot keeps its original rank's gate.
+ *
+ * topk_ids     i32[T,k]  moe_route's output.
+ * sim          f32[N,N]  per-layer expert similarity, row = source expert.
+ * prot         u8[N,N]   per-layer protection, same layout as sim; nonzero
+ *                        forbids moving source e to target p.  A protected
+ *                        expert has an all-ones row.  Must be non-NULL (pass
+ *                        zeros for no protection).
+ * slot_expert  i32[T,k]  out: expert of every slot after re-routing.
+ * flags        u8[T,k]   out: MOE_FLAG_SERE on moved slots, else 0.
+ * Requires 1 <= kprime <= k.  One workgroup; the union bitset and the
+ * per-expert targets live in LDS.
+ */
+int moe_sere_reroute(const int32_t* topk_ids, int T, int N, int k, int kprime,
+                     float rho, const float* sim, const uint8_t* prot,
+                     int32_t* slot_expert, uint8_t* flags, void* stream);
+
+/*
+ * moe_capacity_assign -- MACS weighted load, modality-adaptive capacity and
+ * re-route-else-drop (MACS §3.1 Eq. 3, §3.2 Eq. 5-6, §3.3 Eq. 7, §1 Fig. 1).
+ *
+ * Token weight (fixed point, MOE_WEIGHT_ONE = 1.0): text tokens 1; visual
+ * tokens clamp(entropy_w, 0, 1) (NaN counts as 1), rounded half-to-even.
+ * R_v = (sum of visual weights) / (sum of all weights), or 1/2 if the sum
+ * is 0.  Capacity of expert j, each step one IEEE double operation:
+ *   C_j = max(((gamma*T)*k)/N * (1 + (lam*m_j)*(R_v - 0.5)), 1.0)
+ *   cap_q[j] = floor(C_j * MOE_WEIGHT_ONE)      (clamped at 2^62)
+ * Round 0: each expert keeps its proposers, in increasing (token, slot)
+ * order, while the inclusive running weight of all its proposers so far is
+ * <= cap_q.  Rounds r = 1..R: a token with an unplaced overflowed slot
+ * offers its lowest such slot to its rank k+r expert c when c had a
+ * round-0 proposer, c/group == e/group for the slot's expert e, and the
+ * token holds c in no slot; each expert admits the round's offers in token
+ * order by the same prefix rule against its remaining capacity.  Slots
+ * still unplaced after round R are dropped.  gamma = +inf disables
+ * capacity (everything kept).
+ *
+ * topk_ids      i32[T,k]  router ranking (for MOE_FLAG_SERE).
+ * slot_in       i32[T,k]  experts after SERE (or topk_ids when SERE is off);
+ *                         may equal slot_out (in place).
+ * fallback_ids  i32[T,R]  router ranks k+1..k+R; NULL allowed when R == 0.
+ * is_visual     u8[T]     nonzero = visual token.
+ * entropy_w     f32[T]    semantic weight of visual tokens (ignored for text).
+ * modality      i8[N]     m_j in {+1 visual, -1 text, 0 shared}.
+ * group         locality group size g (N = no restriction), 1 <= g <= N.
+ * slot_out      i32[T,k]  out: final expert, -1 = dropped.
+ * flags         u8[T,k]   out: MOE_FLAG_SERE | MOE_FLAG_MACS | MOE_FLAG_DROP.
+ * load_q        i64[N]    out: admitted weight per expert.
+ * cap_q         i64[N]    out: capacity per expert (INT64_MAX when off).
+ * stats         i64[4]    out: {sum of weights, sum of visual weights,
+ *                         dropped slots, MACS re-routed slots}.
+ * r_v           f64[1]    out: effective visual ratio R_v.
+ */
+size_t moe_capacity_workspace_size(int T, int N, int k);
+int moe_capacity_assign(const int32_t* topk_ids, const int32_t* slot_in,
+                        const int32_t* fallback_ids, const uint8_t* is_visual,
+                        const float* entropy_w, const int8_t* modality,
+                        int T, int N, int k, int R, int group,
+                        double gamma, double lam,
+                        int32_t* slot_out, uint8_t* flags, int64_t* load_q,
+                        int64_t* cap_q, int64_t* stats, double* r_v,
+                        void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
+ * moe_dispatch -- permutation of the kept slots into expert-major rows,
+ * ordered by (token, slot) inside each expert; feeds the grouped FFN.
+ *
+ * slot_expert     i32[T,k]   final experts, -1 = dropped.
+ * expert_offsets  i32[N+1]   out: rows of expert j are
+ *                            [expert_offsets[j], expert_offsets[j+1]);
+ *                            expert_offsets[N] = M, the number of kept slots.
+ * row_token       i32[T*k]   out: token of each row (first M valid).
+ * row_slot        i32[T*k]   out: slot of each row (first M valid).
+ * slot_row        i32[T,k]   out: row of each slot, -1 when dropped.
+ */
+size_t moe_dispatch_workspace_size(int T, int N, int k);
+int moe_dispatch(const int32_t* slot_expert, int T, int N, int k,
+                 int32_t* expert_offsets, int32_t* row_token,
+                 int32_t* row_slot, int32_t* slot_row,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_expert_ffn -- grouped SwiGLU expert FFN over the dispatched rows
+ * (MACS §3.1 Eq. 1, E_j(x) of every kept token-expert pair): for row r of
+ * expert j with token t = row_token[r],
+ *   h[r]        = silu(W1_j x_t) * (W3_j x_t),   silu(a) = a / (1 + e^-a)
+ *   out_rows[r] = W2_j h[r]
+ * The rows of x are gathered inside the GEMM; no permuted copy of x is made.
+ * M = expert_offsets[N] rows are computed; M is read on the device.
+ *
+ * x               [T,H]      activations (dtype).
+ * row_token       i32[T*k], expert_offsets i32[N+1]: moe_dispatch output.
+ * w13             [N,2I,H]   per expert: gate rows W1 (0..I-1), then up
+ *                            rows W3 (I..2I-1); each row H contiguous.
+ * w2              [N,H,I]    per expert down projection, each row I
+ *                            contiguous.
+ * out_rows        [T*k,H]    out: un-gated expert outputs, first M rows.
+ * dtype           MOE_F32 (fp32 FMA) or MOE_BF16 (bf16 MFMA with fp32
+ *                 accumulation; h and out_rows are rounded to bf16).
+ * The workspace holds h ([T*k, I] of dtype).
+ * Shapes: MOE_BF16 needs H % 256 == 0 and I % 128 == 0; MOE_F32 needs
+ * H % 4 == 0 and I % 4 == 0; otherwise MOE_EUNSUP.
+ *
+ * moe_ffn_gate_up and moe_ffn_down are the two halves of moe_expert_ffn
+ * (same arguments, h passed explicitly, [T*k, I] of dtype), for callers that
+ * schedule or time them separately.
+ */
+size_t moe_ffn_workspace_size(int T, int N, int k, int H, int I, int dtype);
+int moe_expert_ffn(const void* x, const int32_t* row_token,
+                   const int32_t* expert_offsets, const void* w13,
+                   const void* w2, int T, int N, int k, int H, int I,
+                   int dtype, void* out_rows,
+                   void* workspace, size_t workspace_bytes, void* stream);
+int moe_ffn_gate_up(const void* x, const int32_t* row_token,
+                    const int32_t* expert_offsets, const void* w13,
+                    int T, int N, int k, int H, int I, int dtype, void* h,
+                    void* stream);
+int moe_ffn_down(const void* h, const int32_t* expert_offsets, const void* w2,
+                 int T, int N, int k, int H, int I, int dtype, void* out_rows,
+                 void* stream);
+
+/*
+ * moe_combine -- gate-weighted combine (MACS §3.1 Eq. 1):
+ *   y[t] = sum over s = 0..k-1 with slot_row[t,s] >= 0 of
+ *          topk_gates[t,s] * out_rows[slot_row[t,s]]
+ * accumulated in fp32 in slot order, then stored in dtype.  Dropped slots
+ * contribute nothing and the remaining gates are not renormalised.
+ *
+ * out_rows [T*k,H] (dtype), slot_row i32[T,k], topk_gates f32[T,k],
+ * y [T,H] out (dtype).  Requires H % 8 == 0.
+ */
+int moe_combine(const void* out_rows, const int32_t* slot_row,
+                const float* topk_gates, int T, int k, int H, int dtype,
+                void* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MACS_H */

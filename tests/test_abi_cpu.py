@@ -1,0 +1,94 @@
+"""The C-ABI library without a GPU: it builds, loads, exports every entry
+point that include/moe_macs.h declares, answers workspace queries, and
+rejects bad arguments on the host before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_macs.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from mixture_experts_layer_macs_amd import build
+    if not os.path.exists(build.LIB):
+        build.build()
+    return ctypes.CDLL(build.LIB)
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_path():
+    names = declared()
+    for n in ("moe_route", "moe_sere_reroute", "moe_capacity_assign",
+              "moe_dispatch", "moe_expert_ffn", "moe_combine"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared():
+        assert hasattr(lib, name), name
+
+
+def test_binding_covers_every_symbol():
+    from mixture_experts_layer_macs_amd import binding  # loads on CPU too
+    assert set(binding._SIGS) == set(declared())
+
+
+def test_workspace_queries(lib):
+    for fn in ("moe_capacity_workspace_size", "moe_dispatch_workspace_size"):
+        f = getattr(lib, fn)
+        f.restype = ctypes.c_size_t
+        small, big = f(128, 128, 8), f(8192, 128, 8)
+        assert 0 < small < big
+        assert f(0, 128, 8) > 0 and f(-1, 128, 8) == 0
+    f = lib.moe_ffn_workspace_size
+    f.restype = ctypes.c_size_t
+    assert f(128, 128, 8, 2048, 768, 1) >= 128 * 8 * 768 * 2
+    assert f(128, 128, 8, 2048, 768, 0) >= 128 * 8 * 768 * 4
+
+
+def test_host_side_argument_errors(lib):
+    P = ctypes.c_void_p
+    fake = P(0x1000)   # never dereferenced: every call below fails its checks
+    lib.moe_route.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                              ctypes.c_int, P, P, P, P]
+    assert lib.moe_route(fake, 4, 0, 1, 0, fake, fake, None, None) == -1  # N<1
+    assert lib.moe_route(fake, 4, 8, 9, 0, fake, fake, None, None) == -1  # k>N
+    assert lib.moe_route(fake, 4, 8, 2, 7, fake, fake, fake, None) == -1  # R>N-k
+    assert lib.moe_route(fake, 4, 2048, 2, 0, fake, fake, None, None) == -1
+    assert lib.moe_route(None, 4, 8, 2, 0, fake, fake, None, None) == -1
+    assert lib.moe_route(fake, 4, 8, 2, 2, fake, fake, None, None) == -1
+    assert lib.moe_route(None, 0, 8, 2, 0, None, None, None, None) == 0   # T=0
+    lib.moe_sere_reroute.argtypes = [P, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                     P, P, P, P, P]
+    assert lib.moe_sere_reroute(fake, 4, 8, 2, 3, 0.5, fake, fake, fake, fake, None) == -1
+    assert lib.moe_sere_reroute(fake, 4, 8, 2, 0, 0.5, fake, fake, fake, fake, None) == -1
+    assert lib.moe_sere_reroute(fake, 4, 8, 2, 1, 0.5, fake, None, fake, fake, None) == -1
+    D = ctypes.c_double
+    lib.moe_capacity_assign.argtypes = (
+        [P] * 6 + [ctypes.c_int] * 5 + [D, D] + [P] * 7 + [ctypes.c_size_t, P])
+    args = [fake] * 6 + [4, 8, 2, 2, 8, 1.0, 1.0] + [fake] * 7
+    assert lib.moe_capacity_assign(*args, 0, None) == -1        # workspace short
+    bad_group = [fake] * 6 + [4, 8, 2, 2, 0, 1.0, 1.0] + [fake] * 7
+    assert lib.moe_capacity_assign(*bad_group, 1 << 20, None) == -1
+    bad_gamma = [fake] * 6 + [4, 8, 2, 2, 8, float("nan"), 1.0] + [fake] * 7
+    assert lib.moe_capacity_assign(*bad_gamma, 1 << 20, None) == -1
+    lib.moe_expert_ffn.argtypes = ([P] * 5 + [ctypes.c_int] * 6 + [P, P,
+                                   ctypes.c_size_t, P])
+    # bf16 needs H % 256 == 0 and I % 128 == 0
+    assert lib.moe_expert_ffn(fake, fake, fake, fake, fake, 4, 8, 2, 200, 768,
+                              1, fake, fake, 1 << 30, None) == -2
+    assert lib.moe_expert_ffn(fake, fake, fake, fake, fake, 4, 8, 2, 2048, 768,
+                              7, fake, fake, 1 << 30, None) == -2   # dtype
+    lib.moe_combine.argtypes = [P, P, P] + [ctypes.c_int] * 4 + [P, P]
+    assert lib.moe_combine(fake, fake, fake, 4, 2, 100, 1, fake, None) == -2
+    assert lib.moe_combine(None, fake, fake, 4, 2, 64, 1, fake, None) == -1

@@ -1,0 +1,199 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Integer outputs (expert ids, fallback ids, re-routed slots, flags, loads,
+capacities, R_v, dispatch maps) must match bit for bit; gates and the layer
+output y within the tolerances stated in gpu_util.  Inputs are the seeded
+workloads of the pages' shapes, small variants that still span several GEMM
+tiles with ragged tails, and adversarial routing cases (ties, +-0, forced
+overflow and drops, full protection, K' = k).  Full-size workloads compare
+the whole routing and a sample of output tokens that the oracle evaluates
+one by one.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from gpu_util import (assert_routing_equal, assert_y_close, load_binding,
+                      needs_gpu, run_gpu_layer, say)
+from mixture_experts_layer_macs_amd import configs, synth
+from oracle import moe_oracle as O
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    return load_binding()
+
+
+def _mid_bf16(**kw):
+    """Mid-size bf16 layer: several row and column tiles, ragged tails."""
+    base = configs.MM_PREFILL.with_(name="mid_bf16", T=600, H=512, N=16, k=4,
+                                    I=256, gamma=1.0, R=4, group=16)
+    return base.with_(**kw)
+
+
+FULL_Y_CASES = [
+    ("tiny_f32", configs.TINY_F32, 0),
+    ("tiny_f32_skew", configs.tiny_variants()["tiny_f32_skew"], 0),
+    ("tiny_f32_tight", configs.tiny_variants()["tiny_f32_tight"], 1),
+    ("tiny_f32_tight_r0", configs.tiny_variants()["tiny_f32_tight_r0"], 2),
+    ("mid_bf16_macs", _mid_bf16(), 0),
+    ("mid_bf16_tight", _mid_bf16(gamma=0.6, skew_expert0=2.0), 3),
+    ("mid_bf16_group4", _mid_bf16(gamma=0.8, group=4), 4),
+    ("mid_bf16_sere", _mid_bf16(kprime=2, n_protected=3, logits="zipf",
+                                gamma=math.inf), 5),
+    ("mid_bf16_small_decode", _mid_bf16(T=7, kprime=1, n_protected=2,
+                                        gamma=1.25), 6),
+    ("qwen3_decode_b128", configs.QWEN3_DECODE, 0),
+    ("qwen3_decode_b128_s1", configs.QWEN3_DECODE, 1),
+    ("sweep_layer_macs_b64", configs.SWEEP_LAYER.with_(T=64, kprime=2), 0),
+    ("sweep_layer_b1", configs.SWEEP_LAYER.with_(T=1, kprime=1), 0),
+]
+
+
+@pytest.mark.parametrize("name,wl,seed", FULL_Y_CASES, ids=[c[0] for c in FULL_Y_CASES])
+def test_layer_parity_all_tokens(name, wl, seed):
+    say(f"layer parity {name} seed={seed} T={wl.T} H={wl.H} N={wl.N} k={wl.k} I={wl.I}")
+    inp = synth.make_inputs(wl, seed)
+    rt = O.layer_routing(inp)
+    g = run_gpu_layer(inp)
+    assert_routing_equal(g, rt, inp)
+    y_ref = O.layer_outputs(inp, rt)
+    assert_y_close(g["y"], y_ref, wl.dtype)
+
+
+SAMPLED_CASES = [
+    ("mm_prefill_t8192", configs.MM_PREFILL, 0, 48),
+    ("mixtral_decode_t64", configs.MIXTRAL_DECODE, 0, 64),
+    ("mixtral_prefill_t4096", configs.MIXTRAL_PREFILL, 0, 24),
+]
+
+
+@pytest.mark.parametrize("name,wl,seed,n_tok", SAMPLED_CASES,
+                         ids=[c[0] for c in SAMPLED_CASES])
+def test_full_size_parity_sampled(name, wl, seed, n_tok):
+    say(f"full-size parity {name} T={wl.T} H={wl.H} N={wl.N} I={wl.I}")
+    inp = synth.make_inputs(wl, seed)
+    rt = O.layer_routing(inp)
+    g = run_gpu_layer(inp)
+    assert_routing_equal(g, rt, inp)
+    rng = np.random.default_rng(1234)
+    T = wl.T
+    toks = sorted(set(rng.choice(T, size=min(n_tok, T) - 2, replace=False).tolist())
+                  | {0, T - 1})
+    # make sure a dropped or re-routed token is among the samples when any
+    flagged = np.nonzero((rt["flags"] & (O.FLAG_DROP | O.FLAG_MACS)).any(axis=1))[0]
+    if len(flagged):
+        toks = sorted(set(toks) | {int(flagged[0]), int(flagged[-1])})
+    y_ref = O.layer_outputs(inp, rt, toks)
+    assert_y_close(g["y"][toks], y_ref, wl.dtype)
+
+
+ROUTING_CASES = [
+    ("mm_prefill_seed1", configs.MM_PREFILL, 1),
+    ("mm_prefill_tight", configs.MM_PREFILL.with_(gamma=0.5, R=2), 2),
+    ("mm_prefill_r0", configs.MM_PREFILL.with_(R=0), 3),
+    ("qwen3_prefill_sere_off", configs.QWEN3_DECODE.with_(T=2048, kprime=0,
+                                                          gamma=1.0), 0),
+    ("sweep_b256_k1", configs.SWEEP_LAYER.with_(T=256, kprime=1), 4),
+    ("sweep_b8_k2_vis09", configs.SWEEP_LAYER.with_(T=8, kprime=2,
+                                                    visual="frac:0.9"), 5),
+    ("n100_odd", configs.TINY_F32.with_(T=333, N=100, k=3, R=5, group=25,
+                                        gamma=0.7), 6),
+    ("n1024_wide", configs.TINY_F32.with_(T=40, N=1024, k=16, R=16,
+                                          group=1024, gamma=1.0), 7),
+    ("k1_many_tokens", configs.TINY_F32.with_(T=9000, N=8, k=1, R=3, gamma=0.9,
+                                              skew_expert0=3.0), 8),
+]
+
+
+@pytest.mark.parametrize("name,wl,seed", ROUTING_CASES, ids=[c[0] for c in ROUTING_CASES])
+def test_routing_parity(name, wl, seed):
+    say(f"routing parity {name} T={wl.T} N={wl.N} k={wl.k} R={wl.R}")
+    inp = synth.make_inputs(wl, seed, weights=False)
+    rt = O.layer_routing(inp)
+    g = run_gpu_layer(inp, tokens_out=False)
+    assert_routing_equal(g, rt, inp)
+
+
+def _adversarial_inputs(seed, T=96, N=12, k=4, R=3):
+    rng = np.random.default_rng(seed)
+    vals = np.array([-1.5, -0.0, 0.0, 0.25, 0.25, 1.0, 2.0], dtype=np.float32)
+    logits = vals[rng.integers(0, len(vals), size=(T, N))]
+    a = np.round(rng.uniform(0, 1, size=(N, N)) * 8) / 8
+    s = np.triu(a, 1)
+    sim = (s + s.T).astype(np.float32)
+    np.fill_diagonal(sim, 1.0)
+    ew = rng.choice([np.float32("nan"), -0.5, 0.0, 0.25, 0.5, 1.0, 1.5],
+                    size=T).astype(np.float32)
+    return dict(T=T, H=256, N=N, k=k, I=128, dtype="bf16", R=R, group=N,
+                gamma=0.8, lam=2.0, kprime=1, rho=0.5, logits=logits,
+                is_visual=(rng.uniform(size=T) < 0.6).astype(np.uint8),
+                entropy_w=ew,
+                modality=rng.integers(-1, 2, size=N).astype(np.int8),
+                sim=sim, prot=(rng.uniform(size=(N, N)) < 0.3).astype(np.uint8))
+
+
+ADV = ["ties", "all_protected", "kprime_eq_k", "rho_low", "no_sere", "cap_off"]
+
+
+@pytest.mark.parametrize("variant", ADV)
+def test_adversarial_routing(variant):
+    say(f"adversarial routing {variant}")
+    inp = _adversarial_inputs(100 + ADV.index(variant))
+    if variant == "all_protected":
+        inp["prot"][:] = 1
+    elif variant == "kprime_eq_k":
+        inp["kprime"] = inp["k"]
+    elif variant == "rho_low":
+        inp["rho"] = -1.0
+    elif variant == "no_sere":
+        inp["kprime"] = 0
+    elif variant == "cap_off":
+        inp["gamma"] = math.inf
+    rt = O.layer_routing(inp)
+    g = run_gpu_layer(inp, tokens_out=False)
+    assert_routing_equal(g, rt, inp)
+
+
+def test_deterministic_and_workspace_reuse():
+    """Two runs are bit-identical, and one workspace serves batches of
+    different sizes back to back (its control words reset themselves)."""
+    import torch
+    from mixture_experts_layer_macs_amd import binding as B
+    from mixture_experts_layer_macs_amd.staging import to_device
+    say("determinism + workspace reuse")
+    big = synth.make_inputs(configs.MM_PREFILL.with_(H=256, I=128), 0)
+    small = synth.make_inputs(configs.SWEEP_LAYER.with_(T=32, H=256, I=128,
+                                                        kprime=2), 0)
+    T, N, k = big["T"], big["N"], big["k"]
+    ws = B.new_workspace(max(B.moe_capacity_workspace_size(T, N, k), 1 << 20), "cuda")
+    wd = B.new_workspace(max(B.moe_dispatch_workspace_size(T, N, k), 1 << 20), "cuda")
+    results = []
+    for inp in (big, small, big, small):
+        d = to_device(inp, "cuda", weights=False)
+        ids, gates, fb = B.moe_route(d["logits"], inp["k"], inp["R"])
+        cap = B.moe_capacity_assign(ids, ids, fb, d["is_visual"], d["entropy_w"],
+                                    d["modality"], inp["N"], inp["R"],
+                                    inp["group"], inp["gamma"], inp["lam"], ws)
+        disp = B.moe_dispatch(cap["slot_out"], inp["N"], wd)
+        torch.cuda.synchronize()
+        results.append((cap["slot_out"].cpu().numpy(), cap["load_q"].cpu().numpy(),
+                        disp["slot_row"].cpu().numpy()))
+    for a, b in zip(results[0], results[2]):
+        np.testing.assert_array_equal(a, b)
+    for a, b in zip(results[1], results[3]):
+        np.testing.assert_array_equal(a, b)
+    rt = O.layer_routing(dict(small, kprime=0))
+    np.testing.assert_array_equal(results[1][0], rt["slot_expert"])
+
+
+def test_empty_batch_is_noop():
+    import torch
+    from mixture_experts_layer_macs_amd import binding as B
+    lib = B.library()
+    assert lib.moe_route(None, 0, 8, 2, 0, None, None, None, None) == 0
+    assert lib.moe_combine(None, None, None, 0, 2, 64, 1, None, None) == 0
+    torch.cuda.synchronize()
