@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--copies", type=int, default=2,
                    help="weight copies rotated between steps")
+    p.add_argument("--no-graph", action="store_true",
+                   help="skip the HIP-graph timed region")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     return p.parse_args()
@@ -154,6 +156,29 @@ def main():
     gu_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     dn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
 
+    # second timed region: the same step captured once per weight copy in a
+    # HIP graph and replayed (no host launch overhead between kernels)
+    graph_ms = None
+    if not args.no_graph:
+        graphs = []
+        cap_stream = torch.cuda.Stream()
+        for c in range(len(w13s)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap_stream):
+                step(c)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for i in range(args.steps):
+            graphs[i % len(graphs)].replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / args.steps
+
     off = lay.disp["expert_offsets"].cpu().numpy()
     counts = np.diff(off)
     M = int(off[-1])
@@ -181,15 +206,18 @@ def main():
                     kernel="gate_up_swiglu", kernel_ms=round(gu_ms, 4),
                     flops_per_launch=gu_flops)
 
+    best_ms = ms if graph_ms is None else min(ms, graph_ms)
     res = {
         "metric": METRIC,
-        "value": round(T / (ms * 1e-3), 1),
+        "value": round(T / (best_ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
-        "step_us": round(ms * 1e3, 2),
+        "ms_per_step": round(best_ms, 5),
+        "step_us": round(best_ms * 1e3, 2),
+        "eager_ms_per_step": round(ms, 5),
+        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -203,7 +231,8 @@ def main():
             "union_sere": int(len(np.unique(slot_sere))),
             "union_final": U, "kept_rows": M,
             "dropped": int(stats[2]), "macs_rerouted": int(stats[3]),
-            "weight_copies": args.copies, "mode": "eager",
+            "weight_copies": args.copies,
+            "mode": "eager" if graph_ms is None or ms <= graph_ms else "hip-graph",
         },
         "roofline": roof,
         "kernels_ms": {"gate_up_swiglu": round(gu_ms, 4),

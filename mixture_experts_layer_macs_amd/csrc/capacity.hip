@@ -25,6 +25,7 @@
 // fits one workgroup (decode), all rounds run in one launch.
 #include <math.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "common.h"
@@ -61,16 +62,17 @@ struct Args {
   int32_t* offer_s;    // [T]      offered slot this round (-1 = none)
   int32_t* offer_c;    // [T]      offered expert this round
   int32_t* part;       // [G*N]    per-block per-expert proposal weight
-  uint32_t* pact;      // [G*32]   per-block bitset of round-0 proposers
   int64_t* base;       // [G*N]    exclusive block prefix of part
-  int64_t* admg;       // [G*N]    per-block max admitted running weight
   int64_t* wsum;       // [G*4]    per-block {W, W_vis, dropped, rerouted}
   int64_t* capv;       // [N]
   int64_t* drem;       // [N]      capacity left for the pending round
-  int64_t* total;      // [N]      all round-0 proposal weight (cap off)
   uint8_t* active;     // [N]
-  unsigned* ticket;    // [1]
-  int TB, G;
+  // control words: zero between calls (each is cleared after its last use)
+  unsigned* ticket;                 // [1]
+  uint32_t* act_bits;               // [32]  experts with a round-0 proposer
+  unsigned long long* adm;          // [N]   max admitted running weight
+  unsigned long long* total;        // [N]   proposal weight (capacity off)
+  int TB, G, lds_scan;
 };
 
 __device__ __forceinline__ int32_t quant_weight(uint8_t vis, float w) {
@@ -124,7 +126,7 @@ __device__ void propose0(const Args& a, int g, int t0, int t1, int32_t* run,
              },
              a.incl_slot + static_cast<size_t>(t0) * k,
              a.part + static_cast<size_t>(g) * a.N, act_bits);
-  if (tid < 32) a.pact[g * 32 + tid] = act_bits[tid];
+  if (tid < 32 && act_bits[tid]) atomicOr(&a.act_bits[tid], act_bits[tid]);
 }
 
 // Offers of fallback round r >= 1: one per token with an unplaced overflow.
@@ -196,7 +198,7 @@ __device__ void apply(const Args& a, int r, int g, int t0, int t1,
   }
   __syncthreads();
   for (int e = tid; e < N; e += nthr)
-    a.admg[static_cast<size_t>(g) * N + e] = static_cast<int64_t>(amax[e]);
+    if (amax[e]) atomicMax(&a.adm[e], amax[e]);
 }
 
 __device__ void finalize_slots(const Args& a, int g, int t0, int t1,
@@ -228,7 +230,7 @@ __device__ void finalize_slots(const Args& a, int g, int t0, int t1,
 
 // Global step after round r's proposals (r <= R) or after the last apply
 // (r == R + 1).  Run by exactly one workgroup.
-__device__ void global_step(const Args& a, int r, int64_t* red) {
+__device__ void global_step(const Args& a, int r, int64_t* red, int32_t* lds) {
   const int tid = threadIdx.x, nthr = blockDim.x, N = a.N, G = a.G;
   __shared__ double s_rv;
   if (r == 0) {
@@ -255,32 +257,21 @@ __device__ void global_step(const Args& a, int r, int64_t* red) {
       a.capv[e] = c;
       a.cap_q[e] = c;
       a.drem[e] = c;
-      uint32_t act = 0;
-      for (int g = 0; g < G; ++g) act |= a.pact[g * 32 + (e >> 5)];
-      a.active[e] = (act >> (e & 31)) & 1u;
+      a.active[e] = (a.act_bits[e >> 5] >> (e & 31)) & 1u;
     }
+    __syncthreads();
+    if (tid < 32) a.act_bits[tid] = 0u;
   } else {
     for (int e = tid; e < N; e += nthr) {
-      int64_t m = 0;
-      for (int g = 0; g < G; ++g) {
-        const int64_t v = a.admg[static_cast<size_t>(g) * N + e];
-        m = v > m ? v : m;
-      }
+      const int64_t m = static_cast<int64_t>(a.adm[e]);
+      a.adm[e] = 0ull;
       const int64_t d = a.drem[e] - m;
       a.drem[e] = d;
       if (r > a.R) a.load_q[e] = a.capv[e] - d;
     }
   }
   if (r <= a.R) {
-    for (int e = tid; e < N; e += nthr) {
-      int64_t acc = 0;
-      for (int g = 0; g < G; ++g) {
-        const size_t j = static_cast<size_t>(g) * N + e;
-        const int64_t p = a.part[j];
-        a.base[j] = acc;
-        acc += p;
-      }
-    }
+    column_scan<int64_t>(a.part, a.base, nullptr, G, N, lds, a.lds_scan);
   } else {
     int64_t nd = 0, nm = 0;
     for (int g = tid; g < G; g += nthr) {
@@ -316,10 +307,9 @@ __device__ bool last_block(const Args& a) {
 __global__ __launch_bounds__(1024) void cap_kernel(Args a, int r_first,
                                                    int r_last) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int W = blockDim.x / MOE_WAVE;
-  int32_t* run = reinterpret_cast<int32_t*>(smem);
-  unsigned long long* amax =
-      reinterpret_cast<unsigned long long*>(smem + sizeof(int32_t) * W * a.N);
+  // [amax: N u64][run table / column-scan staging: lds_scan int32]
+  unsigned long long* amax = reinterpret_cast<unsigned long long*>(smem);
+  int32_t* run = reinterpret_cast<int32_t*>(smem + sizeof(unsigned long long) * a.N);
   __shared__ uint32_t act_bits[32];
   __shared__ int64_t red[16];
   const int g = blockIdx.x;
@@ -340,7 +330,7 @@ __global__ __launch_bounds__(1024) void cap_kernel(Args a, int r_first,
     } else {
       __syncthreads();
     }
-    global_step(a, r, red);
+    global_step(a, r, red, run);
     __syncthreads();
   }
 }
@@ -371,24 +361,27 @@ __global__ __launch_bounds__(1024) void cap_off_kernel(Args a) {
   w_all = block_sum_i64(w_all, red);
   w_vis = block_sum_i64(w_vis, red);
   __syncthreads();
-  for (int e = tid; e < N; e += nthr)
-    a.admg[static_cast<size_t>(g) * N + e] = static_cast<int64_t>(tot[e]);
   if (tid == 0) {
     a.wsum[g * 4 + 0] = w_all;
     a.wsum[g * 4 + 1] = w_vis;
   }
   if (a.G > 1) {
+    for (int e = tid; e < N; e += nthr)
+      if (tot[e]) atomicAdd(&a.total[e], tot[e]);
     if (!last_block(a)) return;
   } else {
     __syncthreads();
   }
-  int64_t W = 0, Wv = 0;
-  for (int b = tid; b < a.G; b += nthr) {
-    W += a.wsum[b * 4 + 0];
-    Wv += a.wsum[b * 4 + 1];
+  int64_t W = w_all, Wv = w_vis;
+  if (a.G > 1) {
+    W = Wv = 0;
+    for (int b = tid; b < a.G; b += nthr) {
+      W += a.wsum[b * 4 + 0];
+      Wv += a.wsum[b * 4 + 1];
+    }
+    W = block_sum_i64(W, red);
+    Wv = block_sum_i64(Wv, red);
   }
-  W = block_sum_i64(W, red);
-  Wv = block_sum_i64(Wv, red);
   if (tid == 0) {
     a.r_v[0] = W > 0 ? static_cast<double>(Wv) / static_cast<double>(W) : 0.5;
     a.stats[0] = W;
@@ -397,18 +390,30 @@ __global__ __launch_bounds__(1024) void cap_off_kernel(Args a) {
     a.stats[3] = 0;
   }
   for (int e = tid; e < N; e += nthr) {
-    int64_t s = 0;
-    for (int b = 0; b < a.G; ++b) s += a.admg[static_cast<size_t>(b) * N + e];
-    a.load_q[e] = s;
+    if (a.G > 1) {
+      a.load_q[e] = static_cast<int64_t>(a.total[e]);
+      a.total[e] = 0ull;
+    } else {
+      a.load_q[e] = static_cast<int64_t>(tot[e]);
+    }
     a.cap_q[e] = INT64_MAX;
   }
 }
 
 // ------------------------------------------------------------------ host
+// Workspace: a fixed control block (zero between calls, independent of T so
+// one workspace serves any batch size), then the per-call arrays.
+constexpr size_t CTRL_TICKET = 0;
+constexpr size_t CTRL_ACT = 256;
+constexpr size_t CTRL_ADM = 512;
+constexpr size_t CTRL_TOTAL = CTRL_ADM + 8 * 1024;
+constexpr size_t CTRL_BYTES = CTRL_TOTAL + 8 * 1024;
+constexpr int SCAN_LDS = 8192;  // int32 staging for the block-prefix scan
+
 struct Layout {
   int G, TB, threads;
-  size_t wq, cur, st, incl_slot, incl_tok, offer_s, offer_c, part, pact, base,
-      admg, wsum, capv, drem, total, active, ticket, bytes;
+  size_t wq, cur, st, incl_slot, incl_tok, offer_s, offer_c, part, base, wsum,
+      capv, drem, active, bytes;
 };
 
 static size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
@@ -425,14 +430,13 @@ static Layout layout(int T, int N, int k) {
     L.G = (T + L.TB - 1) / L.TB;
     L.threads = 256;
   }
-  size_t o = 0;
+  size_t o = CTRL_BYTES;
   auto take = [&](size_t n) {
     const size_t at = o;
     o = align_up(o + n);
     return at;
   };
   const size_t Tk = static_cast<size_t>(T) * k, GN = static_cast<size_t>(L.G) * N;
-  L.ticket = take(sizeof(unsigned));  // first: the word that must start at 0
   L.wq = take(sizeof(int32_t) * T);
   L.cur = take(sizeof(int32_t) * Tk);
   L.st = take(Tk);
@@ -441,13 +445,10 @@ static Layout layout(int T, int N, int k) {
   L.offer_s = take(sizeof(int32_t) * T);
   L.offer_c = take(sizeof(int32_t) * T);
   L.part = take(sizeof(int32_t) * GN);
-  L.pact = take(sizeof(uint32_t) * 32 * L.G);
   L.base = take(sizeof(int64_t) * GN);
-  L.admg = take(sizeof(int64_t) * GN);
   L.wsum = take(sizeof(int64_t) * 4 * L.G);
   L.capv = take(sizeof(int64_t) * N);
   L.drem = take(sizeof(int64_t) * N);
-  L.total = take(sizeof(int64_t) * N);
   L.active = take(N);
   L.bytes = o;
   return L;
@@ -516,15 +517,15 @@ extern "C" int moe_capacity_assign(
   a.offer_s = reinterpret_cast<int32_t*>(ws + L.offer_s);
   a.offer_c = reinterpret_cast<int32_t*>(ws + L.offer_c);
   a.part = reinterpret_cast<int32_t*>(ws + L.part);
-  a.pact = reinterpret_cast<uint32_t*>(ws + L.pact);
   a.base = reinterpret_cast<int64_t*>(ws + L.base);
-  a.admg = reinterpret_cast<int64_t*>(ws + L.admg);
   a.wsum = reinterpret_cast<int64_t*>(ws + L.wsum);
   a.capv = reinterpret_cast<int64_t*>(ws + L.capv);
   a.drem = reinterpret_cast<int64_t*>(ws + L.drem);
-  a.total = reinterpret_cast<int64_t*>(ws + L.total);
   a.active = reinterpret_cast<uint8_t*>(ws + L.active);
-  a.ticket = reinterpret_cast<unsigned*>(ws + L.ticket);
+  a.ticket = reinterpret_cast<unsigned*>(ws + CTRL_TICKET);
+  a.act_bits = reinterpret_cast<uint32_t*>(ws + CTRL_ACT);
+  a.adm = reinterpret_cast<unsigned long long*>(ws + CTRL_ADM);
+  a.total = reinterpret_cast<unsigned long long*>(ws + CTRL_TOTAL);
   a.TB = L.TB;
   a.G = L.G;
 
@@ -536,7 +537,8 @@ extern "C" int moe_capacity_assign(
     hipLaunchKernelGGL(cap_off_kernel, grid, block, lds, s, a);
     return launch_status();
   }
-  const size_t lds = sizeof(int32_t) * W * N + sizeof(unsigned long long) * N;
+  a.lds_scan = std::max(W * N, SCAN_LDS);
+  const size_t lds = sizeof(unsigned long long) * N + sizeof(int32_t) * a.lds_scan;
   if (lds > 65536 &&
       hipFuncSetAttribute(reinterpret_cast<const void*>(cap_kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize,

@@ -107,10 +107,13 @@ __device__ __forceinline__ uint64_t match_any(int key, int valid, int nbits) {
   return valid ? peers : 0ull;
 }
 
-__device__ __forceinline__ int bits_for(int n) {  // bits to hold 0..n-1
-  int b = 1;
-  while ((1 << b) < n) ++b;
-  return b;
+// Inverse of f32_order_key (-0.0 comes back as +0.0).
+__device__ __forceinline__ float f32_from_order_key(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+__device__ __forceinline__ float rank_key_value(uint64_t key) {
+  return f32_from_order_key(static_cast<uint32_t>(key >> 32));
 }
 
 __device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
@@ -196,6 +199,46 @@ __device__ inline void key_prefix(int n, int N, int nbits, int32_t* run, Get get
     if (key >= 0) incl[idx] += run[(idx / per) * N + key];
   }
   __syncthreads();
+}
+
+// Column-wise exclusive prefix of a [G][N] int32 matrix held in global
+// memory (one row per token block): excl[g][e] = sum_{g' < g} in[g'][e],
+// column totals to tot[e] (either output may be null).  Columns are staged
+// through LDS (lds: lds_elems int32) with batches of independent loads, so
+// the cost is a few memory round trips rather than one per block.
+template <class OutT>
+__device__ void column_scan(const int32_t* in, OutT* excl, OutT* tot, int G,
+                            int N, int32_t* lds, int lds_elems) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int EC = max(1, min(N, lds_elems / max(G, 1)));
+  for (int e0 = 0; e0 < N; e0 += EC) {
+    const int ec = min(EC, N - e0);
+    const int n = G * ec;
+    for (int i0 = tid; i0 < n; i0 += nthr * 8) {
+      int32_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * nthr;
+        v[u] = i < n ? in[static_cast<size_t>(i / ec) * N + e0 + i % ec] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * nthr;
+        if (i < n) lds[i] = v[u];
+      }
+    }
+    __syncthreads();
+    for (int c = tid; c < ec; c += nthr) {
+      OutT acc = 0;
+      for (int g = 0; g < G; ++g) {
+        const int32_t p = lds[g * ec + c];
+        if (excl) excl[static_cast<size_t>(g) * N + e0 + c] = acc;
+        acc += p;
+      }
+      if (tot) tot[e0 + c] = acc;
+    }
+    __syncthreads();
+  }
 }
 
 }  // namespace moe

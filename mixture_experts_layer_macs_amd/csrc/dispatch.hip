@@ -8,6 +8,8 @@
 // workgroup to finish turns the per-block counts into expert offsets and
 // per-block bases, and a second launch scatters the row maps.  A batch that
 // fits one workgroup does everything in a single launch.
+#include <algorithm>
+
 #include "common.h"
 
 namespace moe {
@@ -22,9 +24,9 @@ struct Args {
   int32_t* slot_row;
   int32_t* rank;   // [T*k]  1-based rank of the slot inside its block/expert
   int32_t* part;   // [G*N]  per-block per-expert counts
-  int32_t* base;   // [G*N]  first row of each block's share of each expert
+  int32_t* base;   // [G*N]  rows of each expert in earlier blocks
   unsigned* ticket;
-  int TB, G;
+  int TB, G, lds_scan;
 };
 
 __device__ void count_block(const Args& a, int g, int t0, int t1,
@@ -40,16 +42,12 @@ __device__ void count_block(const Args& a, int g, int t0, int t1,
              a.part + static_cast<size_t>(g) * a.N, nullptr);
 }
 
-// Expert offsets = exclusive scan of the per-expert totals; block bases.
-__device__ void scan_offsets(const Args& a, int32_t* tot) {
+// Expert offsets = exclusive scan of the per-expert totals; per-block bases
+// (exclusive prefix over the blocks, without the expert offset).
+__device__ void scan_offsets(const Args& a, int32_t* tot, int32_t* stage) {
   const int tid = threadIdx.x, nthr = blockDim.x, N = a.N, G = a.G;
-  for (int e = tid; e < N; e += nthr) {
-    int32_t s = 0;
-    for (int g = 0; g < G; ++g) s += a.part[static_cast<size_t>(g) * N + e];
-    tot[e] = s;
-  }
-  __syncthreads();
-  // chunked block scan over N <= 1024 values, carried between chunks
+  column_scan<int32_t>(a.part, a.base, tot, G, N, stage, a.lds_scan);
+  // chunked block scan over the N totals, carried between chunks
   __shared__ int32_t wsum[16];
   __shared__ int32_t carry;
   if (tid == 0) carry = 0;
@@ -63,7 +61,8 @@ __device__ void scan_offsets(const Args& a, int32_t* tot) {
     __syncthreads();
     int32_t pre = carry;
     for (int i = 0; i < wave; ++i) pre += wsum[i];
-    if (e < N) tot[e] = pre + inc - v;  // exclusive
+    if (e < N) a.offsets[e] = pre + inc - v;  // exclusive
+    if (e == N - 1) a.offsets[N] = pre + inc;
     __syncthreads();
     if (tid == nthr - 1) {
       int32_t s = carry;
@@ -71,17 +70,6 @@ __device__ void scan_offsets(const Args& a, int32_t* tot) {
       carry = s;
     }
     __syncthreads();
-  }
-  for (int e = tid; e < N; e += nthr) {
-    int32_t acc = tot[e];
-    a.offsets[e] = acc;
-    for (int g = 0; g < G; ++g) {
-      const size_t j = static_cast<size_t>(g) * N + e;
-      const int32_t p = a.part[j];
-      a.base[j] = acc;
-      acc += p;
-    }
-    if (e == N - 1) a.offsets[N] = acc;
   }
 }
 
@@ -94,7 +82,7 @@ __device__ void scatter_block(const Args& a, int g, int t0, int t1) {
       a.slot_row[i] = -1;
       continue;
     }
-    const int row = base[e] + a.rank[i] - 1;
+    const int row = a.offsets[e] + base[e] + a.rank[i] - 1;
     a.slot_row[i] = row;
     a.row_token[row] = i / k;
     a.row_slot[row] = i % k;
@@ -105,8 +93,9 @@ __device__ void scatter_block(const Args& a, int g, int t0, int t1) {
 __global__ __launch_bounds__(1024) void dispatch_kernel(Args a, int phase_first,
                                                         int phase_last) {
   extern __shared__ __align__(16) unsigned char smem[];
-  int32_t* run = reinterpret_cast<int32_t*>(smem);
-  int32_t* tot = run + (blockDim.x / MOE_WAVE) * a.N;
+  // [tot: N int32][run table / scan staging: lds_scan int32]
+  int32_t* tot = reinterpret_cast<int32_t*>(smem);
+  int32_t* run = tot + a.N;
   __shared__ int s_last;
   const int g = blockIdx.x;
   const int t0 = g * a.TB, t1 = min(a.T, t0 + a.TB);
@@ -123,7 +112,7 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(Args a, int phase_first,
       if (!s_last) return;
       __threadfence();
     }
-    scan_offsets(a, tot);
+    scan_offsets(a, tot, run);
     __syncthreads();
   }
   if (phase_last == 1) scatter_block(a, g, t0, t1);
@@ -207,7 +196,8 @@ extern "C" int moe_dispatch(const int32_t* slot_expert, int T, int N, int k,
   a.ticket = reinterpret_cast<unsigned*>(ws + L.ticket);
   a.TB = L.TB;
   a.G = L.G;
-  const size_t lds = sizeof(int32_t) * ((L.threads / MOE_WAVE) * N + N);
+  a.lds_scan = std::max((L.threads / MOE_WAVE) * N, 8192);
+  const size_t lds = sizeof(int32_t) * (N + a.lds_scan);
   if (lds > 65536 &&
       hipFuncSetAttribute(reinterpret_cast<const void*>(dispatch_kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize,

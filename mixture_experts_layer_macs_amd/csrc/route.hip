@@ -55,7 +55,9 @@ __global__ __launch_bounds__(256) void route_kernel(
     if (lane == 0) {
       if (r < k) {
         topk_ids[static_cast<size_t>(t) * k + r] = e;
-        topk_gates[static_cast<size_t>(t) * k + r] = expf(row[e] - mx) / se;
+        // the winning logit is recovered from its key: no reload
+        topk_gates[static_cast<size_t>(t) * k + r] =
+            expf(rank_key_value(best) - mx) / se;
       } else {
         fallback_ids[static_cast<size_t>(t) * R + (r - k)] = e;
       }

@@ -33,7 +33,6 @@ __global__ __launch_bounds__(1024) void sere_kernel(
   }
   __syncthreads();
 
-  const int nsec = k - kprime;
   const long total = static_cast<long>(T) * k;
   for (long i = tid; i < total; i += nthr) {
     const int s = static_cast<int>(i % k);
@@ -45,29 +44,44 @@ __global__ __launch_bounds__(1024) void sere_kernel(
   }
   __syncthreads();
 
-  const int wave = tid / MOE_WAVE, lane = lane_id();
-  const int nwaves = nthr / MOE_WAVE;
-  for (int e = wave; e < N; e += nwaves) {
-    const bool e_in_p = (in_p[e >> 5] >> (e & 31)) & 1u;
-    const bool e_sec = (is_sec[e >> 5] >> (e & 31)) & 1u;
-    int tgt = e;
-    if (e_sec && !e_in_p && nsec > 0) {
+  // 8 lanes per source expert, nthr/8 experts in flight per pass; each
+  // lane scans every 8th candidate of the similarity row, then the 8 lanes
+  // combine their best keys with three xor-shuffles.
+  constexpr int LPE = 8;
+  const int sub = tid % LPE;
+  for (int e0 = 0; e0 < N; e0 += nthr / LPE) {
+    const int e = e0 + tid / LPE;
+    bool want = false;
+    if (e < N) {
+      const bool e_in_p = (in_p[e >> 5] >> (e & 31)) & 1u;
+      const bool e_sec = (is_sec[e >> 5] >> (e & 31)) & 1u;
+      want = e_sec && !e_in_p;
+    }
+    uint64_t best = 0ull;
+    if (want) {
       const float* srow = sim + static_cast<size_t>(e) * N;
-      uint64_t best = 0ull;
-      for (int p = lane; p < N; p += MOE_WAVE) {
+#pragma unroll 4
+      for (int p = sub; p < N; p += LPE) {
         if ((in_p[p >> 5] >> (p & 31)) & 1u) {
           const uint64_t key = rank_key(srow[p], p);
           best = key > best ? key : best;
         }
       }
-      best = wave_max_u64(best);
-      if (best != 0ull) {
-        const int ps = rank_key_index(best);
-        const float vs = srow[ps];
-        if (vs > rho && prot[static_cast<size_t>(e) * N + ps] == 0) tgt = ps;
-      }
     }
-    if (lane == 0) target[e] = static_cast<int16_t>(tgt);
+#pragma unroll
+    for (int off = LPE / 2; off > 0; off >>= 1) {
+      const uint64_t o = shfl_u64(best, lane_id() ^ off);
+      best = o > best ? o : best;
+    }
+    if (e < N && sub == 0) {
+      int tgt = e;
+      if (want && best != 0ull) {
+        const int ps = rank_key_index(best);
+        if (rank_key_value(best) > rho && prot[static_cast<size_t>(e) * N + ps] == 0)
+          tgt = ps;
+      }
+      target[e] = static_cast<int16_t>(tgt);
+    }
   }
   __syncthreads();
 

@@ -197,3 +197,41 @@ def test_empty_batch_is_noop():
     assert lib.moe_route(None, 0, 8, 2, 0, None, None, None, None) == 0
     assert lib.moe_combine(None, None, None, 0, 2, 64, 1, None, None) == 0
     torch.cuda.synchronize()
+
+
+def test_graph_replay_matches_eager():
+    """The whole six-call sequence captured in a HIP graph: every replay,
+    with eager work and synchronisations in between, reproduces the eager
+    result bit for bit."""
+    import torch
+    from mixture_experts_layer_macs_amd import binding as B
+    from mixture_experts_layer_macs_amd.staging import to_device, torch_elem_dtype
+    wl = configs.SWEEP_LAYER.with_(T=96, H=512, I=256, kprime=2, gamma=0.8)
+    say("graph replay vs eager")
+    inp = synth.make_inputs(wl, 3)
+    d = to_device(inp, "cuda")
+    lay = B.Layer(wl.T, wl.H, wl.N, wl.k, wl.I, wl.R, torch_elem_dtype(wl.dtype))
+    args = (d["logits"], d["x"], d["w13"], d["w2"], d["is_visual"],
+            d["entropy_w"], d["modality"], d["sim"], d["prot"], wl.kprime,
+            wl.rho, wl.gamma, wl.lam, wl.group)
+    lay.forward(*args)
+    torch.cuda.synchronize()
+    ref_y = lay.y.clone()
+    ref_slot = lay.cap["slot_out"].clone()
+    ref_row = lay.disp["slot_row"].clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=s):
+        lay.forward(*args)
+    for i in range(4):
+        lay.y.zero_()
+        lay.cap["slot_out"].fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(lay.y, ref_y), f"replay {i}: y"
+        assert torch.equal(lay.cap["slot_out"], ref_slot), f"replay {i}: slots"
+        assert torch.equal(lay.disp["slot_row"], ref_row), f"replay {i}: rows"
+        lay.forward(*args)           # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(lay.y, ref_y)
