@@ -29,8 +29,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 enum { GATEUP = 0, DOWN = 1 };
-constexpr int BK = 64;
 constexpr int NT = 256;
+// LDS chunk swizzle: 0 = by row (bank rows of 128 bytes), 1 = by the row's
+// position among the rows that share a 256-byte bank row.
+#ifndef MOE_SWZ_MODE
+#define MOE_SWZ_MODE 0
+#endif
 
 struct Args {
   const uint16_t* a;       // GATEUP: x [T,H]; DOWN: h [T*k, I]
@@ -98,17 +102,27 @@ __device__ bool find_tile(const Args& a, int* cum, int& j, int& m0, int& nt,
   return true;
 }
 
-template <int MODE, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(NT) void gemm_kernel(Args a) {
+// One (expert, row tile, column tile) per workgroup of 4 waves arranged
+// WM x WN; each wave owns a (BM/WM) x (BN/WN) block of the C tile made of
+// 32x32 MFMA fragments (accumulators live in AGPRs).  K advances in BK
+// slices through two LDS buffers; the next slice is fetched into registers
+// while the current one feeds the MFMAs.
+template <int MODE, int BM, int BN, int BK, int WM, int WN>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void gemm_kernel(Args a) {
   static_assert(WM * WN == NT / MOE_WAVE, "4 waves");
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
   static_assert(FM >= 1 && FN >= 1, "fragment grid");
   static_assert(MODE == DOWN || FN % 2 == 0, "gate/up pairs");
   constexpr int CPR = BK / 8;               // 16-byte chunks per tile row
+  constexpr int SWZ = CPR - 1;              // chunk swizzle mask
+  constexpr int SWS = MOE_SWZ_MODE == 0 ? 0 : (BK == 64 ? 1 : (BK == 32 ? 2 : 0));
+  // LDS row r stores its 16-byte chunk c at slot c ^ ((r >> SWS) & SWZ)
   constexpr int A_CH = BM * CPR / NT;       // A chunks per thread per stage
   constexpr int B_CH = BN * CPR / NT;
   static_assert(A_CH >= 1 && B_CH >= 1, "tile too small");
+  static_assert(BK % 16 == 0, "K slice");
 
   __shared__ __align__(16) uint16_t sa[2][BM * BK];
   __shared__ __align__(16) uint16_t sb[2][BN * BK];
@@ -121,37 +135,37 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Args a) {
   const int wm = wave / WN, wn = wave % WN;
   const int K = a.K;
 
-  // global source pointers of this thread's chunks
+  // Thread tid loads chunk ch = tid % CPR of tile rows r = tid / CPR + i * RPI
+  // (RPI = NT / CPR rows per pass), so its LDS swizzle is the same for every
+  // i and all per-i offsets are wave-uniform strides.
+  constexpr int RPI = NT / CPR;
+  const int r_t = tid / CPR, ch_t = tid % CPR;
+  const int l_t = r_t * BK + ((ch_t ^ ((r_t >> SWS) & SWZ)) << 3);  // + i*RPI*BK
   const uint16_t* ga[A_CH];
-  const uint16_t* gb[B_CH];
-  int la[A_CH], lb[B_CH];  // LDS element offsets (swizzled)
 #pragma unroll
   for (int i = 0; i < A_CH; ++i) {
-    const int c = tid + i * NT, r = c / CPR, ch = c % CPR;
-    const int rr = min(m0 + r, Mj - 1);
+    const int rr = min(m0 + r_t + i * RPI, Mj - 1);
     size_t src_row;
     if (MODE == GATEUP)
       src_row = static_cast<size_t>(a.row_token[row0 + rr]);
     else
       src_row = static_cast<size_t>(row0 + rr);
-    ga[i] = a.a + src_row * K + ch * 8;
-    la[i] = r * BK + ((ch ^ (r & 7)) << 3);
+    ga[i] = a.a + src_row * K + ch_t * 8;
   }
   const uint16_t* wj = a.w + static_cast<size_t>(j) * a.w_stride;
-#pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int c = tid + i * NT, r = c / CPR, ch = c % CPR;
-    size_t wrow;
-    if (MODE == GATEUP) {
-      const int nh0 = nt * (BN / 2);
-      wrow = r < BN / 2 ? static_cast<size_t>(nh0 + r)
-                        : static_cast<size_t>(a.I + nh0 + (r - BN / 2));
-    } else {
-      wrow = static_cast<size_t>(nt * BN + r);
-    }
-    gb[i] = wj + wrow * K + ch * 8;
-    lb[i] = r * BK + ((ch ^ (r & 7)) << 3);
-  }
+  size_t wrow0;
+  if (MODE == GATEUP)
+    wrow0 = static_cast<size_t>(nt * (BN / 2) + r_t);
+  else
+    wrow0 = static_cast<size_t>(nt * BN + r_t);
+  const uint16_t* gb0 = wj + wrow0 * K + ch_t * 8;
+  // weight-row offset of pass i (gate rows, then the up rows I further on)
+  auto brow_off = [&](int i) -> size_t {
+    const int r = i * RPI;
+    if (MODE == GATEUP && r >= BN / 2)
+      return static_cast<size_t>(r - BN / 2 + a.I) * K;
+    return static_cast<size_t>(r) * K;
+  };
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -161,96 +175,360 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Args a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.f;
 
-  u32x4 ra[A_CH], rb[B_CH];
+  // Fragment rows of a lane differ by multiples of 32, so the swizzle term
+  // (row & SWZ) is the lane's own (frow & SWZ) for every fragment.
+  const int frow = lane & 31, fhalf = lane >> 5;
+  const int a_lane = (wm * TM + frow) * BK;
+  const int b_lane = (MODE == GATEUP ? wn * (TN / 2) + frow : wn * TN + frow) * BK;
+  auto brow_rel = [](int y) {  // fragment y's first row within the B tile
+    if (MODE == GATEUP)
+      return (y < FN / 2) ? y * 32 : BN / 2 + (y - FN / 2) * 32;
+    return y * 32;
+  };
+
+  // Two register staging sets: slice kt+2 is requested while slice kt is
+  // multiplied out of LDS and slice kt+1 waits in registers.
+  u32x4 ra[2][A_CH], rb[2][B_CH];
+#define MOE_FETCH(set, kslice)                                               \
+  do {                                                                       \
+    const int k0_ = (kslice) * BK;                                           \
+    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                         \
+        ra[set][i] = *reinterpret_cast<const u32x4*>(ga[i] + k0_);           \
+    _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                         \
+        rb[set][i] = *reinterpret_cast<const u32x4*>(gb0 + brow_off(i) + k0_); \
+  } while (0)
+#define MOE_STASH(set, buf)                                                  \
+  do {                                                                       \
+    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                         \
+        *reinterpret_cast<u32x4*>(&sa[buf][l_t + i * RPI * BK]) = ra[set][i]; \
+    _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                         \
+        *reinterpret_cast<u32x4*>(&sb[buf][l_t + i * RPI * BK]) = rb[set][i]; \
+  } while (0)
+  // C^T = W x^T: the weight fragment is the MFMA's A operand, so each lane
+  // ends up holding 4 consecutive output columns of one row.
+#define MOE_MMA(buf)                                                         \
+  do {                                                                       \
+    const uint16_t* A_ = sa[buf];                                            \
+    const uint16_t* B_ = sb[buf];                                            \
+    _Pragma("unroll") for (int kk = 0; kk < BK / 16; ++kk) {                 \
+      const int sw = ((kk * 2 + fhalf) ^ ((frow >> SWS) & SWZ)) << 3;        \
+      bf16x8 fa[FM], fb[FN];                                                 \
+      _Pragma("unroll") for (int x = 0; x < FM; ++x)                         \
+          fa[x] = *reinterpret_cast<const bf16x8*>(&A_[a_lane + x * 32 * BK + sw]); \
+      _Pragma("unroll") for (int y = 0; y < FN; ++y)                         \
+          fb[y] = *reinterpret_cast<const bf16x8*>(&B_[b_lane + brow_rel(y) * BK + sw]); \
+      _Pragma("unroll") for (int x = 0; x < FM; ++x)                         \
+          _Pragma("unroll") for (int y = 0; y < FN; ++y)                     \
+              acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(           \
+                  fb[y], fa[x], acc[x][y], 0, 0, 0);                         \
+    }                                                                        \
+  } while (0)
 
   const int nk = K / BK;
-  {
-#pragma unroll
-      for (int i = 0; i < A_CH; ++i)
-        ra[i] = *(reinterpret_cast<const u32x4*>(ga[i] + 0));
-#pragma unroll
-      for (int i = 0; i < B_CH; ++i)
-        rb[i] = *(reinterpret_cast<const u32x4*>(gb[i] + 0));
-    }
-  {
-#pragma unroll
-      for (int i = 0; i < A_CH; ++i)
-        *reinterpret_cast<u32x4*>(&sa[0][la[i]]) = ra[i];
-#pragma unroll
-      for (int i = 0; i < B_CH; ++i)
-        *reinterpret_cast<u32x4*>(&sb[0][lb[i]]) = rb[i];
-    }
+  MOE_FETCH(0, 0);
+  if (nk > 1) MOE_FETCH(1, 1);
+  MOE_STASH(0, 0);
   __syncthreads();
-  const int frow = lane & 31, fhalf = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) {
-#pragma unroll
-      for (int i = 0; i < A_CH; ++i)
-        ra[i] = *(reinterpret_cast<const u32x4*>(ga[i] + (kt + 1) * BK));
-#pragma unroll
-      for (int i = 0; i < B_CH; ++i)
-        rb[i] = *(reinterpret_cast<const u32x4*>(gb[i] + (kt + 1) * BK));
-    }
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int ch = kk * 2 + fhalf;
-      bf16x8 fa[FM], fb[FN];
-#pragma unroll
-      for (int x = 0; x < FM; ++x) {
-        const int r = wm * TM + x * 32 + frow;
-        fa[x] = *reinterpret_cast<const bf16x8*>(&sa[buf][r * BK + ((ch ^ (r & 7)) << 3)]);
-      }
-#pragma unroll
-      for (int y = 0; y < FN; ++y) {
-        int r;
-        if (MODE == GATEUP)
-          r = (y < FN / 2) ? (wn * (TN / 2) + y * 32 + frow)
-                           : (BN / 2 + wn * (TN / 2) + (y - FN / 2) * 32 + frow);
-        else
-          r = wn * TN + y * 32 + frow;
-        fb[y] = *reinterpret_cast<const bf16x8*>(&sb[buf][r * BK + ((ch ^ (r & 7)) << 3)]);
-      }
-#pragma unroll
-      for (int x = 0; x < FM; ++x)
-#pragma unroll
-        for (int y = 0; y < FN; ++y)
-          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[x], fb[y],
-                                                              acc[x][y], 0, 0, 0);
-    }
-    if (kt + 1 < nk) {
-#pragma unroll
-      for (int i = 0; i < A_CH; ++i)
-        *reinterpret_cast<u32x4*>(&sa[(buf ^ 1)][la[i]]) = ra[i];
-#pragma unroll
-      for (int i = 0; i < B_CH; ++i)
-        *reinterpret_cast<u32x4*>(&sb[(buf ^ 1)][lb[i]]) = rb[i];
-    }
+  // iteration kt: slice kt in LDS buffer kt&1, slice kt+1 in register set
+  // (kt+1)&1, slice kt+2 requested into set kt&1 (freed by the stash above)
+  int kt = 0;
+  for (; kt + 2 <= nk; kt += 2) {
+    if (kt + 2 < nk) MOE_FETCH(0, kt + 2);
+    MOE_MMA(0);
+    MOE_STASH(1, 1);
+    __syncthreads();
+    if (kt + 3 < nk) MOE_FETCH(1, kt + 3);
+    MOE_MMA(1);
+    if (kt + 2 < nk) MOE_STASH(0, 0);
     __syncthreads();
   }
+  if (kt < nk) MOE_MMA(0);  // odd slice count: the last slice sits in buffer 0
+#undef MOE_FETCH
+#undef MOE_STASH
+#undef MOE_MMA
 
-  // epilogue: lane holds column (lane & 31) and rows 8*(r/4) + 4*(lane/32) + r%4
-  const int col = lane & 31;
+  // epilogue: fragment (x, y) holds C^T, so lane holds row (lane & 31) of the
+  // fragment and columns 8*q + 4*(lane/32) + i in register 4*q + i
+  const int fr = lane & 31;
+  constexpr int OUT_FN = MODE == GATEUP ? FN / 2 : FN;
 #pragma unroll
   for (int x = 0; x < FM; ++x) {
+    const int row = wm * TM + x * 32 + fr;
+    const bool live = m0 + row < Mj;
+    const size_t orow = static_cast<size_t>(row0 + m0 + row) * a.NC;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = wm * TM + x * 32 + 8 * (r / 4) + 4 * fhalf + (r % 4);
-      if (m0 + row >= Mj) continue;
-      const size_t orow = static_cast<size_t>(row0 + m0 + row);
-      if (MODE == GATEUP) {
+    for (int y = 0; y < OUT_FN; ++y) {
+      const int c0 = MODE == GATEUP ? nt * (BN / 2) + wn * (TN / 2) + y * 32
+                                    : nt * BN + wn * TN + y * 32;
 #pragma unroll
-        for (int y = 0; y < FN / 2; ++y) {
-          const float g = acc[x][y][r], u = acc[x][y + FN / 2][r];
-          const int hc = nt * (BN / 2) + wn * (TN / 2) + y * 32 + col;
-          a.out[orow * a.NC + hc] = f32_to_bf16(silu(g) * u);
+      for (int q = 0; q < 4; ++q) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * q + i;
+          v[i] = MODE == GATEUP ? silu(acc[x][y][r]) * acc[x][y + FN / 2][r]
+                                : acc[x][y][r];
         }
-      } else {
+        uint2 pk;
+        pk.x = static_cast<uint32_t>(f32_to_bf16(v[0])) |
+               (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+        pk.y = static_cast<uint32_t>(f32_to_bf16(v[2])) |
+               (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+        if (live)
+          *reinterpret_cast<uint2*>(&a.out[orow + c0 + 8 * q + 4 * fhalf]) = pk;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------- direct-to-LDS pipeline
+// Prefill variant: A and B slices travel global -> LDS with
+// global_load_lds_dwordx4 (16 bytes per lane, 1 KB per wave instruction,
+// written at consecutive LDS addresses), so no VGPRs hold staged tiles and
+// the whole register file serves the accumulators and fragments.  S LDS
+// stages form a ring; slice kt+S-1 is requested while slice kt is consumed.
+// The swizzle is applied on the global side: the lane that fills LDS slot
+// (row, s) fetches chunk s ^ ((row >> SWS) & SWZ) of that row.
+
+// Issued as inline assembly so the compiler's automatic wait insertion
+// does not treat later LDS reads as dependent on it: completion is tracked
+// explicitly (wait_vmcnt + barrier) by the pipeline below.
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>(
+          (__attribute__((address_space(3))) unsigned char*)(lds_wave_base))));
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+
+// s_waitcnt with only the vector-memory counter limited (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Barrier without the memory fence of __syncthreads: LDS here is written
+// only by the DMA loads, whose completion each wave has already waited for.
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+#ifndef MOE_DMA_WPE
+#define MOE_DMA_WPE 1
+#endif
+template <int MODE, int BM, int BN, int BK, int WM, int WN, int S>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, MOE_DMA_WPE)))
+void gemm_dma_kernel(Args a) {
+  static_assert(S >= 2 && S <= 5, "pipeline depth");
+  static_assert(WM * WN == NT / MOE_WAVE, "4 waves");
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  static_assert(MODE == DOWN || FN % 2 == 0, "gate/up pairs");
+  constexpr int CPR = BK / 8;                 // 16-byte chunks per row
+  constexpr int SWZ = CPR - 1;
+  constexpr int SWS = BK == 64 ? 1 : (BK == 32 ? 2 : 0);  // 256-byte bank rows
+  constexpr int RPJ = MOE_WAVE / CPR;         // rows per DMA instruction
+  constexpr int NA = BM / RPJ, NB = BN / RPJ; // instructions per stage
+  static_assert(NA % 4 == 0 && NB % 4 == 0, "split over 4 waves");
+  constexpr int QA = NA / 4, QB = NB / 4;     // per wave
+  constexpr int LPW = QA + QB;                // DMA loads per wave per stage
+  constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int cum[1025];
+
+  int j, m0, nt, Mj, row0;
+  if (!find_tile<BM>(a, cum, j, m0, nt, Mj, row0)) return;
+
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / MOE_WAVE;
+  const int wm = wave / WN, wn = wave % WN;
+  const int K = a.K;
+
+  // per-lane source pointers of this wave's DMA instructions
+  const int lrow = lane / CPR, lslot = lane % CPR;
+  const uint16_t* ga[QA];
+  const uint16_t* gb[QB];
 #pragma unroll
-        for (int y = 0; y < FN; ++y) {
-          const int c = nt * BN + wn * TN + y * 32 + col;
-          a.out[orow * a.NC + c] = f32_to_bf16(acc[x][y][r]);
+  for (int q = 0; q < QA; ++q) {
+    const int row = (wave * QA + q) * RPJ + lrow;
+    const int ch = lslot ^ ((row >> SWS) & SWZ);
+    const int rr = min(m0 + row, Mj - 1);
+    size_t src_row;
+    if (MODE == GATEUP)
+      src_row = static_cast<size_t>(a.row_token[row0 + rr]);
+    else
+      src_row = static_cast<size_t>(row0 + rr);
+    ga[q] = a.a + src_row * K + ch * 8;
+  }
+  const uint16_t* wj = a.w + static_cast<size_t>(j) * a.w_stride;
+#pragma unroll
+  for (int q = 0; q < QB; ++q) {
+    const int row = (wave * QB + q) * RPJ + lrow;
+    const int ch = lslot ^ ((row >> SWS) & SWZ);
+    size_t wrow;
+    if (MODE == GATEUP)
+      wrow = row < BN / 2 ? static_cast<size_t>(nt * (BN / 2) + row)
+                          : static_cast<size_t>(a.I + nt * (BN / 2) + (row - BN / 2));
+    else
+      wrow = static_cast<size_t>(nt * BN + row);
+    gb[q] = wj + wrow * K + ch * 8;
+  }
+  // Slice kslice goes to ring stage kslice % S.  Requests past the last
+  // slice re-fetch the last slice into a stage that is never read again, so
+  // every iteration issues the same number of loads.
+  const int nk = K / BK;
+  auto issue = [&](int kslice) {
+    unsigned char* st = smem + (kslice % S) * STAGE;
+    const int k0 = min(kslice, nk - 1) * BK;
+#pragma unroll
+    for (int q = 0; q < QA; ++q) lds_dma16(ga[q] + k0, st + (wave * QA + q) * 1024);
+#pragma unroll
+    for (int q = 0; q < QB; ++q)
+      lds_dma16(gb[q] + k0, st + A_BYTES + (wave * QB + q) * 1024);
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int x = 0; x < FM; ++x)
+#pragma unroll
+    for (int y = 0; y < FN; ++y)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.f;
+
+  const int frow = lane & 31, fhalf = lane >> 5;
+  const int a_lane = (wm * TM + frow) * BK;
+  const int b_lane = (MODE == GATEUP ? wn * (TN / 2) + frow : wn * TN + frow) * BK;
+  auto brow_rel = [](int y) {
+    if (MODE == GATEUP)
+      return (y < FN / 2) ? y * 32 : BN / 2 + (y - FN / 2) * 32;
+    return y * 32;
+  };
+
+  // Ring protocol (slice t in stage t % S, D = S - 2 slices requested ahead):
+  //  - before the last sub-slice of slice kt: wait for this wave's loads of
+  //    slice kt+1, barrier (everyone's slice kt+1 landed; everyone's reads of
+  //    slice kt-1 are long consumed), request slice kt+1+D into the stage of
+  //    slice kt-1;
+  //  - the last sub-slice's MFMAs overlap the reads of slice kt+1's first
+  //    fragments, so no LDS latency is exposed at slice boundaries.
+  constexpr int D = S > 2 ? S - 2 : 1;
+  constexpr int KK = BK / 16;
+  constexpr int NFR = FM + FN, NMF = FM * FN;
+  // fragment reads go through an LDS-typed pointer so they stay ds_read
+  typedef __attribute__((address_space(3))) const bf16x8 lds_frag;
+  typedef __attribute__((address_space(3))) const unsigned char lds_byte;
+  lds_byte* lds0 = (lds_byte*)(smem);
+  bf16x8 fa[2][FM], fb[2][FN];
+  auto read_frags = [&](int stage, int kk, bf16x8* pa, bf16x8* pb) {
+    lds_byte* A_ = lds0 + stage * STAGE;
+    lds_byte* B_ = A_ + A_BYTES;
+    const int sw = ((kk * 2 + fhalf) ^ ((frow >> SWS) & SWZ)) << 4;  // bytes
+#pragma unroll
+    for (int x = 0; x < FM; ++x)
+      pa[x] = *(lds_frag*)(A_ + (a_lane + x * 32 * BK) * 2 + sw);
+#pragma unroll
+    for (int y = 0; y < FN; ++y)
+      pb[y] = *(lds_frag*)(B_ + (b_lane + brow_rel(y) * BK) * 2 + sw);
+  };
+  auto mma = [&](const bf16x8* pa, const bf16x8* pb) {
+#pragma unroll
+    for (int x = 0; x < FM; ++x)
+#pragma unroll
+      for (int y = 0; y < FN; ++y)
+        acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb[y], pa[x], acc[x][y], 0, 0, 0);
+  };
+  auto interleave = [&]() {  // MFMAs of one sub-slice paired with DS reads
+#pragma unroll
+    for (int i = 0; i < NFR; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x0008, NMF / NFR, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);          // DS read
+    }
+  };
+
+  if constexpr (S == 2) {
+    // Two stages: slice kt+1 is requested at the top of iteration kt (its
+    // stage was last read in iteration kt-1, before this barrier).
+    issue(0);
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_vmcnt<0>();
+      wg_barrier();
+      issue(kt + 1);
+      const int cur = kt & 1;
+      read_frags(cur, 0, fa[0], fb[0]);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        if (kk + 1 < KK) read_frags(cur, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+        mma(fa[kk & 1], fb[kk & 1]);
+        if (kk == 0) {
+          __builtin_amdgcn_sched_group_barrier(0x0020, LPW, 0);  // VMEM (DMA)
+          __builtin_amdgcn_sched_group_barrier(0x0100, NFR, 0);  // first reads
         }
+        if (kk + 1 < KK) interleave();
+        else __builtin_amdgcn_sched_group_barrier(0x0008, NMF, 0);
+      }
+    }
+  } else {
+  #pragma unroll
+    for (int t = 0; t <= D; ++t) issue(t);
+    wait_vmcnt<D * LPW>();
+    wg_barrier();
+    read_frags(0, 0, fa[0], fb[0]);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt % S;
+      const int nxt = (kt + 1) % S;
+      // sub-slices 0 .. KK-2 of slice kt (fragment set kk & 1)
+  #pragma unroll
+      for (int kk = 0; kk + 1 < KK; ++kk) {
+        read_frags(cur, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+        mma(fa[kk & 1], fb[kk & 1]);
+        interleave();
+      }
+      wait_vmcnt<(D - 1) * LPW>();
+      wg_barrier();
+      issue(kt + 1 + D);
+      // last sub-slice of kt, reading slice kt+1's first fragments meanwhile
+      // (on the last slice those reads fetch stale data that nobody uses)
+      read_frags(nxt, 0, fa[KK & 1], fb[KK & 1]);
+      mma(fa[(KK - 1) & 1], fb[(KK - 1) & 1]);
+      __builtin_amdgcn_sched_group_barrier(0x0020, LPW, 0);  // VMEM (DMA)
+      interleave();
+      if (KK & 1) {  // keep set 0 as "current" at the top of the loop
+  #pragma unroll
+        for (int x = 0; x < FM; ++x) fa[0][x] = fa[1][x];
+  #pragma unroll
+        for (int y = 0; y < FN; ++y) fb[0][y] = fb[1][y];
+      }
+    }
+  }
+  wait_vmcnt<0>();  // no DMA write may land after the workgroup ends
+
+  const int fr = lane & 31;
+  constexpr int OUT_FN = MODE == GATEUP ? FN / 2 : FN;
+#pragma unroll
+  for (int x = 0; x < FM; ++x) {
+    const int row = wm * TM + x * 32 + fr;
+    const bool live = m0 + row < Mj;
+    const size_t orow = static_cast<size_t>(row0 + m0 + row) * a.NC;
+#pragma unroll
+    for (int y = 0; y < OUT_FN; ++y) {
+      const int c0 = MODE == GATEUP ? nt * (BN / 2) + wn * (TN / 2) + y * 32
+                                    : nt * BN + wn * TN + y * 32;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * q + i;
+          v[i] = MODE == GATEUP ? silu(acc[x][y][r]) * acc[x][y + FN / 2][r]
+                                : acc[x][y][r];
+        }
+        uint2 pk;
+        pk.x = static_cast<uint32_t>(f32_to_bf16(v[0])) |
+               (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+        pk.y = static_cast<uint32_t>(f32_to_bf16(v[2])) |
+               (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+        if (live)
+          *reinterpret_cast<uint2*>(&a.out[orow + c0 + 8 * q + 4 * fhalf]) = pk;
       }
     }
   }
@@ -302,13 +580,32 @@ __global__ __launch_bounds__(256) void down_f32(
 }
 
 // ------------------------------------------------------------------ host
-template <int MODE, int BM, int BN, int WM, int WN>
+template <int MODE, int BM, int BN, int BK, int WM, int WN>
 static void launch_gemm(const Args& a, int rows_cap, hipStream_t s) {
   const int mt_ub = (rows_cap + BM - 1) / BM + a.N;
   long grid = static_cast<long>(mt_ub) * a.n_tiles;
   grid = (grid + 7) / 8 * 8;
-  hipLaunchKernelGGL((gemm_kernel<MODE, BM, BN, WM, WN>), dim3(grid), dim3(NT),
-                     0, s, a);
+  hipLaunchKernelGGL((gemm_kernel<MODE, BM, BN, BK, WM, WN>), dim3(grid),
+                     dim3(NT), 0, s, a);
+}
+
+template <int MODE, int BM, int BN, int BK, int WM, int WN, int S>
+static int launch_gemm_dma(const Args& a, int rows_cap, hipStream_t s) {
+  constexpr size_t lds = static_cast<size_t>(S) * (BM + BN) * BK * 2;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute(
+            reinterpret_cast<const void*>(gemm_dma_kernel<MODE, BM, BN, BK, WM, WN, S>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)) != hipSuccess)
+      return MOE_EHIP;
+    attr_set = true;
+  }
+  const int mt_ub = (rows_cap + BM - 1) / BM + a.N;
+  long grid = static_cast<long>(mt_ub) * a.n_tiles;
+  grid = (grid + 7) / 8 * 8;
+  hipLaunchKernelGGL((gemm_dma_kernel<MODE, BM, BN, BK, WM, WN, S>), dim3(grid),
+                     dim3(NT), lds, s, a);
+  return MOE_OK;
 }
 
 }  // namespace ffn
@@ -316,6 +613,30 @@ static void launch_gemm(const Args& a, int rows_cap, hipStream_t s) {
 
 using namespace moe;
 using namespace moe::ffn;
+
+// Prefill tiles: 256 rows x 256 columns of C per workgroup (2 x 2 waves,
+// each a 128 x 128 block of 4 x 4 fragments), K slices of 32 through a
+// 4-stage direct-to-LDS ring.  The gate-up tile covers 128 h columns (128
+// gate rows + 128 up rows of W13), the down tile 256 output columns.
+// Shapes whose I or H is not a multiple of that use 128 x 256 tiles.
+#ifndef MOE_GU_CFG
+#define MOE_GU_CFG 256, 256, 32, 2, 2
+#endif
+#ifndef MOE_DN_CFG
+#define MOE_DN_CFG 256, 256, 32, 2, 2
+#endif
+#ifndef MOE_DMA
+#define MOE_DMA 1
+#endif
+#ifndef MOE_STAGES
+#define MOE_STAGES 4
+#endif
+constexpr int GU_CFG[] = {MOE_GU_CFG};
+constexpr int DN_CFG[] = {MOE_DN_CFG};
+constexpr int GU_BM = GU_CFG[0], GU_BN = GU_CFG[1], GU_BK = GU_CFG[2],
+              GU_WM = GU_CFG[3], GU_WN = GU_CFG[4];
+constexpr int DN_BM = DN_CFG[0], DN_BN = DN_CFG[1], DN_BK = DN_CFG[2],
+              DN_WM = DN_CFG[3], DN_WN = DN_CFG[4];
 
 // Tile shapes: decode-sized batches (at most 32 rows per expert on average)
 // use 32-row tiles so the weight panels stream with little padding work;
@@ -374,10 +695,16 @@ extern "C" int moe_ffn_gate_up(const void* x, const int32_t* row_token,
   g.w_stride = 2L * I * H;
   if (decode_tiles(T, N, k)) {
     g.n_tiles = I / 128;
-    launch_gemm<GATEUP, 32, 256, 1, 4>(g, rows_cap, s);
+    launch_gemm<GATEUP, 32, 256, 64, 1, 4>(g, rows_cap, s);
+  } else if (I % (GU_BN / 2) == 0) {
+    g.n_tiles = I / (GU_BN / 2);
+    if (MOE_DMA)
+      return launch_gemm_dma<GATEUP, GU_BM, GU_BN, GU_BK, GU_WM, GU_WN, MOE_STAGES>(g, rows_cap, s) == MOE_OK
+                 ? launch_status() : MOE_EHIP;
+    launch_gemm<GATEUP, GU_BM, GU_BN, GU_BK, GU_WM, GU_WN>(g, rows_cap, s);
   } else {
-    g.n_tiles = I / 64;
-    launch_gemm<GATEUP, 128, 128, 2, 2>(g, rows_cap, s);
+    g.n_tiles = I / 128;
+    launch_gemm<GATEUP, 128, 256, 32, 1, 4>(g, rows_cap, s);
   }
   return launch_status();
 }
@@ -412,10 +739,16 @@ extern "C" int moe_ffn_down(const void* h, const int32_t* expert_offsets,
   d.w_stride = static_cast<long>(H) * I;
   if (decode_tiles(T, N, k)) {
     d.n_tiles = H / 256;
-    launch_gemm<DOWN, 32, 256, 1, 4>(d, rows_cap, s);
+    launch_gemm<DOWN, 32, 256, 64, 1, 4>(d, rows_cap, s);
+  } else if (H % DN_BN == 0) {
+    d.n_tiles = H / DN_BN;
+    if (MOE_DMA)
+      return launch_gemm_dma<DOWN, DN_BM, DN_BN, DN_BK, DN_WM, DN_WN, MOE_STAGES>(d, rows_cap, s) == MOE_OK
+                 ? launch_status() : MOE_EHIP;
+    launch_gemm<DOWN, DN_BM, DN_BN, DN_BK, DN_WM, DN_WN>(d, rows_cap, s);
   } else {
-    d.n_tiles = H / 128;
-    launch_gemm<DOWN, 128, 128, 2, 2>(d, rows_cap, s);
+    d.n_tiles = H / 256;
+    launch_gemm<DOWN, 128, 256, 32, 1, 4>(d, rows_cap, s);
   }
   return launch_status();
 }
