@@ -6,10 +6,10 @@
 //
 // bf16 path: MFMA v_mfma_f32_32x32x16_bf16 (gfx950), fp32 accumulation.
 // Each workgroup (4 waves) owns one (expert, row tile, column tile).  A and B
-// tiles are staged through LDS in BK = 64 slices, double buffered, with the
-// 16-byte chunks of each row XOR-swizzled by the row index so the 16-byte
-// fragment reads of a wave spread over the banks.  The gate-up tile holds the
-// gate rows and the matching up rows of the same h columns, so the SwiGLU
+// tiles travel global -> LDS by direct-to-LDS loads through a ring of S
+// stages, with the 16-byte chunks of each row XOR-swizzled so that fragment
+// reads of a wave are bank-conflict free.  The gate-up tile holds the gate
+// rows and the matching up rows of the same h columns, so the SwiGLU
 // epilogue pairs two accumulators held by the same lane.  The x rows are
 // gathered through row_token inside the load; no permuted x is written.
 //
@@ -30,11 +30,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 enum { GATEUP = 0, DOWN = 1 };
 constexpr int NT = 256;
-// LDS chunk swizzle: 0 = by row (bank rows of 128 bytes), 1 = by the row's
-// position among the rows that share a 256-byte bank row.
-#ifndef MOE_SWZ_MODE
-#define MOE_SWZ_MODE 0
-#endif
 
 struct Args {
   const uint16_t* a;       // GATEUP: x [T,H]; DOWN: h [T*k, I]
@@ -102,185 +97,6 @@ __device__ bool find_tile(const Args& a, int* cum, int& j, int& m0, int& nt,
   return true;
 }
 
-// One (expert, row tile, column tile) per workgroup of 4 waves arranged
-// WM x WN; each wave owns a (BM/WM) x (BN/WN) block of the C tile made of
-// 32x32 MFMA fragments (accumulators live in AGPRs).  K advances in BK
-// slices through two LDS buffers; the next slice is fetched into registers
-// while the current one feeds the MFMAs.
-template <int MODE, int BM, int BN, int BK, int WM, int WN>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2)))
-void gemm_kernel(Args a) {
-  static_assert(WM * WN == NT / MOE_WAVE, "4 waves");
-  constexpr int TM = BM / WM, TN = BN / WN;
-  constexpr int FM = TM / 32, FN = TN / 32;
-  static_assert(FM >= 1 && FN >= 1, "fragment grid");
-  static_assert(MODE == DOWN || FN % 2 == 0, "gate/up pairs");
-  constexpr int CPR = BK / 8;               // 16-byte chunks per tile row
-  constexpr int SWZ = CPR - 1;              // chunk swizzle mask
-  constexpr int SWS = MOE_SWZ_MODE == 0 ? 0 : (BK == 64 ? 1 : (BK == 32 ? 2 : 0));
-  // LDS row r stores its 16-byte chunk c at slot c ^ ((r >> SWS) & SWZ)
-  constexpr int A_CH = BM * CPR / NT;       // A chunks per thread per stage
-  constexpr int B_CH = BN * CPR / NT;
-  static_assert(A_CH >= 1 && B_CH >= 1, "tile too small");
-  static_assert(BK % 16 == 0, "K slice");
-
-  __shared__ __align__(16) uint16_t sa[2][BM * BK];
-  __shared__ __align__(16) uint16_t sb[2][BN * BK];
-  __shared__ int cum[1025];
-
-  int j, m0, nt, Mj, row0;
-  if (!find_tile<BM>(a, cum, j, m0, nt, Mj, row0)) return;
-
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / MOE_WAVE;
-  const int wm = wave / WN, wn = wave % WN;
-  const int K = a.K;
-
-  // Thread tid loads chunk ch = tid % CPR of tile rows r = tid / CPR + i * RPI
-  // (RPI = NT / CPR rows per pass), so its LDS swizzle is the same for every
-  // i and all per-i offsets are wave-uniform strides.
-  constexpr int RPI = NT / CPR;
-  const int r_t = tid / CPR, ch_t = tid % CPR;
-  const int l_t = r_t * BK + ((ch_t ^ ((r_t >> SWS) & SWZ)) << 3);  // + i*RPI*BK
-  const uint16_t* ga[A_CH];
-#pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int rr = min(m0 + r_t + i * RPI, Mj - 1);
-    size_t src_row;
-    if (MODE == GATEUP)
-      src_row = static_cast<size_t>(a.row_token[row0 + rr]);
-    else
-      src_row = static_cast<size_t>(row0 + rr);
-    ga[i] = a.a + src_row * K + ch_t * 8;
-  }
-  const uint16_t* wj = a.w + static_cast<size_t>(j) * a.w_stride;
-  size_t wrow0;
-  if (MODE == GATEUP)
-    wrow0 = static_cast<size_t>(nt * (BN / 2) + r_t);
-  else
-    wrow0 = static_cast<size_t>(nt * BN + r_t);
-  const uint16_t* gb0 = wj + wrow0 * K + ch_t * 8;
-  // weight-row offset of pass i (gate rows, then the up rows I further on)
-  auto brow_off = [&](int i) -> size_t {
-    const int r = i * RPI;
-    if (MODE == GATEUP && r >= BN / 2)
-      return static_cast<size_t>(r - BN / 2 + a.I) * K;
-    return static_cast<size_t>(r) * K;
-  };
-
-  f32x16 acc[FM][FN];
-#pragma unroll
-  for (int x = 0; x < FM; ++x)
-#pragma unroll
-    for (int y = 0; y < FN; ++y)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.f;
-
-  // Fragment rows of a lane differ by multiples of 32, so the swizzle term
-  // (row & SWZ) is the lane's own (frow & SWZ) for every fragment.
-  const int frow = lane & 31, fhalf = lane >> 5;
-  const int a_lane = (wm * TM + frow) * BK;
-  const int b_lane = (MODE == GATEUP ? wn * (TN / 2) + frow : wn * TN + frow) * BK;
-  auto brow_rel = [](int y) {  // fragment y's first row within the B tile
-    if (MODE == GATEUP)
-      return (y < FN / 2) ? y * 32 : BN / 2 + (y - FN / 2) * 32;
-    return y * 32;
-  };
-
-  // Two register staging sets: slice kt+2 is requested while slice kt is
-  // multiplied out of LDS and slice kt+1 waits in registers.
-  u32x4 ra[2][A_CH], rb[2][B_CH];
-#define MOE_FETCH(set, kslice)                                               \
-  do {                                                                       \
-    const int k0_ = (kslice) * BK;                                           \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                         \
-        ra[set][i] = *reinterpret_cast<const u32x4*>(ga[i] + k0_);           \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                         \
-        rb[set][i] = *reinterpret_cast<const u32x4*>(gb0 + brow_off(i) + k0_); \
-  } while (0)
-#define MOE_STASH(set, buf)                                                  \
-  do {                                                                       \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                         \
-        *reinterpret_cast<u32x4*>(&sa[buf][l_t + i * RPI * BK]) = ra[set][i]; \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                         \
-        *reinterpret_cast<u32x4*>(&sb[buf][l_t + i * RPI * BK]) = rb[set][i]; \
-  } while (0)
-  // C^T = W x^T: the weight fragment is the MFMA's A operand, so each lane
-  // ends up holding 4 consecutive output columns of one row.
-#define MOE_MMA(buf)                                                         \
-  do {                                                                       \
-    const uint16_t* A_ = sa[buf];                                            \
-    const uint16_t* B_ = sb[buf];                                            \
-    _Pragma("unroll") for (int kk = 0; kk < BK / 16; ++kk) {                 \
-      const int sw = ((kk * 2 + fhalf) ^ ((frow >> SWS) & SWZ)) << 3;        \
-      bf16x8 fa[FM], fb[FN];                                                 \
-      _Pragma("unroll") for (int x = 0; x < FM; ++x)                         \
-          fa[x] = *reinterpret_cast<const bf16x8*>(&A_[a_lane + x * 32 * BK + sw]); \
-      _Pragma("unroll") for (int y = 0; y < FN; ++y)                         \
-          fb[y] = *reinterpret_cast<const bf16x8*>(&B_[b_lane + brow_rel(y) * BK + sw]); \
-      _Pragma("unroll") for (int x = 0; x < FM; ++x)                         \
-          _Pragma("unroll") for (int y = 0; y < FN; ++y)                     \
-              acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(           \
-                  fb[y], fa[x], acc[x][y], 0, 0, 0);                         \
-    }                                                                        \
-  } while (0)
-
-  const int nk = K / BK;
-  MOE_FETCH(0, 0);
-  if (nk > 1) MOE_FETCH(1, 1);
-  MOE_STASH(0, 0);
-  __syncthreads();
-  // iteration kt: slice kt in LDS buffer kt&1, slice kt+1 in register set
-  // (kt+1)&1, slice kt+2 requested into set kt&1 (freed by the stash above)
-  int kt = 0;
-  for (; kt + 2 <= nk; kt += 2) {
-    if (kt + 2 < nk) MOE_FETCH(0, kt + 2);
-    MOE_MMA(0);
-    MOE_STASH(1, 1);
-    __syncthreads();
-    if (kt + 3 < nk) MOE_FETCH(1, kt + 3);
-    MOE_MMA(1);
-    if (kt + 2 < nk) MOE_STASH(0, 0);
-    __syncthreads();
-  }
-  if (kt < nk) MOE_MMA(0);  // odd slice count: the last slice sits in buffer 0
-#undef MOE_FETCH
-#undef MOE_STASH
-#undef MOE_MMA
-
-  // epilogue: fragment (x, y) holds C^T, so lane holds row (lane & 31) of the
-  // fragment and columns 8*q + 4*(lane/32) + i in register 4*q + i
-  const int fr = lane & 31;
-  constexpr int OUT_FN = MODE == GATEUP ? FN / 2 : FN;
-#pragma unroll
-  for (int x = 0; x < FM; ++x) {
-    const int row = wm * TM + x * 32 + fr;
-    const bool live = m0 + row < Mj;
-    const size_t orow = static_cast<size_t>(row0 + m0 + row) * a.NC;
-#pragma unroll
-    for (int y = 0; y < OUT_FN; ++y) {
-      const int c0 = MODE == GATEUP ? nt * (BN / 2) + wn * (TN / 2) + y * 32
-                                    : nt * BN + wn * TN + y * 32;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float v[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * q + i;
-          v[i] = MODE == GATEUP ? silu(acc[x][y][r]) * acc[x][y + FN / 2][r]
-                                : acc[x][y][r];
-        }
-        uint2 pk;
-        pk.x = static_cast<uint32_t>(f32_to_bf16(v[0])) |
-               (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-        pk.y = static_cast<uint32_t>(f32_to_bf16(v[2])) |
-               (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
-        if (live)
-          *reinterpret_cast<uint2*>(&a.out[orow + c0 + 8 * q + 4 * fhalf]) = pk;
-      }
-    }
-  }
-}
-
 // ------------------------------------------------- direct-to-LDS pipeline
 // Prefill variant: A and B slices travel global -> LDS with
 // global_load_lds_dwordx4 (16 bytes per lane, 1 KB per wave instruction,
@@ -312,11 +128,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 // only by the DMA loads, whose completion each wave has already waited for.
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-#ifndef MOE_DMA_WPE
-#define MOE_DMA_WPE 1
-#endif
-template <int MODE, int BM, int BN, int BK, int WM, int WN, int S>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, MOE_DMA_WPE)))
+template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WPE>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, WPE)))
 void gemm_dma_kernel(Args a) {
   static_assert(S >= 2 && S <= 5, "pipeline depth");
   static_assert(WM * WN == NT / MOE_WAVE, "4 waves");
@@ -580,22 +393,13 @@ __global__ __launch_bounds__(256) void down_f32(
 }
 
 // ------------------------------------------------------------------ host
-template <int MODE, int BM, int BN, int BK, int WM, int WN>
-static void launch_gemm(const Args& a, int rows_cap, hipStream_t s) {
-  const int mt_ub = (rows_cap + BM - 1) / BM + a.N;
-  long grid = static_cast<long>(mt_ub) * a.n_tiles;
-  grid = (grid + 7) / 8 * 8;
-  hipLaunchKernelGGL((gemm_kernel<MODE, BM, BN, BK, WM, WN>), dim3(grid),
-                     dim3(NT), 0, s, a);
-}
-
-template <int MODE, int BM, int BN, int BK, int WM, int WN, int S>
+template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WPE = 1>
 static int launch_gemm_dma(const Args& a, int rows_cap, hipStream_t s) {
   constexpr size_t lds = static_cast<size_t>(S) * (BM + BN) * BK * 2;
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute(
-            reinterpret_cast<const void*>(gemm_dma_kernel<MODE, BM, BN, BK, WM, WN, S>),
+            reinterpret_cast<const void*>(gemm_dma_kernel<MODE, BM, BN, BK, WM, WN, S, WPE>),
             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)) != hipSuccess)
       return MOE_EHIP;
     attr_set = true;
@@ -603,7 +407,7 @@ static int launch_gemm_dma(const Args& a, int rows_cap, hipStream_t s) {
   const int mt_ub = (rows_cap + BM - 1) / BM + a.N;
   long grid = static_cast<long>(mt_ub) * a.n_tiles;
   grid = (grid + 7) / 8 * 8;
-  hipLaunchKernelGGL((gemm_dma_kernel<MODE, BM, BN, BK, WM, WN, S>), dim3(grid),
+  hipLaunchKernelGGL((gemm_dma_kernel<MODE, BM, BN, BK, WM, WN, S, WPE>), dim3(grid),
                      dim3(NT), lds, s, a);
   return MOE_OK;
 }
@@ -618,29 +422,41 @@ using namespace moe::ffn;
 // each a 128 x 128 block of 4 x 4 fragments), K slices of 32 through a
 // 4-stage direct-to-LDS ring.  The gate-up tile covers 128 h columns (128
 // gate rows + 128 up rows of W13), the down tile 256 output columns.
-// Shapes whose I or H is not a multiple of that use 128 x 256 tiles.
 #ifndef MOE_GU_CFG
 #define MOE_GU_CFG 256, 256, 32, 2, 2
 #endif
 #ifndef MOE_DN_CFG
 #define MOE_DN_CFG 256, 256, 32, 2, 2
 #endif
-#ifndef MOE_DMA
-#define MOE_DMA 1
-#endif
 #ifndef MOE_STAGES
 #define MOE_STAGES 4
 #endif
+// Decode tiles: 32 token rows x 256 columns (1 x 4 waves, each 32 x 64),
+// K slices of 64 through a 2-stage ring, two workgroups per CU so one
+// streams its next weight slice while the other multiplies.
+#ifndef MOE_DEC_CFG
+#define MOE_DEC_CFG 32, 256, 64, 1, 4, 2, 2
+#endif
+constexpr int DEC_CFG[] = {MOE_DEC_CFG};
+constexpr int DEC_BM = DEC_CFG[0], DEC_BN = DEC_CFG[1], DEC_BK = DEC_CFG[2],
+              DEC_WM = DEC_CFG[3], DEC_WN = DEC_CFG[4], DEC_S = DEC_CFG[5],
+              DEC_WPE = DEC_CFG[6];
 constexpr int GU_CFG[] = {MOE_GU_CFG};
 constexpr int DN_CFG[] = {MOE_DN_CFG};
 constexpr int GU_BM = GU_CFG[0], GU_BN = GU_CFG[1], GU_BK = GU_CFG[2],
               GU_WM = GU_CFG[3], GU_WN = GU_CFG[4];
 constexpr int DN_BM = DN_CFG[0], DN_BN = DN_CFG[1], DN_BK = DN_CFG[2],
               DN_WM = DN_CFG[3], DN_WN = DN_CFG[4];
+// every bf16 shape the entry points accept (H % 256 == 0, I % 128 == 0)
+// splits into whole column tiles and whole K slices
+static_assert(128 % (GU_BN / 2) == 0 && 128 % (DEC_BN / 2) == 0, "h column tiles");
+static_assert(256 % DN_BN == 0 && 256 % DEC_BN == 0, "output column tiles");
+static_assert(256 % GU_BK == 0 && 256 % DEC_BK == 0, "gate-up K slices");
+static_assert(128 % DN_BK == 0 && 128 % DEC_BK == 0, "down K slices");
 
 // Tile shapes: decode-sized batches (at most 32 rows per expert on average)
 // use 32-row tiles so the weight panels stream with little padding work;
-// larger batches use 128 x 128 tiles.
+// larger batches use the 256 x 256 prefill tiles.
 static bool decode_tiles(int T, int N, int k) {
   return static_cast<long>(T) * k <= 32L * N;
 }
@@ -694,17 +510,15 @@ extern "C" int moe_ffn_gate_up(const void* x, const int32_t* row_token,
   g.I = I;
   g.w_stride = 2L * I * H;
   if (decode_tiles(T, N, k)) {
-    g.n_tiles = I / 128;
-    launch_gemm<GATEUP, 32, 256, 64, 1, 4>(g, rows_cap, s);
-  } else if (I % (GU_BN / 2) == 0) {
-    g.n_tiles = I / (GU_BN / 2);
-    if (MOE_DMA)
-      return launch_gemm_dma<GATEUP, GU_BM, GU_BN, GU_BK, GU_WM, GU_WN, MOE_STAGES>(g, rows_cap, s) == MOE_OK
-                 ? launch_status() : MOE_EHIP;
-    launch_gemm<GATEUP, GU_BM, GU_BN, GU_BK, GU_WM, GU_WN>(g, rows_cap, s);
+    g.n_tiles = I / (DEC_BN / 2);
+    if (launch_gemm_dma<GATEUP, DEC_BM, DEC_BN, DEC_BK, DEC_WM, DEC_WN, DEC_S, DEC_WPE>(
+            g, rows_cap, s) != MOE_OK)
+      return MOE_EHIP;
   } else {
-    g.n_tiles = I / 128;
-    launch_gemm<GATEUP, 128, 256, 32, 1, 4>(g, rows_cap, s);
+    g.n_tiles = I / (GU_BN / 2);
+    if (launch_gemm_dma<GATEUP, GU_BM, GU_BN, GU_BK, GU_WM, GU_WN, MOE_STAGES, 1>(
+            g, rows_cap, s) != MOE_OK)
+      return MOE_EHIP;
   }
   return launch_status();
 }
@@ -738,17 +552,15 @@ extern "C" int moe_ffn_down(const void* h, const int32_t* expert_offsets,
   d.I = I;
   d.w_stride = static_cast<long>(H) * I;
   if (decode_tiles(T, N, k)) {
-    d.n_tiles = H / 256;
-    launch_gemm<DOWN, 32, 256, 64, 1, 4>(d, rows_cap, s);
-  } else if (H % DN_BN == 0) {
-    d.n_tiles = H / DN_BN;
-    if (MOE_DMA)
-      return launch_gemm_dma<DOWN, DN_BM, DN_BN, DN_BK, DN_WM, DN_WN, MOE_STAGES>(d, rows_cap, s) == MOE_OK
-                 ? launch_status() : MOE_EHIP;
-    launch_gemm<DOWN, DN_BM, DN_BN, DN_BK, DN_WM, DN_WN>(d, rows_cap, s);
+    d.n_tiles = H / DEC_BN;
+    if (launch_gemm_dma<DOWN, DEC_BM, DEC_BN, DEC_BK, DEC_WM, DEC_WN, DEC_S, DEC_WPE>(
+            d, rows_cap, s) != MOE_OK)
+      return MOE_EHIP;
   } else {
-    d.n_tiles = H / 256;
-    launch_gemm<DOWN, 128, 256, 32, 1, 4>(d, rows_cap, s);
+    d.n_tiles = H / DN_BN;
+    if (launch_gemm_dma<DOWN, DN_BM, DN_BN, DN_BK, DN_WM, DN_WN, MOE_STAGES, 1>(
+            d, rows_cap, s) != MOE_OK)
+      return MOE_EHIP;
   }
   return launch_status();
 }
