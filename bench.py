@@ -48,6 +48,12 @@ def parse():
                    help="skip the HIP-graph timed region")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="only copy a buffer of this many MiB device to device "
+                        "three times and exit (calibrates HBM byte counters)")
+    p.add_argument("--separate-routing", action="store_true",
+                   help="route with the four separate calls instead of the "
+                        "single fused launch")
     return p.parse_args()
 
 
@@ -90,6 +96,15 @@ def main():
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+        return
     from mixture_experts_layer_macs_amd import build as _build
     if not os.path.exists(_build.LIB):
         _build.build()
@@ -111,18 +126,13 @@ def main():
     h = torch.empty((T * k, I), dtype=torch_elem_dtype(wl.dtype), device=dev)
     decode = wl.kprime > 0 or T * k <= 32 * N
 
+    fused = lay.can_fuse and not args.separate_routing
+
     def step(i, ev=None):
         w13, w2 = w13s[i % len(w13s)], w2s[i % len(w2s)]
-        B.moe_route(d["logits"], k, R, lay.topk_ids, lay.topk_gates, lay.fallback_ids)
-        slot_in = lay.topk_ids
-        if wl.kprime:
-            B.moe_sere_reroute(lay.topk_ids, N, wl.kprime, wl.rho, d["sim"],
-                               d["prot"], lay.slot_sere, lay.flags_sere)
-            slot_in = lay.slot_sere
-        B.moe_capacity_assign(lay.topk_ids, slot_in, lay.fallback_ids,
-                              d["is_visual"], d["entropy_w"], d["modality"], N,
-                              R, wl.group, wl.gamma, wl.lam, lay.ws_cap, lay.cap)
-        B.moe_dispatch(lay.cap["slot_out"], N, lay.ws_disp, lay.disp)
+        lay.routing(d["logits"], d["is_visual"], d["entropy_w"], d["modality"],
+                    d["sim"], d["prot"], wl.kprime, wl.rho, wl.gamma, wl.lam,
+                    wl.group, fused=fused)
         if ev is not None:
             ev[0].record()
         B.moe_ffn_gate_up(d["x"], lay.disp["row_token"],
@@ -232,6 +242,7 @@ def main():
             "union_final": U, "kept_rows": M,
             "dropped": int(stats[2]), "macs_rerouted": int(stats[3]),
             "weight_copies": args.copies,
+            "routing": "fused" if fused else "separate",
             "mode": "eager" if graph_ms is None or ms <= graph_ms else "hip-graph",
         },
         "roofline": roof,

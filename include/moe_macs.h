@@ -17,6 +17,8 @@
  * keeps the original top-K):
  *   moe_route -> moe_sere_reroute -> moe_capacity_assign -> moe_dispatch
  *   -> moe_expert_ffn -> moe_combine
+ * Decode-sized batches can replace the first four calls by one
+ * moe_routing_fused launch.
  *
  * Conventions shared by every entry point
  *   - Every array argument is a DEVICE pointer owned by the caller; the
@@ -40,9 +42,10 @@
  *     reductions only where order cannot matter.
  *
  * Workspaces
- *   moe_capacity_assign, moe_dispatch and moe_expert_ffn take a workspace of
- *   at least the size their *_workspace_size() query returns.  The capacity
- *   and dispatch workspaces hold a few control words: they must be filled
+ *   moe_capacity_assign, moe_dispatch, moe_routing_fused and moe_expert_ffn
+ *   take a workspace of at least the size their *_workspace_size() query
+ *   returns.  The capacity, dispatch and fused-routing workspaces hold a
+ *   few control words: they must be filled
  *   with zero bytes once, before their first use (e.g. allocated zeroed);
  *   every call leaves those words zero again.  A workspace must not be
  *   shared by calls that may run concurrently.
@@ -175,6 +178,46 @@ int moe_dispatch(const int32_t* slot_expert, int T, int N, int k,
                  int32_t* expert_offsets, int32_t* row_token,
                  int32_t* row_slot, int32_t* slot_row,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_routing_fused -- moe_route, moe_sere_reroute (when kprime > 0),
+ * moe_capacity_assign and moe_dispatch in ONE launch, for decode-sized
+ * batches.  SERE write-up §4.3: the re-route operator is a
+ * single fused kernel with no host round trip that feeds the fused MoE
+ * directly; here the router and the capacity step join it.
+ *
+ * Every output has the meaning, layout and value that the four separate
+ * calls give when run in order on the same inputs:
+ *   topk_ids, topk_gates, fallback_ids      as moe_route;
+ *   slot_sere  i32[T,k]  as moe_sere_reroute's slot_expert (required when
+ *                        kprime > 0, unused and may be NULL when kprime == 0);
+ *   slot_expert, flags, load_q, cap_q, stats, r_v
+ *                        as moe_capacity_assign (flags carry MOE_FLAG_SERE);
+ *   expert_offsets, row_token, row_slot, slot_row
+ *                        as moe_dispatch.
+ * kprime == 0 turns SERE off (sim and prot may then be NULL); gamma = +inf
+ * turns capacity off.  The workspace holds a control word: fill it with
+ * zero bytes once before its first use; every call leaves it zero again.
+ * The batch-wide steps run in one workgroup with every array in LDS, which
+ * bounds the batch: moe_routing_workspace_size returns 0 for shapes the
+ * fused launch does not cover (about T*k <= 4096 at N = 128, k = R = 8),
+ * and moe_routing_fused returns MOE_EUNSUP for them; the separate calls
+ * cover every shape.
+ * Errors: as the separate calls, plus MOE_EUNSUP as above.
+ */
+size_t moe_routing_workspace_size(int T, int N, int k, int R);
+int moe_routing_fused(const float* logits, const uint8_t* is_visual,
+                      const float* entropy_w, const int8_t* modality,
+                      const float* sim, const uint8_t* prot,
+                      int T, int N, int k, int R, int kprime, float rho,
+                      int group, double gamma, double lam,
+                      int32_t* topk_ids, float* topk_gates,
+                      int32_t* fallback_ids, int32_t* slot_sere,
+                      int32_t* slot_expert, uint8_t* flags, int64_t* load_q,
+                      int64_t* cap_q, int64_t* stats, double* r_v,
+                      int32_t* expert_offsets, int32_t* row_token,
+                      int32_t* row_slot, int32_t* slot_row,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * moe_expert_ffn -- grouped SwiGLU expert FFN over the dispatched rows

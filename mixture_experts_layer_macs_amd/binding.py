@@ -44,6 +44,10 @@ _SIGS = {
                                  _D, _D, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_dispatch_workspace_size": (_SZ, [_I, _I, _I]),
     "moe_dispatch": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_routing_workspace_size": (_SZ, [_I, _I, _I, _I]),
+    "moe_routing_fused": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F,
+                               _I, _D, _D, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                               _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_ffn_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "moe_expert_ffn": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P,
                             _P, _SZ, _P]),
@@ -154,6 +158,12 @@ def moe_dispatch_workspace_size(T, N, k) -> int:
     return int(_lib.moe_dispatch_workspace_size(T, N, k))
 
 
+def moe_routing_workspace_size(T, N, k, R) -> int:
+    """Workspace bytes of moe_routing_fused; 0 = shape not covered by the
+    fused launch (use the separate calls)."""
+    return int(_lib.moe_routing_workspace_size(T, N, k, R))
+
+
 def moe_ffn_workspace_size(T, N, k, H, I, dtype) -> int:
     return int(_lib.moe_ffn_workspace_size(T, N, k, H, I, _elem(dtype)))
 
@@ -211,6 +221,38 @@ def moe_dispatch(slot_expert, N, workspace, out=None):
         _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
     _check(rc, "moe_dispatch")
     return out
+
+
+def moe_routing_fused(logits, is_visual, entropy_w, modality, sim, prot, k, R,
+                      kprime, rho, group, gamma, lam, workspace, topk_ids,
+                      topk_gates, fallback_ids, slot_sere, cap, disp):
+    """Route, SERE, capacity and dispatch in one launch; fills the given
+    buffers exactly as the four separate calls would."""
+    T, N = logits.shape
+    rc = _lib.moe_routing_fused(
+        _dev(logits, torch.float32, "logits"),
+        _dev(is_visual, torch.uint8, "is_visual", (T,)),
+        _dev(entropy_w, torch.float32, "entropy_w", (T,)),
+        _dev(modality, torch.int8, "modality", (N,)),
+        _opt(sim, torch.float32, "sim", (N, N)) if kprime else None,
+        _opt(prot, torch.uint8, "prot", (N, N)) if kprime else None,
+        T, N, k, R, kprime, float(rho), group, float(gamma), float(lam),
+        _dev(topk_ids, torch.int32, "topk_ids", (T, k)),
+        _dev(topk_gates, torch.float32, "topk_gates", (T, k)),
+        _dev(fallback_ids, torch.int32, "fallback_ids", (T, R)) if R > 0 else None,
+        _dev(slot_sere, torch.int32, "slot_sere", (T, k)) if kprime else None,
+        _dev(cap["slot_out"], torch.int32, "slot_out", (T, k)),
+        _dev(cap["flags"], torch.uint8, "flags", (T, k)),
+        _dev(cap["load_q"], torch.int64, "load_q", (N,)),
+        _dev(cap["cap_q"], torch.int64, "cap_q", (N,)),
+        _dev(cap["stats"], torch.int64, "stats", (4,)),
+        _dev(cap["r_v"], torch.float64, "r_v", (1,)),
+        _dev(disp["expert_offsets"], torch.int32, "expert_offsets", (N + 1,)),
+        _dev(disp["row_token"], torch.int32, "row_token", (T * k,)),
+        _dev(disp["row_slot"], torch.int32, "row_slot", (T * k,)),
+        _dev(disp["slot_row"], torch.int32, "slot_row", (T, k)),
+        _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
+    _check(rc, "moe_routing_fused")
 
 
 def moe_expert_ffn(x, row_token, expert_offsets, w13, w2, k, workspace,
@@ -274,9 +316,10 @@ def moe_combine(out_rows, slot_row, topk_gates, y=None):
 
 # ------------------------------------------------------------- one layer
 class Layer:
-    """Preallocated buffers for one layer shape; ``forward`` enqueues the six
+    """Preallocated buffers for one layer shape; ``forward`` enqueues the
     calls on the current stream (route -> SERE -> capacity -> dispatch ->
-    expert FFN -> combine) with no host synchronisation."""
+    expert FFN -> combine) with no host synchronisation.  Decode-sized
+    batches route with the single fused launch unless ``fused=False``."""
 
     def __init__(self, T, H, N, k, I, R, dtype, device="cuda"):
         self.T, self.H, self.N, self.k, self.I, self.R = T, H, N, k, I, R
@@ -301,11 +344,26 @@ class Layer:
         self.ws_cap = new_workspace(moe_capacity_workspace_size(T, N, k), dev)
         self.ws_disp = new_workspace(moe_dispatch_workspace_size(T, N, k), dev)
         self.ws_ffn = new_workspace(moe_ffn_workspace_size(T, N, k, H, I, dtype), dev)
+        ws_route = moe_routing_workspace_size(T, N, k, R)
+        self.can_fuse = ws_route > 0
+        self.ws_route = new_workspace(ws_route, dev) if self.can_fuse else None
 
-    def forward(self, logits, x, w13, w2, is_visual, entropy_w, modality,
-                sim=None, prot=None, kprime=0, rho=0.5, gamma=math.inf,
-                lam=1.0, group=None):
+    def routing(self, logits, is_visual, entropy_w, modality, sim=None,
+                prot=None, kprime=0, rho=0.5, gamma=math.inf, lam=1.0,
+                group=None, fused=None):
+        """Route, re-route, assign capacity and dispatch (fused launch or the
+        four separate calls)."""
         N, k, R = self.N, self.k, self.R
+        group = N if group is None else group
+        if fused is None:
+            fused = self.can_fuse
+        if fused:
+            moe_routing_fused(logits, is_visual, entropy_w, modality, sim, prot,
+                              k, R, kprime, rho, group, gamma, lam,
+                              self.ws_route, self.topk_ids, self.topk_gates,
+                              self.fallback_ids, self.slot_sere, self.cap,
+                              self.disp)
+            return
         moe_route(logits, k, R, self.topk_ids, self.topk_gates, self.fallback_ids)
         slot_in = self.topk_ids
         if kprime:
@@ -313,10 +371,16 @@ class Layer:
                              self.slot_sere, self.flags_sere)
             slot_in = self.slot_sere
         moe_capacity_assign(self.topk_ids, slot_in, self.fallback_ids,
-                            is_visual, entropy_w, modality, N, R,
-                            N if group is None else group, gamma, lam,
-                            self.ws_cap, self.cap)
+                            is_visual, entropy_w, modality, N, R, group, gamma,
+                            lam, self.ws_cap, self.cap)
         moe_dispatch(self.cap["slot_out"], N, self.ws_disp, self.disp)
+
+    def forward(self, logits, x, w13, w2, is_visual, entropy_w, modality,
+                sim=None, prot=None, kprime=0, rho=0.5, gamma=math.inf,
+                lam=1.0, group=None, fused=None):
+        k = self.k
+        self.routing(logits, is_visual, entropy_w, modality, sim, prot, kprime,
+                     rho, gamma, lam, group, fused)
         moe_expert_ffn(x, self.disp["row_token"], self.disp["expert_offsets"],
                        w13, w2, k, self.ws_ffn, self.out_rows)
         moe_combine(self.out_rows, self.disp["slot_row"], self.topk_gates, self.y)

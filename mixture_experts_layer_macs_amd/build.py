@@ -1,10 +1,10 @@
 """Build libmoe_macs.so (gfx950) in-tree with hipcc.
 
 Each HIP source is compiled to an object in parallel, then linked into one
-shared library next to this file.  The capacity unit is compiled with
--ffp-contract=off so its double-precision capacity formula is evaluated one
-rounded operation at a time.  Packed fp32 instructions are disabled for all
-device code.
+shared library next to this file.  The units that evaluate the
+double-precision capacity formula (capacity and fused routing) are compiled
+with -ffp-contract=off, so it is evaluated one rounded operation at a time.
+Packed fp32 instructions are disabled for all device code.
 """
 from __future__ import annotations
 
@@ -18,8 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_macs.so")
-SOURCES = ["route.hip", "sere.hip", "capacity.hip", "dispatch.hip", "ffn.hip",
-           "combine.hip"]
+SOURCES = ["route.hip", "sere.hip", "capacity.hip", "dispatch.hip",
+           "routing_fused.hip", "ffn.hip", "combine.hip"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 
@@ -35,7 +35,7 @@ def _flags(src: str) -> list:
     f = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-command-line-argument"]
-    if src == "capacity.hip":
+    if src in ("capacity.hip", "routing_fused.hip"):
         f.append("-ffp-contract=off")
     return f
 

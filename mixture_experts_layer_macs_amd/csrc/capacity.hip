@@ -1,457 +1,23 @@
 // moe_capacity_assign: MACS entropy-weighted load, modality-adaptive
 // capacity and re-route-else-drop ("MACS", §3.1 Eq. 3, §3.2 Eq. 5-6,
-// §3.3 Eq. 7 with the expert modality indicator m_j, §1 and Fig. 1 for the
-// two-stage overflow handling).
-//
-// This translation unit is compiled with -ffp-contract=off: the capacity is
-// computed in IEEE double, one rounded operation per step, in a fixed order.
-//
-// Work decomposition.  Tokens are split into G contiguous blocks of TB
-// tokens, one workgroup each.  Every round has the same shape:
-//   propose  each workgroup lists its proposals in (token, slot) order and
-//            computes, per expert, the inclusive running weight of its own
-//            proposals (an ordered per-key prefix: 64-lane chunks, peers
-//            found by ballots over the key bits, a per-wave running total in
-//            LDS, then a per-expert scan over the waves);
-//   global   the last workgroup to finish (an atomic ticket that wraps back
-//            to zero) scans the per-workgroup totals over the blocks, so
-//            every proposal's global running weight is block base + local;
-//   apply    at the start of the next launch each proposal is admitted iff
-//            its global running weight is within the expert's remaining
-//            capacity -- exactly the sequential prefix rule, because block
-//            order is token order.
-// Loads, sums and capacities are integers in units of 2^-16 token, so the
-// parallel sums equal the sequential ones bit for bit.  When the whole batch
-// fits one workgroup (decode), all rounds run in one launch.
-#include <math.h>
-
-#include <algorithm>
-#include <cmath>
-
-#include "common.h"
+// §3.3 Eq. 7, §1 and Fig. 1).  The phases live in capacity_impl.h; this
+// file holds the kernels and the entry point.  When the whole batch fits
+// one workgroup (decode) all rounds run in one launch; otherwise each round
+// is one launch over the token blocks.
+#include "capacity_impl.h"
 
 namespace moe {
 namespace cap {
 
-enum : uint8_t { ST_KEPT = 0, ST_OVER = 1, ST_PLACED = 2, ST_MASK = 3,
-                 ST_SERE = 4 };
-
-constexpr int64_t CAP_CLAMP = int64_t(1) << 62;
-
-struct Args {
-  const int32_t* topk;
-  const int32_t* slot_in;
-  const int32_t* fallback;
-  const uint8_t* is_visual;
-  const float* entropy_w;
-  const int8_t* modality;
-  int T, N, k, R, group, nbits;
-  double gamma, lam;
-  int32_t* slot_out;
-  uint8_t* flags;
-  int64_t* load_q;
-  int64_t* cap_q;
-  int64_t* stats;
-  double* r_v;
-  // workspace
-  int32_t* wq;         // [T]      token weight (fixed point)
-  int32_t* cur;        // [T*k]    current expert of each slot
-  uint8_t* st;         // [T*k]    slot state | ST_SERE
-  int32_t* incl_slot;  // [T*k]    in-block running weight, round 0
-  int32_t* incl_tok;   // [T]      in-block running weight, rounds >= 1
-  int32_t* offer_s;    // [T]      offered slot this round (-1 = none)
-  int32_t* offer_c;    // [T]      offered expert this round
-  int32_t* part;       // [G*N]    per-block per-expert proposal weight
-  int64_t* base;       // [G*N]    exclusive block prefix of part
-  int64_t* wsum;       // [G*4]    per-block {W, W_vis, dropped, rerouted}
-  int64_t* capv;       // [N]
-  int64_t* drem;       // [N]      capacity left for the pending round
-  uint8_t* active;     // [N]
-  // control words: zero between calls (each is cleared after its last use)
-  unsigned* ticket;                 // [1]
-  uint32_t* act_bits;               // [32]  experts with a round-0 proposer
-  unsigned long long* adm;          // [N]   max admitted running weight
-  unsigned long long* total;        // [N]   proposal weight (capacity off)
-  int TB, G, lds_scan;
-};
-
-__device__ __forceinline__ int32_t quant_weight(uint8_t vis, float w) {
-  if (!vis) return MOE_WEIGHT_ONE;
-  if (isnan(w)) w = 1.f;
-  w = fminf(fmaxf(w, 0.f), 1.f);
-  return static_cast<int32_t>(rintf(w * 65536.f));  // exact scale, half-even
-}
-
-__device__ int64_t capacity_of(const Args& a, double rv, int e) {
-  const double base = ((a.gamma * static_cast<double>(a.T)) *
-                       static_cast<double>(a.k)) / static_cast<double>(a.N);
-  const double scale = a.lam * static_cast<double>(a.modality[e]);
-  double c = base * (1.0 + scale * (rv - 0.5));
-  c = (1.0 > c) ? 1.0 : c;
-  const double cq = c * 65536.0;
-  return cq >= 4611686018427387904.0 ? CAP_CLAMP
-                                     : static_cast<int64_t>(floor(cq));
-}
-
-// ---------------------------------------------------------------- phases
-// Round-0 proposals: every slot, in (token, slot) order.
-__device__ void propose0(const Args& a, int g, int t0, int t1, int32_t* run,
-                         uint32_t* act_bits, int64_t* red) {
-  const int tid = threadIdx.x, nthr = blockDim.x, k = a.k;
-  int64_t w_all = 0, w_vis = 0;
-  for (int t = t0 + tid; t < t1; t += nthr) {
-    const int32_t q = quant_weight(a.is_visual[t], a.entropy_w[t]);
-    a.wq[t] = q;
-    w_all += q;
-    if (a.is_visual[t]) w_vis += q;
-  }
-  for (int i = t0 * k + tid; i < t1 * k; i += nthr) {
-    const int32_t e = a.slot_in[i];
-    a.cur[i] = e;
-    a.st[i] = (e != a.topk[i]) ? ST_SERE : ST_KEPT;
-  }
-  if (tid < 32) act_bits[tid] = 0u;
-  w_all = block_sum_i64(w_all, red);
-  w_vis = block_sum_i64(w_vis, red);
-  if (tid == 0) {
-    a.wsum[g * 4 + 0] = w_all;
-    a.wsum[g * 4 + 1] = w_vis;
-  }
-  const int32_t* cur = a.cur + static_cast<size_t>(t0) * k;
-  const int32_t* wq = a.wq;
-  key_prefix((t1 - t0) * k, a.N, a.nbits, run,
-             [&](int idx, int& key, int32_t& w) {
-               key = cur[idx];
-               w = wq[t0 + idx / k];
-             },
-             a.incl_slot + static_cast<size_t>(t0) * k,
-             a.part + static_cast<size_t>(g) * a.N, act_bits);
-  if (tid < 32 && act_bits[tid]) atomicOr(&a.act_bits[tid], act_bits[tid]);
-}
-
-// Offers of fallback round r >= 1: one per token with an unplaced overflow.
-__device__ void propose_round(const Args& a, int r, int g, int t0, int t1,
-                              int32_t* run) {
-  const int tid = threadIdx.x, nthr = blockDim.x, k = a.k;
-  for (int t = t0 + tid; t < t1; t += nthr) {
-    const int32_t* cs = a.cur + static_cast<size_t>(t) * k;
-    const uint8_t* ss = a.st + static_cast<size_t>(t) * k;
-    int s_off = -1;
-    for (int s = 0; s < k; ++s)
-      if ((ss[s] & ST_MASK) == ST_OVER) {
-        s_off = s;
-        break;
-      }
-    int c = -1;
-    if (s_off >= 0) {
-      c = a.fallback[static_cast<size_t>(t) * a.R + (r - 1)];
-      const int e = cs[s_off];
-      bool ok = a.active[c] && (c / a.group) == (e / a.group);
-      for (int s = 0; s < k && ok; ++s) ok = cs[s] != c;
-      if (!ok) s_off = -1;
-    }
-    a.offer_s[t] = s_off;
-    a.offer_c[t] = s_off >= 0 ? c : -1;
-  }
-  __syncthreads();
-  const int32_t* oc = a.offer_c + t0;
-  const int32_t* wq = a.wq + t0;
-  key_prefix(t1 - t0, a.N, a.nbits, run,
-             [&](int idx, int& key, int32_t& w) {
-               key = oc[idx];
-               w = wq[idx];
-             },
-             a.incl_tok + t0, a.part + static_cast<size_t>(g) * a.N,
-             nullptr);
-}
-
-// Admit or refuse the proposals of round r (decided against base and drem
-// from the global step of round r).
-__device__ void apply(const Args& a, int r, int g, int t0, int t1,
-                      unsigned long long* amax) {
-  const int tid = threadIdx.x, nthr = blockDim.x, k = a.k, N = a.N;
-  for (int e = tid; e < N; e += nthr) amax[e] = 0ull;
-  __syncthreads();
-  const int64_t* base = a.base + static_cast<size_t>(g) * N;
-  if (r == 0) {
-    for (int i = t0 * k + tid; i < t1 * k; i += nthr) {
-      const int e = a.cur[i];
-      const int64_t v = base[e] + a.incl_slot[i];
-      if (v <= a.drem[e])
-        atomicMax(&amax[e], static_cast<unsigned long long>(v));
-      else
-        a.st[i] = (a.st[i] & ST_SERE) | ST_OVER;
-    }
-  } else {
-    for (int t = t0 + tid; t < t1; t += nthr) {
-      const int s = a.offer_s[t];
-      if (s < 0) continue;
-      const int c = a.offer_c[t];
-      const int64_t v = base[c] + a.incl_tok[t];
-      if (v <= a.drem[c]) {
-        const size_t i = static_cast<size_t>(t) * k + s;
-        a.st[i] = (a.st[i] & ST_SERE) | ST_PLACED;
-        a.cur[i] = c;
-        atomicMax(&amax[c], static_cast<unsigned long long>(v));
-      }
-    }
-  }
-  __syncthreads();
-  for (int e = tid; e < N; e += nthr)
-    if (amax[e]) atomicMax(&a.adm[e], amax[e]);
-}
-
-__device__ void finalize_slots(const Args& a, int g, int t0, int t1,
-                               int64_t* red) {
-  const int tid = threadIdx.x, nthr = blockDim.x, k = a.k;
-  int64_t n_drop = 0, n_macs = 0;
-  for (int i = t0 * k + tid; i < t1 * k; i += nthr) {
-    const uint8_t s = a.st[i];
-    uint8_t f = (s & ST_SERE) ? MOE_FLAG_SERE : 0;
-    int32_t o = a.cur[i];
-    if ((s & ST_MASK) == ST_OVER) {
-      o = -1;
-      f |= MOE_FLAG_DROP;
-      ++n_drop;
-    } else if ((s & ST_MASK) == ST_PLACED) {
-      f |= MOE_FLAG_MACS;
-      ++n_macs;
-    }
-    a.slot_out[i] = o;
-    a.flags[i] = f;
-  }
-  n_drop = block_sum_i64(n_drop, red);
-  n_macs = block_sum_i64(n_macs, red);
-  if (tid == 0) {
-    a.wsum[g * 4 + 2] = n_drop;
-    a.wsum[g * 4 + 3] = n_macs;
-  }
-}
-
-// Global step after round r's proposals (r <= R) or after the last apply
-// (r == R + 1).  Run by exactly one workgroup.
-__device__ void global_step(const Args& a, int r, int64_t* red, int32_t* lds) {
-  const int tid = threadIdx.x, nthr = blockDim.x, N = a.N, G = a.G;
-  __shared__ double s_rv;
-  if (r == 0) {
-    int64_t w_all = 0, w_vis = 0;
-    for (int g = tid; g < G; g += nthr) {
-      w_all += a.wsum[g * 4 + 0];
-      w_vis += a.wsum[g * 4 + 1];
-    }
-    w_all = block_sum_i64(w_all, red);
-    w_vis = block_sum_i64(w_vis, red);
-    if (tid == 0) {
-      const double rv = w_all > 0 ? static_cast<double>(w_vis) /
-                                        static_cast<double>(w_all)
-                                  : 0.5;
-      s_rv = rv;
-      a.r_v[0] = rv;
-      a.stats[0] = w_all;
-      a.stats[1] = w_vis;
-    }
-    __syncthreads();
-    const double rv = s_rv;
-    for (int e = tid; e < N; e += nthr) {
-      const int64_t c = capacity_of(a, rv, e);
-      a.capv[e] = c;
-      a.cap_q[e] = c;
-      a.drem[e] = c;
-      a.active[e] = (a.act_bits[e >> 5] >> (e & 31)) & 1u;
-    }
-    __syncthreads();
-    if (tid < 32) a.act_bits[tid] = 0u;
-  } else {
-    for (int e = tid; e < N; e += nthr) {
-      const int64_t m = static_cast<int64_t>(a.adm[e]);
-      a.adm[e] = 0ull;
-      const int64_t d = a.drem[e] - m;
-      a.drem[e] = d;
-      if (r > a.R) a.load_q[e] = a.capv[e] - d;
-    }
-  }
-  if (r <= a.R) {
-    column_scan<int64_t>(a.part, a.base, nullptr, G, N, lds, a.lds_scan);
-  } else {
-    int64_t nd = 0, nm = 0;
-    for (int g = tid; g < G; g += nthr) {
-      nd += a.wsum[g * 4 + 2];
-      nm += a.wsum[g * 4 + 3];
-    }
-    nd = block_sum_i64(nd, red);
-    nm = block_sum_i64(nm, red);
-    if (tid == 0) {
-      a.stats[2] = nd;
-      a.stats[3] = nm;
-    }
-  }
-}
-
-// True in every thread of the workgroup that finished last (G > 1).
-__device__ bool last_block(const Args& a) {
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = atomicInc(a.ticket, static_cast<unsigned>(a.G - 1));
-    s_last = prev == static_cast<unsigned>(a.G - 1);
-  }
-  __syncthreads();
-  const bool last = s_last != 0;
-  if (last) __threadfence();
-  return last;
-}
-
-// Rounds r_first..r_last (r = 0: round-0 proposals; 1..R: apply the previous
-// round, then offers; R+1: apply the last round and write the outputs).
 __global__ __launch_bounds__(1024) void cap_kernel(Args a, int r_first,
                                                    int r_last) {
   extern __shared__ __align__(16) unsigned char smem[];
-  // [amax: N u64][run table / column-scan staging: lds_scan int32]
-  unsigned long long* amax = reinterpret_cast<unsigned long long*>(smem);
-  int32_t* run = reinterpret_cast<int32_t*>(smem + sizeof(unsigned long long) * a.N);
-  __shared__ uint32_t act_bits[32];
-  __shared__ int64_t red[16];
-  const int g = blockIdx.x;
-  const int t0 = g * a.TB, t1 = min(a.T, t0 + a.TB);
-  for (int r = r_first; r <= r_last; ++r) {
-    if (r >= 1) {
-      apply(a, r - 1, g, t0, t1, amax);
-      __syncthreads();
-    }
-    if (r == 0)
-      propose0(a, g, t0, t1, run, act_bits, red);
-    else if (r <= a.R)
-      propose_round(a, r, g, t0, t1, run);
-    else
-      finalize_slots(a, g, t0, t1, red);
-    if (a.G > 1) {
-      if (!last_block(a)) return;
-    } else {
-      __syncthreads();
-    }
-    global_step(a, r, red, run);
-    __syncthreads();
-  }
+  cap_rounds(a, blockIdx.x, r_first, r_last, smem);
 }
 
-// Capacity off: everything kept; loads are the plain weight totals.
 __global__ __launch_bounds__(1024) void cap_off_kernel(Args a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned long long* tot = reinterpret_cast<unsigned long long*>(smem);
-  __shared__ int64_t red[16];
-  const int tid = threadIdx.x, nthr = blockDim.x, k = a.k, N = a.N;
-  const int g = blockIdx.x;
-  const int t0 = g * a.TB, t1 = min(a.T, t0 + a.TB);
-  for (int e = tid; e < N; e += nthr) tot[e] = 0ull;
-  __syncthreads();
-  int64_t w_all = 0, w_vis = 0;
-  for (int t = t0 + tid; t < t1; t += nthr) {
-    const int32_t q = quant_weight(a.is_visual[t], a.entropy_w[t]);
-    w_all += q;
-    if (a.is_visual[t]) w_vis += q;
-    for (int s = 0; s < k; ++s) {
-      const size_t i = static_cast<size_t>(t) * k + s;
-      const int32_t e = a.slot_in[i];
-      atomicAdd(&tot[e], static_cast<unsigned long long>(q));
-      a.slot_out[i] = e;
-      a.flags[i] = (e != a.topk[i]) ? MOE_FLAG_SERE : 0;
-    }
-  }
-  w_all = block_sum_i64(w_all, red);
-  w_vis = block_sum_i64(w_vis, red);
-  __syncthreads();
-  if (tid == 0) {
-    a.wsum[g * 4 + 0] = w_all;
-    a.wsum[g * 4 + 1] = w_vis;
-  }
-  if (a.G > 1) {
-    for (int e = tid; e < N; e += nthr)
-      if (tot[e]) atomicAdd(&a.total[e], tot[e]);
-    if (!last_block(a)) return;
-  } else {
-    __syncthreads();
-  }
-  int64_t W = w_all, Wv = w_vis;
-  if (a.G > 1) {
-    W = Wv = 0;
-    for (int b = tid; b < a.G; b += nthr) {
-      W += a.wsum[b * 4 + 0];
-      Wv += a.wsum[b * 4 + 1];
-    }
-    W = block_sum_i64(W, red);
-    Wv = block_sum_i64(Wv, red);
-  }
-  if (tid == 0) {
-    a.r_v[0] = W > 0 ? static_cast<double>(Wv) / static_cast<double>(W) : 0.5;
-    a.stats[0] = W;
-    a.stats[1] = Wv;
-    a.stats[2] = 0;
-    a.stats[3] = 0;
-  }
-  for (int e = tid; e < N; e += nthr) {
-    if (a.G > 1) {
-      a.load_q[e] = static_cast<int64_t>(a.total[e]);
-      a.total[e] = 0ull;
-    } else {
-      a.load_q[e] = static_cast<int64_t>(tot[e]);
-    }
-    a.cap_q[e] = INT64_MAX;
-  }
-}
-
-// ------------------------------------------------------------------ host
-// Workspace: a fixed control block (zero between calls, independent of T so
-// one workspace serves any batch size), then the per-call arrays.
-constexpr size_t CTRL_TICKET = 0;
-constexpr size_t CTRL_ACT = 256;
-constexpr size_t CTRL_ADM = 512;
-constexpr size_t CTRL_TOTAL = CTRL_ADM + 8 * 1024;
-constexpr size_t CTRL_BYTES = CTRL_TOTAL + 8 * 1024;
-constexpr int SCAN_LDS = 8192;  // int32 staging for the block-prefix scan
-
-struct Layout {
-  int G, TB, threads;
-  size_t wq, cur, st, incl_slot, incl_tok, offer_s, offer_c, part, base, wsum,
-      capv, drem, active, bytes;
-};
-
-static size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
-
-static Layout layout(int T, int N, int k) {
-  Layout L{};
-  const long items = static_cast<long>(T) * k;
-  if (items <= 8192) {
-    L.G = 1;
-    L.TB = T > 0 ? T : 1;
-    L.threads = 1024;
-  } else {
-    L.TB = k >= 1024 ? 1 : 1024 / k;
-    L.G = (T + L.TB - 1) / L.TB;
-    L.threads = 256;
-  }
-  size_t o = CTRL_BYTES;
-  auto take = [&](size_t n) {
-    const size_t at = o;
-    o = align_up(o + n);
-    return at;
-  };
-  const size_t Tk = static_cast<size_t>(T) * k, GN = static_cast<size_t>(L.G) * N;
-  L.wq = take(sizeof(int32_t) * T);
-  L.cur = take(sizeof(int32_t) * Tk);
-  L.st = take(Tk);
-  L.incl_slot = take(sizeof(int32_t) * Tk);
-  L.incl_tok = take(sizeof(int32_t) * T);
-  L.offer_s = take(sizeof(int32_t) * T);
-  L.offer_c = take(sizeof(int32_t) * T);
-  L.part = take(sizeof(int32_t) * GN);
-  L.base = take(sizeof(int64_t) * GN);
-  L.wsum = take(sizeof(int64_t) * 4 * L.G);
-  L.capv = take(sizeof(int64_t) * N);
-  L.drem = take(sizeof(int64_t) * N);
-  L.active = take(N);
-  L.bytes = o;
-  return L;
+  cap_off(a, blockIdx.x, smem);
 }
 
 }  // namespace cap
@@ -485,60 +51,17 @@ extern "C" int moe_capacity_assign(
     return MOE_EINVAL;
   const Layout L = layout(T, N, k);
   if (workspace_bytes < L.bytes) return MOE_EINVAL;
-  char* ws = static_cast<char*>(workspace);
-  Args a{};
-  a.topk = topk_ids;
-  a.slot_in = slot_in;
-  a.fallback = fallback_ids;
-  a.is_visual = is_visual;
-  a.entropy_w = entropy_w;
-  a.modality = modality;
-  a.T = T;
-  a.N = N;
-  a.k = k;
-  a.R = R;
-  a.group = group;
-  int nb = 1;
-  while ((1 << nb) < N) ++nb;
-  a.nbits = nb;
-  a.gamma = gamma;
-  a.lam = lam;
-  a.slot_out = slot_out;
-  a.flags = flags;
-  a.load_q = load_q;
-  a.cap_q = cap_q;
-  a.stats = stats;
-  a.r_v = r_v;
-  a.wq = reinterpret_cast<int32_t*>(ws + L.wq);
-  a.cur = reinterpret_cast<int32_t*>(ws + L.cur);
-  a.st = reinterpret_cast<uint8_t*>(ws + L.st);
-  a.incl_slot = reinterpret_cast<int32_t*>(ws + L.incl_slot);
-  a.incl_tok = reinterpret_cast<int32_t*>(ws + L.incl_tok);
-  a.offer_s = reinterpret_cast<int32_t*>(ws + L.offer_s);
-  a.offer_c = reinterpret_cast<int32_t*>(ws + L.offer_c);
-  a.part = reinterpret_cast<int32_t*>(ws + L.part);
-  a.base = reinterpret_cast<int64_t*>(ws + L.base);
-  a.wsum = reinterpret_cast<int64_t*>(ws + L.wsum);
-  a.capv = reinterpret_cast<int64_t*>(ws + L.capv);
-  a.drem = reinterpret_cast<int64_t*>(ws + L.drem);
-  a.active = reinterpret_cast<uint8_t*>(ws + L.active);
-  a.ticket = reinterpret_cast<unsigned*>(ws + CTRL_TICKET);
-  a.act_bits = reinterpret_cast<uint32_t*>(ws + CTRL_ACT);
-  a.adm = reinterpret_cast<unsigned long long*>(ws + CTRL_ADM);
-  a.total = reinterpret_cast<unsigned long long*>(ws + CTRL_TOTAL);
-  a.TB = L.TB;
-  a.G = L.G;
-
+  const Args a = make_args(topk_ids, slot_in, fallback_ids, is_visual,
+                           entropy_w, modality, T, N, k, R, group, gamma, lam,
+                           slot_out, flags, load_q, cap_q, stats, r_v,
+                           static_cast<char*>(workspace), L);
   hipStream_t s = as_stream(stream);
   const dim3 grid(L.G), block(L.threads);
-  const int W = L.threads / MOE_WAVE;
   if (std::isinf(gamma)) {
-    const size_t lds = sizeof(unsigned long long) * N;
-    hipLaunchKernelGGL(cap_off_kernel, grid, block, lds, s, a);
+    hipLaunchKernelGGL(cap_off_kernel, grid, block, off_lds_bytes(a), s, a);
     return launch_status();
   }
-  a.lds_scan = std::max(W * N, SCAN_LDS);
-  const size_t lds = sizeof(unsigned long long) * N + sizeof(int32_t) * a.lds_scan;
+  const size_t lds = rounds_lds_bytes(a);
   if (lds > 65536 &&
       hipFuncSetAttribute(reinterpret_cast<const void*>(cap_kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize,

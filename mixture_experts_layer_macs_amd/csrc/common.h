@@ -31,51 +31,114 @@ __device__ __forceinline__ uint64_t lanemask_le() {
   return l == 63 ? ~0ull : ((2ull << l) - 1ull);
 }
 
+// ------------------------------------------------ DPP wave primitives
+// Cross-lane steps use DPP row operations (a VALU operand modifier, a few
+// cycles each) instead of LDS-crossbar shuffles (ds_bpermute, about a
+// hundred cycles each), so a full-wave reduction or scan costs six dependent
+// VALU steps.  Every lane of the wave must be active.
+enum : int {
+  DPP_QUAD_1032 = 0xb1,  // lane ^ 1 inside each quad
+  DPP_QUAD_2301 = 0x4e,  // lane ^ 2 inside each quad
+  DPP_ROW_SHR1 = 0x111,  // lane - n inside each row of 16
+  DPP_ROW_SHR2 = 0x112,
+  DPP_ROW_SHR4 = 0x114,
+  DPP_ROW_SHR8 = 0x118,
+  DPP_ROW_BCAST15 = 0x142,  // lane 15 of each row into the next row
+  DPP_ROW_BCAST31 = 0x143,  // lane 31 into rows 2 and 3
+};
+
+// Value of the DPP source lane; lanes without a source (or outside
+// ROW_MASK) get `old`.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      static_cast<int>(old), static_cast<int>(v), CTRL, ROW_MASK, 0xf, false));
+}
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint64_t dpp64(uint64_t old, uint64_t v) {
+  const uint32_t lo = dpp<CTRL, ROW_MASK>(static_cast<uint32_t>(old),
+                                          static_cast<uint32_t>(v));
+  const uint32_t hi = dpp<CTRL, ROW_MASK>(static_cast<uint32_t>(old >> 32),
+                                          static_cast<uint32_t>(v >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint32_t bits_of(float v) { return __float_as_uint(v); }
+__device__ __forceinline__ uint32_t bits_of(int v) { return static_cast<uint32_t>(v); }
+__device__ __forceinline__ uint32_t bits_of(uint32_t v) { return v; }
+template <typename T> __device__ __forceinline__ T from_bits(uint32_t b);
+template <> __device__ __forceinline__ float from_bits<float>(uint32_t b) { return __uint_as_float(b); }
+template <> __device__ __forceinline__ int from_bits<int>(uint32_t b) { return static_cast<int>(b); }
+template <> __device__ __forceinline__ uint32_t from_bits<uint32_t>(uint32_t b) { return b; }
+
+template <typename T, int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ T dpp_t(T ident, T v) {
+  return from_bits<T>(dpp<CTRL, ROW_MASK>(bits_of(ident), bits_of(v)));
+}
+
+// Full-wave reduction; the result (lane 63's total) is returned to every
+// lane.  `ident` is the identity of `op`.
+template <typename T, class Op>
+__device__ __forceinline__ T wave_reduce(T v, T ident, Op op) {
+  v = op(v, dpp_t<T, DPP_QUAD_1032>(ident, v));
+  v = op(v, dpp_t<T, DPP_QUAD_2301>(ident, v));
+  v = op(v, dpp_t<T, DPP_ROW_SHR4>(ident, v));
+  v = op(v, dpp_t<T, DPP_ROW_SHR8>(ident, v));
+  v = op(v, dpp_t<T, DPP_ROW_BCAST15, 0xa>(ident, v));
+  v = op(v, dpp_t<T, DPP_ROW_BCAST31, 0xc>(ident, v));
+  return from_bits<T>(static_cast<uint32_t>(
+      __builtin_amdgcn_readlane(static_cast<int>(bits_of(v)), 63)));
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, MOE_WAVE);
-  return v;
+  return wave_reduce<T>(v, T(0), [](T a, T b) { return a + b; });
 }
 
-template <typename T>
-__device__ __forceinline__ T wave_max(T v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    T o = __shfl_xor(v, off, MOE_WAVE);
-    v = o > v ? o : v;
-  }
-  return v;
+__device__ __forceinline__ float wave_max(float v) {
+  return wave_reduce<float>(v, -INFINITY, [](float a, float b) { return fmaxf(a, b); });
+}
+__device__ __forceinline__ int wave_max(int v) {
+  return wave_reduce<int>(v, INT32_MIN, [](int a, int b) { return a > b ? a : b; });
 }
 
-__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
-  uint32_t lo = __shfl(static_cast<uint32_t>(v), src, MOE_WAVE);
-  uint32_t hi = __shfl(static_cast<uint32_t>(v >> 32), src, MOE_WAVE);
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(v), lane);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(v >> 32), lane);
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, MOE_WAVE);
-    uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, MOE_WAVE);
-    uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+  auto mx = [](uint64_t a, uint64_t b) { return a > b ? a : b; };
+  v = mx(v, dpp64<DPP_QUAD_1032>(0ull, v));
+  v = mx(v, dpp64<DPP_QUAD_2301>(0ull, v));
+  v = mx(v, dpp64<DPP_ROW_SHR4>(0ull, v));
+  v = mx(v, dpp64<DPP_ROW_SHR8>(0ull, v));
+  v = mx(v, dpp64<DPP_ROW_BCAST15, 0xa>(0ull, v));
+  v = mx(v, dpp64<DPP_ROW_BCAST31, 0xc>(0ull, v));
+  return readlane64(v, 63);
 }
 
 // Inclusive prefix sum across the wave (lane order).
 template <typename T>
 __device__ __forceinline__ T wave_incl_scan(T v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    T o = __shfl_up(v, off, MOE_WAVE);
-    if (l >= off) v += o;
-  }
+  v = v + dpp_t<T, DPP_ROW_SHR1>(T(0), v);
+  v = v + dpp_t<T, DPP_ROW_SHR2>(T(0), v);
+  v = v + dpp_t<T, DPP_ROW_SHR4>(T(0), v);
+  v = v + dpp_t<T, DPP_ROW_SHR8>(T(0), v);
+  v = v + dpp_t<T, DPP_ROW_BCAST15, 0xa>(T(0), v);
+  v = v + dpp_t<T, DPP_ROW_BCAST31, 0xc>(T(0), v);
   return v;
 }
+
+// Value held by `lane` (wave-uniform lane index).
+__device__ __forceinline__ int read_lane(int v, int lane) {
+  return __builtin_amdgcn_readlane(v, lane);
+}
+
+// Wait until this wave's global stores have completed (vector memory
+// counter at zero; LDS and export counters left alone).
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Monotone unsigned image of an fp32 value: a > b  <=>  key(a) > key(b);
 // -0.0 is folded onto +0.0 first so the two compare equal.
@@ -117,14 +180,14 @@ __device__ __forceinline__ float rank_key_value(uint64_t key) {
 }
 
 __device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, MOE_WAVE);
-    uint32_t hi = __shfl_xor(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32),
-                             off, MOE_WAVE);
-    v += static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
-  }
-  return v;
+  uint64_t u = static_cast<uint64_t>(v);
+  u += dpp64<DPP_QUAD_1032>(0ull, u);
+  u += dpp64<DPP_QUAD_2301>(0ull, u);
+  u += dpp64<DPP_ROW_SHR4>(0ull, u);
+  u += dpp64<DPP_ROW_SHR8>(0ull, u);
+  u += dpp64<DPP_ROW_BCAST15, 0xa>(0ull, u);
+  u += dpp64<DPP_ROW_BCAST31, 0xc>(0ull, u);
+  return static_cast<int64_t>(readlane64(u, 63));
 }
 
 // Block-wide sum of one int64 per thread; result valid in every thread.
@@ -144,7 +207,8 @@ __device__ inline int64_t block_sum_i64(int64_t v, int64_t* red) {
 // Items idx = 0..n-1 are in sequence order; key(idx) < 0 means "no item".
 // On return incl[idx] = sum of w over items j <= idx with the same key, and
 // part_row[key] = the block total of that key.  run: LDS [waves * N].
-template <class Get>
+// UNIT: every item weighs 1, so a lane's in-wave prefix is a popcount.
+template <bool UNIT = false, class Get>
 __device__ inline void key_prefix(int n, int N, int nbits, int32_t* run, Get get,
                            int32_t* incl, int32_t* part_row,
                            uint32_t* act_bits) {
@@ -164,14 +228,18 @@ __device__ inline void key_prefix(int n, int N, int nbits, int32_t* run, Get get
     const int valid = key >= 0;
     const uint64_t peers = match_any(key, valid, nbits);
     uint64_t m = peers & lanemask_le();
-    const int maxcnt = wave_max(__popcll(m));
     int32_t local = 0;
-    for (int c = 0; c < maxcnt; ++c) {  // uniform trip count: all lanes shuffle
-      const int j = m ? (__ffsll(static_cast<long long>(m)) - 1) : lane;
-      const int32_t v = __shfl(w, j, MOE_WAVE);
-      if (m) {
-        local += v;
-        m &= m - 1;
+    if constexpr (UNIT) {
+      local = __popcll(m);
+    } else {
+      const int maxcnt = wave_max(static_cast<int>(__popcll(m)));
+      for (int c = 0; c < maxcnt; ++c) {  // uniform trip count: all lanes shuffle
+        const int j = m ? (__ffsll(static_cast<long long>(m)) - 1) : lane;
+        const int32_t v = __shfl(w, j, MOE_WAVE);
+        if (m) {
+          local += v;
+          m &= m - 1;
+        }
       }
     }
     if (valid) {
@@ -182,12 +250,15 @@ __device__ inline void key_prefix(int n, int N, int nbits, int32_t* run, Get get
     }
   }
   __syncthreads();
-  for (int e = tid; e < N; e += nthr) {
+  for (int e = tid; e < N; e += nthr) {  // exclusive scan over the waves
+    int32_t t[16];  // W <= 16: all reads in flight before the first use
+#pragma unroll
+    for (int v = 0; v < 16; ++v) t[v] = v < W ? run[v * N + e] : 0;
     int32_t acc = 0;
-    for (int v = 0; v < W; ++v) {
-      const int32_t t = run[v * N + e];
-      run[v * N + e] = acc;
-      acc += t;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      if (v < W) run[v * N + e] = acc;
+      acc += t[v];
     }
     part_row[e] = acc;
   }

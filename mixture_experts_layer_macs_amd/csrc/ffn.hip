@@ -67,7 +67,7 @@ __device__ bool find_tile(const Args& a, int* cum, int& j, int& m0, int& nt,
       }
       const int inc = wave_incl_scan(cnt);
       if (e < a.N) cum[e + 1] = acc + inc;
-      acc += __shfl(inc, MOE_WAVE - 1, MOE_WAVE);
+      acc += read_lane(inc, MOE_WAVE - 1);
     }
     if (threadIdx.x == 0) {
       cum[0] = 0;

@@ -1,0 +1,114 @@
+// Router softmax and top-k for one token ("MACS", §3.1 Eq. 1), shared by the
+// stand-alone route kernel and the fused routing kernel.
+//
+// A group of GT threads (a whole number of waves) owns one token.  Its N
+// logits become 64-bit rank keys in LDS (order-preserving image of the fp32
+// value, then the inverted expert index, so a larger key means a better rank
+// and equal logits fall to the lower index).  The rank of expert e is the
+// number of keys above its own, counted directly: every thread compares one
+// expert's key against a span of the others (LDS broadcast reads, no
+// cross-lane traffic), and the partial counts meet in an LDS atomic.  The
+// k + R best ranks are then written straight to their output positions.  No
+// step depends on the previous pick, so the latency is a few hundred cycles
+// instead of k + R dependent wave-wide reductions.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+namespace rt {
+
+// LDS per token group: keys u64[N], ranks i32[N], reduction slots f32[GT/64]
+// (rounded up to 16 bytes so consecutive groups stay aligned).
+__host__ __device__ constexpr size_t token_lds_bytes(int N, int GT) {
+  return (static_cast<size_t>(N) * 12 + static_cast<size_t>(GT / MOE_WAVE) * 4 +
+          15) & ~static_cast<size_t>(15);
+}
+
+// Reduction over the GT threads of one token group.  Every thread of the
+// workgroup must call it (it synchronises the workgroup).
+template <int GT, bool MAX>
+__device__ __forceinline__ float group_reduce(float v, float* red) {
+  v = MAX ? wave_max(v) : wave_sum(v);
+  if constexpr (GT > MOE_WAVE) {
+    const int wv = (threadIdx.x % GT) / MOE_WAVE;
+    if (lane_id() == 0) red[wv] = v;
+    __syncthreads();
+    v = red[0];
+#pragma unroll
+    for (int i = 1; i < GT / MOE_WAVE; ++i) v = MAX ? fmaxf(v, red[i]) : v + red[i];
+    __syncthreads();
+  }
+  return v;
+}
+
+// Route token t (live == false: a padding group that only joins the
+// workgroup barriers).  Writes topk_ids[t][0..k), topk_gates[t][0..k) and
+// fallback_ids[t][0..R) in rank order.
+template <int GT>
+__device__ void route_token(const float* __restrict__ logits, int N, int k,
+                            int R, int t, bool live, unsigned char* lds,
+                            int32_t* __restrict__ topk_ids,
+                            float* __restrict__ topk_gates,
+                            int32_t* __restrict__ fallback_ids) {
+  uint64_t* key = reinterpret_cast<uint64_t*>(lds);
+  int* rank = reinterpret_cast<int*>(lds + static_cast<size_t>(N) * 8);
+  float* red = reinterpret_cast<float*>(lds + static_cast<size_t>(N) * 12);
+  const int g = threadIdx.x % GT;
+  const float* row = logits + static_cast<size_t>(t) * N;
+
+  float mx = -INFINITY;
+  if (live)
+    for (int j = g; j < N; j += GT) {
+      const float v = row[j];
+      key[j] = rank_key(v, j);
+      rank[j] = 0;
+      mx = fmaxf(mx, v);
+    }
+  mx = group_reduce<GT, true>(mx, red);
+  float se = 0.f;
+  if (live)
+    for (int j = g; j < N; j += GT) se += expf(rank_key_value(key[j]) - mx);
+  se = group_reduce<GT, false>(se, red);
+  __syncthreads();  // every key and zeroed rank visible to the whole group
+
+  if (live) {
+    if (N <= GT) {
+      // S threads per expert, each counting over one span of the keys
+      const int S = GT / N;
+      const int e = g % N, s = g / N;
+      if (s < S) {
+        const int span = (N + S - 1) / S;
+        const int j0 = s * span, j1 = min(N, j0 + span);
+        const uint64_t ke = key[e];
+        int c = 0;
+#pragma unroll 8
+        for (int j = j0; j < j1; ++j) c += key[j] > ke ? 1 : 0;
+        if (c) atomicAdd(&rank[e], c);
+      }
+    } else {
+      for (int e = g; e < N; e += GT) {
+        const uint64_t ke = key[e];
+        int c = 0;
+#pragma unroll 8
+        for (int j = 0; j < N; ++j) c += key[j] > ke ? 1 : 0;
+        rank[e] = c;
+      }
+    }
+  }
+  __syncthreads();
+  if (live)
+    for (int e = g; e < N; e += GT) {
+      const int r = rank[e];
+      if (r < k) {
+        topk_ids[static_cast<size_t>(t) * k + r] = e;
+        topk_gates[static_cast<size_t>(t) * k + r] =
+            expf(rank_key_value(key[e]) - mx) / se;
+      } else if (r < k + R) {
+        fallback_ids[static_cast<size_t>(t) * R + (r - k)] = e;
+      }
+    }
+}
+
+}  // namespace rt
+}  // namespace moe

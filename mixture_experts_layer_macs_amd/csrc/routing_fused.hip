@@ -1,0 +1,365 @@
+// moe_routing_fused: router top-k, SERE re-routing, MACS capacity with
+// re-route-else-drop, and dispatch in ONE launch, for decode-sized batches
+// ("MACS", §3.1 Eq. 1 and Eq. 3, §3.2 Eq. 5-6, §3.3 Eq. 7, §1 and Fig. 1;
+// multi-image QA inference write-up, §4.1-§4.3: the re-route operator is a
+// single fused kernel with no host round trip and feeds the fused MoE
+// directly).
+//
+// The grid routes the tokens (one group of GT threads per token, rank
+// counting in LDS).  The workgroup that finishes last (atomic ticket that
+// wraps back to zero) sees every token's ranks and runs the batch-wide
+// steps on its own: the SERE union and re-route, the capacity rounds (all of
+// them, or the capacity-off pass), and the counting sort into expert-major
+// rows.  Each step is the same device code as the stand-alone entry points,
+// so the results are identical to calling them in order.
+//
+// The batch-wide steps are a chain of short dependent phases, so each
+// global-memory round trip would cost about a microsecond.  The last
+// workgroup therefore loads every per-slot and per-token input into LDS
+// with one batch of independent loads, runs every phase on LDS copies (the
+// workspace arrays and control words of the capacity and dispatch steps
+// live in LDS too), and writes the results out once, coalesced.  Shapes
+// whose tail does not fit in LDS are not supported here (the separate entry
+// points cover them).
+#include <cmath>
+
+#include "capacity_impl.h"
+#include "dispatch_impl.h"
+#include "route_impl.h"
+#include "sere_impl.h"
+
+namespace moe {
+namespace fused {
+
+// Byte offsets of the tail's arrays in dynamic LDS (16-byte aligned).
+struct TailLayout {
+  unsigned topk, fb, sere, slot, flags, vis, ew, mod;  // inputs and outputs
+  unsigned wq, cur, st, incl_slot, incl_tok, offer_s, offer_c;  // capacity
+  unsigned part, base, wsum, capv, drem, active, act_bits, adm, total;
+  unsigned drank, dpart, dbase, doff;  // dispatch
+  unsigned scratch;                    // phase scratch: [N u64][W*N int32]
+  unsigned bytes;
+  int lds_scan;
+};
+
+__host__ __device__ inline TailLayout tail_layout(int T, int N, int k, int R,
+                                                  int waves) {
+  TailLayout L{};
+  size_t o = 0;
+  auto take = [&](size_t n) {
+    const size_t at = o;
+    o = (o + n + 15) & ~size_t(15);
+    return static_cast<unsigned>(at);
+  };
+  const size_t Tk = static_cast<size_t>(T) * k;
+  L.topk = take(4 * Tk);
+  L.fb = take(4 * static_cast<size_t>(T) * R);
+  L.sere = take(4 * Tk);
+  L.slot = take(4 * Tk);
+  L.flags = take(Tk);
+  L.vis = take(T);
+  L.ew = take(4 * static_cast<size_t>(T));
+  L.mod = take(N);
+  L.wq = take(4 * static_cast<size_t>(T));
+  L.cur = take(4 * Tk);
+  L.st = take(Tk);
+  L.incl_slot = take(4 * Tk);
+  L.incl_tok = take(4 * static_cast<size_t>(T));
+  L.offer_s = take(4 * static_cast<size_t>(T));
+  L.offer_c = take(4 * static_cast<size_t>(T));
+  L.part = take(4 * static_cast<size_t>(N));
+  L.base = take(8 * static_cast<size_t>(N));
+  L.wsum = take(8 * 4);
+  L.capv = take(8 * static_cast<size_t>(N));
+  L.drem = take(8 * static_cast<size_t>(N));
+  L.active = take(N);
+  L.act_bits = take(4 * 32);
+  L.adm = take(8 * static_cast<size_t>(N));
+  L.total = take(8 * static_cast<size_t>(N));
+  L.drank = take(4 * Tk);
+  L.dpart = take(4 * static_cast<size_t>(N));
+  L.dbase = take(4 * static_cast<size_t>(N));
+  L.doff = take(4 * (static_cast<size_t>(N) + 1));
+  L.lds_scan = waves * N;
+  L.scratch = take(8 * static_cast<size_t>(N) + 4 * static_cast<size_t>(L.lds_scan));
+  L.bytes = static_cast<unsigned>(o);
+  return L;
+}
+
+// Dynamic LDS the tail may use (the static LDS of the kernel comes on top).
+constexpr size_t TAIL_LDS_MAX = 150 * 1024;
+
+struct Args {
+  const float* logits;
+  const float* sim;
+  const uint8_t* prot;
+  int32_t* topk_ids;
+  float* topk_gates;
+  int32_t* fallback_ids;
+  int32_t* slot_sere;
+  int32_t* slot_expert;
+  uint8_t* flags;
+  int32_t* expert_offsets;
+  int T, N, k, R, kprime;
+  float rho;
+  bool cap_on;
+  unsigned* ticket;
+  TailLayout tl;
+};
+
+// The batch-wide steps, run by the last workgroup on LDS copies.  cg and dg
+// carry the caller's inputs and outputs; their workspace pointers are
+// replaced by LDS arrays here.
+__device__ void tail(const Args& f, const cap::Args& cg, const disp::Args& dg,
+                     unsigned char* smem, sr::SereLds& sl) {
+  const TailLayout& L = f.tl;
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int T = f.T, N = f.N, k = f.k, R = f.R;
+  const int Tk = T * k, TR = T * R;
+  int32_t* topk = reinterpret_cast<int32_t*>(smem + L.topk);
+  int32_t* fb = reinterpret_cast<int32_t*>(smem + L.fb);
+  int32_t* sere = reinterpret_cast<int32_t*>(smem + L.sere);
+  int32_t* slot = reinterpret_cast<int32_t*>(smem + L.slot);
+  uint8_t* flags = smem + L.flags;
+  uint8_t* vis = smem + L.vis;
+  float* ew = reinterpret_cast<float*>(smem + L.ew);
+  int8_t* mod = reinterpret_cast<int8_t*>(smem + L.mod);
+  uint32_t* act_bits = reinterpret_cast<uint32_t*>(smem + L.act_bits);
+  unsigned long long* adm = reinterpret_cast<unsigned long long*>(smem + L.adm);
+  unsigned long long* total = reinterpret_cast<unsigned long long*>(smem + L.total);
+  int32_t* doff = reinterpret_cast<int32_t*>(smem + L.doff);
+
+  // one batch of independent loads brings every input in; the control
+  // words start at zero
+  const int n_in = max(max(Tk, TR), max(T, N));
+  for (int i = tid; i < n_in; i += nthr) {
+    if (i < Tk) topk[i] = f.topk_ids[i];
+    if (i < TR) fb[i] = f.fallback_ids[i];
+    if (i < T) {
+      vis[i] = cg.is_visual[i];
+      ew[i] = cg.entropy_w[i];
+    }
+    if (i < N) {
+      mod[i] = cg.modality[i];
+      adm[i] = 0ull;
+      total[i] = 0ull;
+    }
+    if (i < 32) act_bits[i] = 0u;
+  }
+  __syncthreads();
+
+  const int32_t* slot_in = topk;
+  if (f.kprime > 0) {
+    sr::sere_block(topk, T, N, k, f.kprime, f.rho, f.sim, f.prot, sere, flags, sl);
+    __syncthreads();
+    slot_in = sere;
+  }
+
+  cap::Args c = cg;
+  c.topk = topk;
+  c.slot_in = slot_in;
+  c.fallback = fb;
+  c.is_visual = vis;
+  c.entropy_w = ew;
+  c.modality = mod;
+  c.slot_out = slot;
+  c.flags = flags;
+  c.wq = reinterpret_cast<int32_t*>(smem + L.wq);
+  c.cur = reinterpret_cast<int32_t*>(smem + L.cur);
+  c.st = smem + L.st;
+  c.incl_slot = reinterpret_cast<int32_t*>(smem + L.incl_slot);
+  c.incl_tok = reinterpret_cast<int32_t*>(smem + L.incl_tok);
+  c.offer_s = reinterpret_cast<int32_t*>(smem + L.offer_s);
+  c.offer_c = reinterpret_cast<int32_t*>(smem + L.offer_c);
+  c.part = reinterpret_cast<int32_t*>(smem + L.part);
+  c.base = reinterpret_cast<int64_t*>(smem + L.base);
+  c.wsum = reinterpret_cast<int64_t*>(smem + L.wsum);
+  c.capv = reinterpret_cast<int64_t*>(smem + L.capv);
+  c.drem = reinterpret_cast<int64_t*>(smem + L.drem);
+  c.active = smem + L.active;
+  c.ticket = nullptr;
+  c.act_bits = act_bits;
+  c.adm = adm;
+  c.total = total;
+  c.lds_scan = L.lds_scan;
+  if (f.cap_on)
+    cap::cap_rounds(c, 0, 0, R + 1, smem + L.scratch);
+  else
+    cap::cap_off(c, 0, smem + L.scratch);
+  __syncthreads();
+
+  disp::Args d = dg;
+  d.slot = slot;
+  d.offsets = doff;
+  d.rank = reinterpret_cast<int32_t*>(smem + L.drank);
+  d.part = reinterpret_cast<int32_t*>(smem + L.dpart);
+  d.base = reinterpret_cast<int32_t*>(smem + L.dbase);
+  d.ticket = nullptr;
+  d.lds_scan = L.lds_scan;
+  disp::dispatch_single(d, smem + L.scratch);
+  __syncthreads();
+
+  const int n_out = max(Tk, N + 1);
+  for (int i = tid; i < n_out; i += nthr) {
+    if (i < Tk) {
+      f.slot_expert[i] = slot[i];
+      f.flags[i] = flags[i];
+      if (f.kprime > 0) f.slot_sere[i] = sere[i];
+    }
+    if (i <= N) f.expert_offsets[i] = doff[i];
+  }
+}
+
+template <int GT>
+__global__ __launch_bounds__(1024) void routing_kernel(Args f, cap::Args ca,
+                                                       disp::Args da) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ sr::SereLds sl;
+  __shared__ int s_last;
+  constexpr int TPB = 1024 / GT;
+  const int grp = threadIdx.x / GT;
+  const int t = blockIdx.x * TPB + grp;
+  rt::route_token<GT>(f.logits, f.N, f.k, f.R, t, t < f.T,
+                      smem + grp * rt::token_lds_bytes(f.N, GT), f.topk_ids,
+                      f.topk_gates, f.fallback_ids);
+
+  // Hand-off to the last workgroup.  On gfx950 an agent-scope fence writes
+  // back (release) or invalidates (acquire) the XCD's L2, so it is issued
+  // once per workgroup, not once per wave: every wave first waits for its
+  // own stores, the barrier joins them, and one thread fences and counts.
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    const unsigned prev = atomicInc(f.ticket, gridDim.x - 1);
+    s_last = prev == gridDim.x - 1;
+    if (s_last) __threadfence();  // see every other workgroup's results
+  }
+  __syncthreads();
+  if (!s_last) return;
+
+  tail(f, ca, da, smem, sl);
+}
+
+// Dynamic LDS of the kernel: the larger of the routing groups and the tail.
+inline size_t kernel_lds(int T, int N, int k, int R, int GT) {
+  const size_t route = static_cast<size_t>(1024 / GT) * rt::token_lds_bytes(N, GT);
+  return std::max(route, static_cast<size_t>(tail_layout(T, N, k, R, 16).bytes));
+}
+
+inline bool supported(int T, int N, int k, int R) {
+  return tail_layout(T, N, k, R, 16).bytes <= TAIL_LDS_MAX;
+}
+
+constexpr size_t WS_BYTES = 256;  // the ticket
+
+}  // namespace fused
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" size_t moe_routing_workspace_size(int T, int N, int k, int R) {
+  if (T < 0 || N < 1 || N > 1024 || k < 1 || k > N || R < 0 || R > N - k ||
+      !fused::supported(T, N, k, R))
+    return 0;
+  return fused::WS_BYTES;
+}
+
+extern "C" int moe_routing_fused(
+    const float* logits, const uint8_t* is_visual, const float* entropy_w,
+    const int8_t* modality, const float* sim, const uint8_t* prot, int T,
+    int N, int k, int R, int kprime, float rho, int group, double gamma,
+    double lam, int32_t* topk_ids, float* topk_gates, int32_t* fallback_ids,
+    int32_t* slot_sere, int32_t* slot_expert, uint8_t* flags, int64_t* load_q,
+    int64_t* cap_q, int64_t* stats, double* r_v, int32_t* expert_offsets,
+    int32_t* row_token, int32_t* row_slot, int32_t* slot_row,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  if (T < 0 || T > (1 << 20) || N < 1 || N > 1024 || k < 1 || k > N ||
+      R < 0 || R > N - k || group < 1 || group > N || kprime < 0 ||
+      kprime > k)
+    return MOE_EINVAL;
+  if (std::isnan(gamma) || gamma <= 0.0 || (!std::isinf(gamma) && gamma > 1e30) ||
+      !std::isfinite(lam))
+    return MOE_EINVAL;
+  if (!fused::supported(T, N, k, R)) return MOE_EUNSUP;
+  if (!expert_offsets) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!logits || !is_visual || !entropy_w || !modality || !topk_ids ||
+      !topk_gates || (R > 0 && !fallback_ids) || !slot_expert || !flags ||
+      !load_q || !cap_q || !stats || !r_v || !row_token || !row_slot ||
+      !slot_row || !workspace)
+    return MOE_EINVAL;
+  if (kprime > 0 && (!sim || !prot || !slot_sere)) return MOE_EINVAL;
+  if (workspace_bytes < fused::WS_BYTES) return MOE_EINVAL;
+  char* ws = static_cast<char*>(workspace);
+
+  fused::Args f{};
+  f.logits = logits;
+  f.sim = sim;
+  f.prot = prot;
+  f.topk_ids = topk_ids;
+  f.topk_gates = topk_gates;
+  f.fallback_ids = fallback_ids;
+  f.slot_sere = slot_sere;
+  f.slot_expert = slot_expert;
+  f.flags = flags;
+  f.expert_offsets = expert_offsets;
+  f.T = T;
+  f.N = N;
+  f.k = k;
+  f.R = R;
+  f.kprime = kprime;
+  f.rho = rho;
+  f.cap_on = !std::isinf(gamma);
+  f.ticket = reinterpret_cast<unsigned*>(ws);
+  f.tl = fused::tail_layout(T, N, k, R, 16);
+  // Caller-side arrays only: the tail points every workspace array of these
+  // argument blocks at LDS.
+  cap::Args ca{};
+  ca.is_visual = is_visual;
+  ca.entropy_w = entropy_w;
+  ca.modality = modality;
+  ca.T = T;
+  ca.N = N;
+  ca.k = k;
+  ca.R = R;
+  ca.group = group;
+  int nb = 1;
+  while ((1 << nb) < N) ++nb;
+  ca.nbits = nb;
+  ca.gamma = gamma;
+  ca.lam = lam;
+  ca.load_q = load_q;
+  ca.cap_q = cap_q;
+  ca.stats = stats;
+  ca.r_v = r_v;
+  ca.TB = T;
+  ca.G = 1;
+  disp::Args da{};
+  da.T = T;
+  da.N = N;
+  da.k = k;
+  da.nbits = nb;
+  da.row_token = row_token;
+  da.row_slot = row_slot;
+  da.slot_row = slot_row;
+  da.TB = T;
+  da.G = 1;
+
+  const int GT = N <= 64 ? 64 : 256;
+  const int TPB = 1024 / GT;
+  const size_t lds = fused::kernel_lds(T, N, k, R, GT);
+  const void* fn = GT == 64 ? reinterpret_cast<const void*>(fused::routing_kernel<64>)
+                            : reinterpret_cast<const void*>(fused::routing_kernel<256>);
+  if (lds > 65536 &&
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          static_cast<int>(lds)) != hipSuccess)
+    return MOE_EHIP;
+  hipStream_t s = as_stream(stream);
+  const dim3 grid((T + TPB - 1) / TPB), block(1024);
+  if (GT == 64)
+    hipLaunchKernelGGL(fused::routing_kernel<64>, grid, block, lds, s, f, ca, da);
+  else
+    hipLaunchKernelGGL(fused::routing_kernel<256>, grid, block, lds, s, f, ca, da);
+  return launch_status();
+}

@@ -45,8 +45,11 @@ def say(msg: str):
     print(f"[gpu-test] {msg}", flush=True)
 
 
-def run_gpu_layer(inp: dict, tokens_out=True):
-    """Run the six calls on the GPU; return host numpy copies of everything."""
+def run_gpu_layer(inp: dict, tokens_out=True, fused=None):
+    """Run the layer on the GPU through the C ABI; return host numpy copies of
+    everything.  fused: True = one moe_routing_fused launch, False = the four
+    separate routing calls, None = the layer's default (fused when the batch
+    is decode-sized)."""
     import torch
     from mixture_experts_layer_macs_amd import binding as B
     from mixture_experts_layer_macs_amd.staging import to_device, torch_elem_dtype
@@ -58,19 +61,11 @@ def run_gpu_layer(inp: dict, tokens_out=True):
         lay.forward(d["logits"], d["x"], d["w13"], d["w2"], d["is_visual"],
                     d["entropy_w"], d["modality"], d["sim"], d["prot"],
                     inp["kprime"], inp["rho"], inp["gamma"], inp["lam"],
-                    inp["group"])
+                    inp["group"], fused=fused)
     else:
-        B.moe_route(d["logits"], k, R, lay.topk_ids, lay.topk_gates, lay.fallback_ids)
-        slot_in = lay.topk_ids
-        if inp["kprime"]:
-            B.moe_sere_reroute(lay.topk_ids, N, inp["kprime"], inp["rho"],
-                               d["sim"], d["prot"], lay.slot_sere, lay.flags_sere)
-            slot_in = lay.slot_sere
-        B.moe_capacity_assign(lay.topk_ids, slot_in, lay.fallback_ids,
-                              d["is_visual"], d["entropy_w"], d["modality"], N,
-                              R, inp["group"], inp["gamma"], inp["lam"],
-                              lay.ws_cap, lay.cap)
-        B.moe_dispatch(lay.cap["slot_out"], N, lay.ws_disp, lay.disp)
+        lay.routing(d["logits"], d["is_visual"], d["entropy_w"], d["modality"],
+                    d["sim"], d["prot"], inp["kprime"], inp["rho"],
+                    inp["gamma"], inp["lam"], inp["group"], fused=fused)
     torch.cuda.synchronize()
     c = lambda t: t.detach().cpu().numpy()
     out = dict(topk_ids=c(lay.topk_ids), gates=c(lay.topk_gates),

@@ -110,13 +110,57 @@ ROUTING_CASES = [
 ]
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
 @pytest.mark.parametrize("name,wl,seed", ROUTING_CASES, ids=[c[0] for c in ROUTING_CASES])
-def test_routing_parity(name, wl, seed):
-    say(f"routing parity {name} T={wl.T} N={wl.N} k={wl.k} R={wl.R}")
+def test_routing_parity(name, wl, seed, fused):
+    from mixture_experts_layer_macs_amd import binding as B
+    if fused and B.moe_routing_workspace_size(wl.T, wl.N, wl.k, wl.R) == 0:
+        pytest.skip("shape not covered by the fused routing launch")
+    say(f"routing parity {name} T={wl.T} N={wl.N} k={wl.k} R={wl.R} fused={fused}")
     inp = synth.make_inputs(wl, seed, weights=False)
     rt = O.layer_routing(inp)
-    g = run_gpu_layer(inp, tokens_out=False)
+    g = run_gpu_layer(inp, tokens_out=False, fused=fused)
     assert_routing_equal(g, rt, inp)
+
+
+FUSED_CASES = [
+    ("qwen3_decode_b128", configs.QWEN3_DECODE, 0),
+    ("sweep_b1_k1", configs.SWEEP_LAYER.with_(T=1, kprime=1), 1),
+    ("sweep_b8_k2", configs.SWEEP_LAYER.with_(T=8, kprime=2), 2),
+    ("sweep_b256_k2", configs.SWEEP_LAYER.with_(T=256, kprime=2), 3),
+    ("sweep_b256_off", configs.SWEEP_LAYER.with_(T=256, kprime=0), 4),
+    ("mixtral_decode", configs.MIXTRAL_DECODE, 5),
+    ("tiny_tight", configs.tiny_variants()["tiny_f32_tight"], 6),
+    ("n100_odd", configs.TINY_F32.with_(T=333, N=100, k=3, R=5, group=25,
+                                        gamma=0.7, kprime=1, n_protected=7,
+                                        logits="zipf"), 7),
+    ("n1024_wide", configs.TINY_F32.with_(T=40, N=1024, k=16, R=16,
+                                          group=1024, gamma=1.0, kprime=4,
+                                          n_protected=100), 8),
+    ("slots_4096", configs.SWEEP_LAYER.with_(T=512, kprime=2, gamma=0.9), 9),
+    ("n99_scalar_rows", configs.TINY_F32.with_(T=50, N=99, k=5, R=3, group=99,
+                                               gamma=1.0, kprime=2,
+                                               n_protected=5, logits="zipf"), 10),
+    ("n50_one_wave", configs.TINY_F32.with_(T=77, N=50, k=4, R=6, group=10,
+                                            gamma=0.8, kprime=2,
+                                            n_protected=4), 11),
+]
+
+
+@pytest.mark.parametrize("name,wl,seed", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_fused_routing_equals_separate_calls(name, wl, seed):
+    """The single fused launch reproduces the four separate calls bit for
+    bit (gates included: both run the same device code), and both match the
+    oracle."""
+    from mixture_experts_layer_macs_amd import binding as B
+    assert B.moe_routing_workspace_size(wl.T, wl.N, wl.k, wl.R) > 0, name
+    say(f"fused vs separate {name} T={wl.T} N={wl.N} k={wl.k} K'={wl.kprime}")
+    inp = synth.make_inputs(wl, seed, weights=False)
+    a = run_gpu_layer(inp, tokens_out=False, fused=False)
+    b = run_gpu_layer(inp, tokens_out=False, fused=True)
+    for key in a:
+        np.testing.assert_array_equal(np.asarray(a[key]), np.asarray(b[key]), key)
+    assert_routing_equal(b, O.layer_routing(inp), inp)
 
 
 def _adversarial_inputs(seed, T=96, N=12, k=4, R=3):
@@ -140,9 +184,10 @@ def _adversarial_inputs(seed, T=96, N=12, k=4, R=3):
 ADV = ["ties", "all_protected", "kprime_eq_k", "rho_low", "no_sere", "cap_off"]
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
 @pytest.mark.parametrize("variant", ADV)
-def test_adversarial_routing(variant):
-    say(f"adversarial routing {variant}")
+def test_adversarial_routing(variant, fused):
+    say(f"adversarial routing {variant} fused={fused}")
     inp = _adversarial_inputs(100 + ADV.index(variant))
     if variant == "all_protected":
         inp["prot"][:] = 1
@@ -155,8 +200,39 @@ def test_adversarial_routing(variant):
     elif variant == "cap_off":
         inp["gamma"] = math.inf
     rt = O.layer_routing(inp)
-    g = run_gpu_layer(inp, tokens_out=False)
+    g = run_gpu_layer(inp, tokens_out=False, fused=fused)
     assert_routing_equal(g, rt, inp)
+
+
+def test_fused_workspace_reuse():
+    """One fused-routing workspace serves batches of different sizes and
+    routing settings back to back (its control words reset themselves)."""
+    import torch
+    from mixture_experts_layer_macs_amd import binding as B
+    from mixture_experts_layer_macs_amd.staging import to_device
+    say("fused routing workspace reuse")
+    cases = [configs.SWEEP_LAYER.with_(T=200, kprime=2, gamma=0.8),
+             configs.SWEEP_LAYER.with_(T=17, kprime=1),
+             configs.QWEN3_DECODE]
+    N, k = 128, 8
+    ws = B.new_workspace(B.moe_routing_workspace_size(200, N, k, 8), "cuda")
+    for rep in range(2):
+        for i, wl in enumerate(cases):
+            inp = synth.make_inputs(wl, 10 + i, weights=False)
+            d = to_device(inp, "cuda", weights=False)
+            lay = B.Layer(wl.T, 256, N, k, 128, wl.R, torch.bfloat16)
+            B.moe_routing_fused(d["logits"], d["is_visual"], d["entropy_w"],
+                                d["modality"], d["sim"], d["prot"], k, wl.R,
+                                wl.kprime, wl.rho, wl.group, wl.gamma, wl.lam,
+                                ws, lay.topk_ids, lay.topk_gates,
+                                lay.fallback_ids, lay.slot_sere, lay.cap,
+                                lay.disp)
+            torch.cuda.synchronize()
+            rt = O.layer_routing(inp)
+            np.testing.assert_array_equal(lay.cap["slot_out"].cpu().numpy(),
+                                          rt["slot_expert"], f"{rep}/{i}")
+            np.testing.assert_array_equal(lay.disp["slot_row"].cpu().numpy(),
+                                          rt["slot_row"], f"{rep}/{i}")
 
 
 def test_deterministic_and_workspace_reuse():
@@ -200,21 +276,22 @@ def test_empty_batch_is_noop():
     torch.cuda.synchronize()
 
 
-def test_graph_replay_matches_eager():
-    """The whole six-call sequence captured in a HIP graph: every replay,
-    with eager work and synchronisations in between, reproduces the eager
-    result bit for bit."""
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+def test_graph_replay_matches_eager(fused):
+    """The whole layer captured in a HIP graph: every replay, with eager work
+    and synchronisations in between, reproduces the eager result bit for
+    bit."""
     import torch
     from mixture_experts_layer_macs_amd import binding as B
     from mixture_experts_layer_macs_amd.staging import to_device, torch_elem_dtype
     wl = configs.SWEEP_LAYER.with_(T=96, H=512, I=256, kprime=2, gamma=0.8)
-    say("graph replay vs eager")
+    say(f"graph replay vs eager fused={fused}")
     inp = synth.make_inputs(wl, 3)
     d = to_device(inp, "cuda")
     lay = B.Layer(wl.T, wl.H, wl.N, wl.k, wl.I, wl.R, torch_elem_dtype(wl.dtype))
     args = (d["logits"], d["x"], d["w13"], d["w2"], d["is_visual"],
             d["entropy_w"], d["modality"], d["sim"], d["prot"], wl.kprime,
-            wl.rho, wl.gamma, wl.lam, wl.group)
+            wl.rho, wl.gamma, wl.lam, wl.group, fused)
     lay.forward(*args)
     torch.cuda.synchronize()
     ref_y = lay.y.clone()
