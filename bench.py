@@ -34,6 +34,39 @@ FP32_VALU_PEAK_TFLOPS = 157.3
 METRIC = ("MoE-layer tokens/s (prefill) + decode-step µs at B=128; "
           "% of HBM/MFMA peak")
 
+# HBM bytes per launch of the dominant kernel, from two rocprofv3 --pmc runs
+# of this script on one MI355X (FETCH_SIZE, then WRITE_SIZE: KiB per
+# dispatch, mean over the dispatches of the run), each scaled by what the
+# same counter reads for a plain 256 MiB device-to-device copy
+# (`--copy-probe-mib 256`: FETCH_SIZE reads 128 MiB -> x2.0, WRITE_SIZE
+# reads 256 MiB -> x1.0).  A reading holds only for the kernel sources it was
+# taken on (sha256 over GEMM_SOURCES); otherwise traffic is reported as null.
+GEMM_SOURCES = ("mixture_experts_layer_macs_amd/csrc/ffn.hip",
+                "mixture_experts_layer_macs_amd/csrc/common.h")
+HBM_COUNTERS = {
+    "qwen3_decode_b128": dict(
+        kernel="gate_up_swiglu", fetch_kib=131704.0, write_kib=1536.0,
+        fetch_scale=2.0, write_scale=1.0,
+        sources_sha256="ce1c48eff0fc13bf10b30ddd238d1aaa1ea4160642fe286bb479f419811bd1b2"),
+}
+
+
+def counted_traffic(workload):
+    """Scaled HBM bytes per launch of the dominant kernel, or None when no
+    reading exists for this workload or the kernel has changed since."""
+    import hashlib
+    rec = HBM_COUNTERS.get(workload)
+    if rec is None:
+        return None
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != rec["sources_sha256"]:
+        return None
+    return int(rec["fetch_kib"] * 1024 * rec["fetch_scale"] +
+               rec["write_kib"] * 1024 * rec["write_scale"])
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -204,7 +237,7 @@ def main():
         achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
                     unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
-                    traffic=None, kernel="gate_up_swiglu",
+                    traffic=counted_traffic(wl.name), kernel="gate_up_swiglu",
                     kernel_ms=round(gu_ms, 4), bytes_per_launch=int(gu_bytes))
     else:
         gu_flops = 2.0 * M * H * 2 * I
@@ -212,7 +245,8 @@ def main():
         peak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_VALU_PEAK_TFLOPS
         roof = dict(bound="mfma" if wl.dtype == "bf16" else "alu",
                     achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
-                    frac=round(achieved / peak, 4), traffic=None,
+                    frac=round(achieved / peak, 4),
+                    traffic=counted_traffic(wl.name),
                     kernel="gate_up_swiglu", kernel_ms=round(gu_ms, 4),
                     flops_per_launch=gu_flops)
 
