@@ -19,6 +19,8 @@
 // row tiles that share an expert's weight panel run on one XCD and share its
 // L2.  The grid is an upper bound sized on the host (no device read-back);
 // surplus workgroups exit after reading the expert offsets.
+#include <algorithm>
+
 #include "common.h"
 
 namespace moe {
@@ -135,7 +137,13 @@ void gemm_dma_kernel(Args a) {
   static_assert(WM * WN == NT / MOE_WAVE, "4 waves");
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
-  static_assert(MODE == DOWN || FN % 2 == 0, "gate/up pairs");
+  // Gate-up pairing: with an even number of fragment columns per wave, the
+  // first half holds gate rows and the second half the matching up rows;
+  // with a single fragment column (MIX) each 32-row fragment holds 16 gate
+  // rows and then the 16 matching up rows, so gate row i and up row i sit in
+  // accumulator registers r and r + 8 of the same lane.
+  constexpr bool MIX = MODE == GATEUP && FN == 1;
+  static_assert(MODE == DOWN || MIX || FN % 2 == 0, "gate/up pairs");
   constexpr int CPR = BK / 8;                 // 16-byte chunks per row
   constexpr int SWZ = CPR - 1;
   constexpr int SWS = BK == 64 ? 1 : (BK == 32 ? 2 : 0);  // 256-byte bank rows
@@ -179,11 +187,15 @@ void gemm_dma_kernel(Args a) {
     const int row = (wave * QB + q) * RPJ + lrow;
     const int ch = lslot ^ ((row >> SWS) & SWZ);
     size_t wrow;
-    if (MODE == GATEUP)
+    if (MIX) {
+      const int hc = nt * (BN / 2) + (row / 32) * 16 + (row % 16);
+      wrow = (row % 32) < 16 ? static_cast<size_t>(hc) : static_cast<size_t>(a.I + hc);
+    } else if (MODE == GATEUP) {
       wrow = row < BN / 2 ? static_cast<size_t>(nt * (BN / 2) + row)
                           : static_cast<size_t>(a.I + nt * (BN / 2) + (row - BN / 2));
-    else
+    } else {
       wrow = static_cast<size_t>(nt * BN + row);
+    }
     gb[q] = wj + wrow * K + ch * 8;
   }
   // Slice kslice goes to ring stage kslice % S.  Requests past the last
@@ -210,9 +222,9 @@ void gemm_dma_kernel(Args a) {
 
   const int frow = lane & 31, fhalf = lane >> 5;
   const int a_lane = (wm * TM + frow) * BK;
-  const int b_lane = (MODE == GATEUP ? wn * (TN / 2) + frow : wn * TN + frow) * BK;
+  const int b_lane = (MODE == GATEUP && !MIX ? wn * (TN / 2) + frow : wn * TN + frow) * BK;
   auto brow_rel = [](int y) {
-    if (MODE == GATEUP)
+    if (MODE == GATEUP && !MIX)
       return (y < FN / 2) ? y * 32 : BN / 2 + (y - FN / 2) * 32;
     return y * 32;
   };
@@ -316,6 +328,29 @@ void gemm_dma_kernel(Args a) {
   wait_vmcnt<0>();  // no DMA write may land after the workgroup ends
 
   const int fr = lane & 31;
+  if constexpr (MIX) {  // h columns 8*(r/4) + 4*fhalf + r%4 of the wave's 16
+#pragma unroll
+    for (int x = 0; x < FM; ++x) {
+      const int row = wm * TM + x * 32 + fr;
+      const size_t orow = static_cast<size_t>(row0 + m0 + row) * a.NC;
+      const int c0 = nt * (BN / 2) + wn * 16;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v[i] = silu(acc[x][0][4 * q + i]) * acc[x][0][4 * q + i + 8];
+        uint2 pk;
+        pk.x = static_cast<uint32_t>(f32_to_bf16(v[0])) |
+               (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+        pk.y = static_cast<uint32_t>(f32_to_bf16(v[2])) |
+               (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+        if (m0 + row < Mj)
+          *reinterpret_cast<uint2*>(&a.out[orow + c0 + 8 * q + 4 * fhalf]) = pk;
+      }
+    }
+    return;
+  }
   constexpr int OUT_FN = MODE == GATEUP ? FN / 2 : FN;
 #pragma unroll
   for (int x = 0; x < FM; ++x) {
@@ -431,16 +466,11 @@ using namespace moe::ffn;
 #ifndef MOE_STAGES
 #define MOE_STAGES 4
 #endif
-// Decode tiles: 32 token rows x 256 columns (1 x 4 waves, each 32 x 64),
-// K slices of 64 through a 2-stage ring, two workgroups per CU so one
-// streams its next weight slice while the other multiplies.
-#ifndef MOE_DEC_CFG
-#define MOE_DEC_CFG 32, 256, 64, 1, 4, 2, 2
-#endif
-constexpr int DEC_CFG[] = {MOE_DEC_CFG};
-constexpr int DEC_BM = DEC_CFG[0], DEC_BN = DEC_CFG[1], DEC_BK = DEC_CFG[2],
-              DEC_WM = DEC_CFG[3], DEC_WN = DEC_CFG[4], DEC_S = DEC_CFG[5],
-              DEC_WPE = DEC_CFG[6];
+// Decode tiles: 32 token rows x 256 weight rows (1 x 4 waves), K slices of
+// 64 through a 2-stage ring, two workgroups per CU so one streams its next
+// slice while the other multiplies.  When even 256-row tiles would leave
+// CUs idle (few experts, e.g. 8), 128-row tiles double the workgroup count.
+constexpr int DEC_BK = 64, DEC_S = 2;
 constexpr int GU_CFG[] = {MOE_GU_CFG};
 constexpr int DN_CFG[] = {MOE_DN_CFG};
 constexpr int GU_BM = GU_CFG[0], GU_BN = GU_CFG[1], GU_BK = GU_CFG[2],
@@ -449,16 +479,37 @@ constexpr int DN_BM = DN_CFG[0], DN_BN = DN_CFG[1], DN_BK = DN_CFG[2],
               DN_WM = DN_CFG[3], DN_WN = DN_CFG[4];
 // every bf16 shape the entry points accept (H % 256 == 0, I % 128 == 0)
 // splits into whole column tiles and whole K slices
-static_assert(128 % (GU_BN / 2) == 0 && 128 % (DEC_BN / 2) == 0, "h column tiles");
-static_assert(256 % DN_BN == 0 && 256 % DEC_BN == 0, "output column tiles");
+static_assert(128 % (GU_BN / 2) == 0, "h column tiles");
+static_assert(256 % DN_BN == 0, "output column tiles");
 static_assert(256 % GU_BK == 0 && 256 % DEC_BK == 0, "gate-up K slices");
 static_assert(128 % DN_BK == 0 && 128 % DEC_BK == 0, "down K slices");
 
-// Tile shapes: decode-sized batches (at most 32 rows per expert on average)
-// use 32-row tiles so the weight panels stream with little padding work;
-// larger batches use the 256 x 256 prefill tiles.
+// Decode-sized batches (at most 32 rows per expert on average) use 32-row
+// tiles so the weight panels stream with little padding work; larger
+// batches use the 256 x 256 prefill tiles.
 static bool decode_tiles(int T, int N, int k) {
   return static_cast<long>(T) * k <= 32L * N;
+}
+
+static int cu_count() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// Decode weight-tile height: 256 rows unless that gives fewer tiles than
+// two per CU (the number of experts with rows is at most min(N, T*k)).
+static bool narrow_decode_tiles(int T, int N, int k, int cols_per_256) {
+  const long experts = std::min(static_cast<long>(N), static_cast<long>(T) * k);
+  return experts * cols_per_256 < 2L * cu_count();
 }
 
 static int check_ffn_shape(int T, int N, int k, int H, int I, int dtype) {
@@ -510,10 +561,15 @@ extern "C" int moe_ffn_gate_up(const void* x, const int32_t* row_token,
   g.I = I;
   g.w_stride = 2L * I * H;
   if (decode_tiles(T, N, k)) {
-    g.n_tiles = I / (DEC_BN / 2);
-    if (launch_gemm_dma<GATEUP, DEC_BM, DEC_BN, DEC_BK, DEC_WM, DEC_WN, DEC_S, DEC_WPE>(
-            g, rows_cap, s) != MOE_OK)
-      return MOE_EHIP;
+    int st;
+    if (narrow_decode_tiles(T, N, k, I / 128)) {
+      g.n_tiles = I / 64;
+      st = launch_gemm_dma<GATEUP, 32, 128, DEC_BK, 1, 4, DEC_S, 2>(g, rows_cap, s);
+    } else {
+      g.n_tiles = I / 128;
+      st = launch_gemm_dma<GATEUP, 32, 256, DEC_BK, 1, 4, DEC_S, 2>(g, rows_cap, s);
+    }
+    if (st != MOE_OK) return MOE_EHIP;
   } else {
     g.n_tiles = I / (GU_BN / 2);
     if (launch_gemm_dma<GATEUP, GU_BM, GU_BN, GU_BK, GU_WM, GU_WN, MOE_STAGES, 1>(
@@ -552,10 +608,15 @@ extern "C" int moe_ffn_down(const void* h, const int32_t* expert_offsets,
   d.I = I;
   d.w_stride = static_cast<long>(H) * I;
   if (decode_tiles(T, N, k)) {
-    d.n_tiles = H / DEC_BN;
-    if (launch_gemm_dma<DOWN, DEC_BM, DEC_BN, DEC_BK, DEC_WM, DEC_WN, DEC_S, DEC_WPE>(
-            d, rows_cap, s) != MOE_OK)
-      return MOE_EHIP;
+    int st;
+    if (narrow_decode_tiles(T, N, k, H / 256)) {
+      d.n_tiles = H / 128;
+      st = launch_gemm_dma<DOWN, 32, 128, DEC_BK, 1, 4, DEC_S, 2>(d, rows_cap, s);
+    } else {
+      d.n_tiles = H / 256;
+      st = launch_gemm_dma<DOWN, 32, 256, DEC_BK, 1, 4, DEC_S, 2>(d, rows_cap, s);
+    }
+    if (st != MOE_OK) return MOE_EHIP;
   } else {
     d.n_tiles = H / DN_BN;
     if (launch_gemm_dma<DOWN, DN_BM, DN_BN, DN_BK, DN_WM, DN_WN, MOE_STAGES, 1>(
