@@ -115,8 +115,7 @@ __device__ void propose0(const Args& a, int g, int t0, int t1, int32_t* run,
     a.st[i] = (e != a.topk[i]) ? ST_SERE : ST_KEPT;
   }
   if (tid < 32) act_bits[tid] = 0u;
-  w_all = block_sum_i64(w_all, red);
-  w_vis = block_sum_i64(w_vis, red);
+  block_sum2_i64(w_all, w_vis, red);
   if (tid == 0) {
     a.wsum[g * 4 + 0] = w_all;
     a.wsum[g * 4 + 1] = w_vis;
@@ -224,8 +223,7 @@ __device__ void finalize_slots(const Args& a, int g, int t0, int t1,
     a.slot_out[i] = o;
     a.flags[i] = f;
   }
-  n_drop = block_sum_i64(n_drop, red);
-  n_macs = block_sum_i64(n_macs, red);
+  block_sum2_i64(n_drop, n_macs, red);
   if (tid == 0) {
     a.wsum[g * 4 + 2] = n_drop;
     a.wsum[g * 4 + 3] = n_macs;
@@ -243,8 +241,7 @@ __device__ void global_step(const Args& a, int r, int64_t* red, int32_t* lds) {
       w_all += a.wsum[g * 4 + 0];
       w_vis += a.wsum[g * 4 + 1];
     }
-    w_all = block_sum_i64(w_all, red);
-    w_vis = block_sum_i64(w_vis, red);
+    block_sum2_i64(w_all, w_vis, red);
     if (tid == 0) {
       const double rv = w_all > 0 ? static_cast<double>(w_vis) /
                                         static_cast<double>(w_all)
@@ -282,8 +279,7 @@ __device__ void global_step(const Args& a, int r, int64_t* red, int32_t* lds) {
       nd += a.wsum[g * 4 + 2];
       nm += a.wsum[g * 4 + 3];
     }
-    nd = block_sum_i64(nd, red);
-    nm = block_sum_i64(nm, red);
+    block_sum2_i64(nd, nm, red);
     if (tid == 0) {
       a.stats[2] = nd;
       a.stats[3] = nm;
@@ -317,7 +313,7 @@ __device__ void cap_rounds(const Args& a, int g, int r_first, int r_last,
   unsigned long long* amax = reinterpret_cast<unsigned long long*>(smem);
   int32_t* run = reinterpret_cast<int32_t*>(smem + sizeof(unsigned long long) * a.N);
   __shared__ uint32_t act_bits[32];
-  __shared__ int64_t red[16];
+  __shared__ int64_t red[32];
   const int t0 = g * a.TB, t1 = min(a.T, t0 + a.TB);
   for (int r = r_first; r <= r_last; ++r) {
     if (r >= 1) {
@@ -344,7 +340,7 @@ __device__ void cap_rounds(const Args& a, int g, int r_first, int r_last,
 // smem: dynamic LDS [N u64].
 __device__ void cap_off(const Args& a, int g, unsigned char* smem) {
   unsigned long long* tot = reinterpret_cast<unsigned long long*>(smem);
-  __shared__ int64_t red[16];
+  __shared__ int64_t red[32];
   const int tid = threadIdx.x, nthr = blockDim.x, k = a.k, N = a.N;
   const int t0 = g * a.TB, t1 = min(a.T, t0 + a.TB);
   for (int e = tid; e < N; e += nthr) tot[e] = 0ull;
@@ -364,9 +360,7 @@ __device__ void cap_off(const Args& a, int g, unsigned char* smem) {
     a.slot_out[i] = e;
     a.flags[i] = (e != a.topk[i]) ? MOE_FLAG_SERE : 0;
   }
-  w_all = block_sum_i64(w_all, red);
-  w_vis = block_sum_i64(w_vis, red);
-  __syncthreads();
+  block_sum2_i64(w_all, w_vis, red);
   if (tid == 0) {
     a.wsum[g * 4 + 0] = w_all;
     a.wsum[g * 4 + 1] = w_vis;
@@ -385,8 +379,7 @@ __device__ void cap_off(const Args& a, int g, unsigned char* smem) {
       W += a.wsum[b * 4 + 0];
       Wv += a.wsum[b * 4 + 1];
     }
-    W = block_sum_i64(W, red);
-    Wv = block_sum_i64(Wv, red);
+    block_sum2_i64(W, Wv, red);
   }
   if (tid == 0) {
     a.r_v[0] = W > 0 ? static_cast<double>(Wv) / static_cast<double>(W) : 0.5;

@@ -203,8 +203,46 @@ __device__ inline int64_t block_sum_i64(int64_t v, int64_t* red) {
   return s;
 }
 
+// Block-wide sums of two int64 values per thread (one set of barriers).
+__device__ inline void block_sum2_i64(int64_t& a, int64_t& b, int64_t* red) {
+  const int wave = threadIdx.x / MOE_WAVE, W = blockDim.x / MOE_WAVE;
+  a = wave_sum_i64(a);
+  b = wave_sum_i64(b);
+  __syncthreads();
+  if (lane_id() == 0) {
+    red[wave] = a;
+    red[16 + wave] = b;
+  }
+  __syncthreads();
+  int64_t sa = 0, sb = 0;
+  for (int i = 0; i < W; ++i) {
+    sa += red[i];
+    sb += red[16 + i];
+  }
+  __syncthreads();
+  a = sa;
+  b = sb;
+}
+
+// Exclusive prefix over groups of G consecutive lanes (G a power of two,
+// G <= 16, groups aligned to G): returns the sum of v over the lanes of the
+// group below this one's position; *total gets the group's sum.
+template <int G>
+__device__ __forceinline__ int32_t group_excl_scan(int32_t v, int32_t* total) {
+  const int pos = lane_id() & (G - 1);
+  int32_t x = v;
+  if constexpr (G > 1) { const int32_t y = dpp_t<int, DPP_ROW_SHR1>(0, x); x += pos >= 1 ? y : 0; }
+  if constexpr (G > 2) { const int32_t y = dpp_t<int, DPP_ROW_SHR2>(0, x); x += pos >= 2 ? y : 0; }
+  if constexpr (G > 4) { const int32_t y = dpp_t<int, DPP_ROW_SHR4>(0, x); x += pos >= 4 ? y : 0; }
+  if constexpr (G > 8) { const int32_t y = dpp_t<int, DPP_ROW_SHR8>(0, x); x += pos >= 8 ? y : 0; }
+  // the group's last lane holds its total
+  *total = __shfl(x, (lane_id() | (G - 1)), MOE_WAVE);
+  return x - v;
+}
+
 // Ordered per-key inclusive prefix of item weights inside one workgroup.
-// Items idx = 0..n-1 are in sequence order; key(idx) < 0 means "no item".
+// Items idx = 0..n-1 are in sequence order; key(idx) < 0 means "no item";
+// weights lie in [0, 2^16] (token weights in units of 2^-16 token).
 // On return incl[idx] = sum of w over items j <= idx with the same key, and
 // part_row[key] = the block total of that key.  run: LDS [waves * N].
 // UNIT: every item weighs 1, so a lane's in-wave prefix is a popcount.
@@ -227,19 +265,19 @@ __device__ inline void key_prefix(int n, int N, int nbits, int32_t* run, Get get
     if (idx < end) get(idx, key, w);
     const int valid = key >= 0;
     const uint64_t peers = match_any(key, valid, nbits);
-    uint64_t m = peers & lanemask_le();
+    const uint64_t m = peers & lanemask_le();
     int32_t local = 0;
     if constexpr (UNIT) {
       local = __popcll(m);
     } else {
-      const int maxcnt = wave_max(static_cast<int>(__popcll(m)));
-      for (int c = 0; c < maxcnt; ++c) {  // uniform trip count: all lanes shuffle
-        const int j = m ? (__ffsll(static_cast<long long>(m)) - 1) : lane;
-        const int32_t v = __shfl(w, j, MOE_WAVE);
-        if (m) {
-          local += v;
-          m &= m - 1;
-        }
+      // weighted prefix over the peers at or below this lane, bit plane by
+      // bit plane: sum_b 2^b * |{peers j <= lane : bit b of w_j set}|
+      // (weights are 0 .. 2^16, so 17 planes; no shuffles, no loops
+      // whose length depends on the data)
+#pragma unroll
+      for (int b = 0; b < 17; ++b) {
+        const uint64_t plane = __ballot(valid && ((w >> b) & 1));
+        local += static_cast<int32_t>(__popcll(m & plane)) << b;
       }
     }
     if (valid) {
@@ -250,17 +288,19 @@ __device__ inline void key_prefix(int n, int N, int nbits, int32_t* run, Get get
     }
   }
   __syncthreads();
-  for (int e = tid; e < N; e += nthr) {  // exclusive scan over the waves
-    int32_t t[16];  // W <= 16: all reads in flight before the first use
-#pragma unroll
-    for (int v = 0; v < 16; ++v) t[v] = v < W ? run[v * N + e] : 0;
-    int32_t acc = 0;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      if (v < W) run[v * N + e] = acc;
-      acc += t[v];
-    }
-    part_row[e] = acc;
+  // exclusive scan over the waves of every key: W consecutive lanes per key
+  // (W = 4 or 16, a power of two), DPP row shifts inside the lane group
+  for (int i = tid; i < W * N; i += nthr) {
+    const int e = i / W, v = i % W;
+    const int32_t x = run[v * N + e];
+    int32_t tot;
+    const int32_t ex = W == 16 ? group_excl_scan<16>(x, &tot)
+                     : W == 8 ? group_excl_scan<8>(x, &tot)
+                     : W == 4 ? group_excl_scan<4>(x, &tot)
+                     : W == 2 ? group_excl_scan<2>(x, &tot)
+                              : group_excl_scan<1>(x, &tot);
+    run[v * N + e] = ex;
+    if (v == 0) part_row[e] = tot;
   }
   __syncthreads();
   for (int idx = tid; idx < n; idx += nthr) {

@@ -41,29 +41,38 @@ __device__ void count_block(const Args& a, int g, int t0, int t1,
 // (exclusive prefix over the blocks, without the expert offset).
 __device__ void scan_offsets(const Args& a, int32_t* tot, int32_t* stage) {
   const int tid = threadIdx.x, nthr = blockDim.x, N = a.N, G = a.G;
-  column_scan<int32_t>(a.part, a.base, tot, G, N, stage, a.lds_scan);
-  // chunked block scan over the N totals, carried between chunks
+  if (G == 1) {
+    for (int e = tid; e < N; e += nthr) {
+      tot[e] = a.part[e];
+      a.base[e] = 0;
+    }
+  } else {
+    column_scan<int32_t>(a.part, a.base, tot, G, N, stage, a.lds_scan);
+  }
+  // block scan over the N totals in chunks of blockDim, carried between
+  // chunks: DPP scan inside each wave, then wave 0 scans the wave totals
   __shared__ int32_t wsum[16];
-  __shared__ int32_t carry;
-  if (tid == 0) carry = 0;
-  __syncthreads();
-  const int W = nthr / MOE_WAVE, wave = tid / MOE_WAVE;
+  __shared__ int32_t wexcl[17];
+  int32_t carry = 0;
+  const int W = nthr / MOE_WAVE, wave = tid / MOE_WAVE, lane = lane_id();
+  __syncthreads();  // tot complete
   for (int c0 = 0; c0 < N; c0 += nthr) {
     const int e = c0 + tid;
     const int32_t v = e < N ? tot[e] : 0;
     const int32_t inc = wave_incl_scan(v);
-    if (lane_id() == MOE_WAVE - 1) wsum[wave] = inc;
+    if (lane == MOE_WAVE - 1) wsum[wave] = inc;
     __syncthreads();
-    int32_t pre = carry;
-    for (int i = 0; i < wave; ++i) pre += wsum[i];
+    if (wave == 0) {
+      const int32_t x = lane < W ? wsum[lane] : 0;
+      const int32_t xi = wave_incl_scan(x);
+      if (lane < W) wexcl[lane] = xi - x;
+      if (lane == MOE_WAVE - 1) wexcl[16] = xi;
+    }
+    __syncthreads();
+    const int32_t pre = carry + wexcl[wave];
     if (e < N) a.offsets[e] = pre + inc - v;  // exclusive
     if (e == N - 1) a.offsets[N] = pre + inc;
-    __syncthreads();
-    if (tid == nthr - 1) {
-      int32_t s = carry;
-      for (int i = 0; i < W; ++i) s += wsum[i];
-      carry = s;
-    }
+    carry += wexcl[16];
     __syncthreads();
   }
 }

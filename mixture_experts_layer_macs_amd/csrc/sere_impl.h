@@ -68,20 +68,36 @@ __device__ void sere_block(const int32_t* __restrict__ topk, int T, int N,
       const float* srow = sim + static_cast<size_t>(e) * N;
       const uint8_t* prow = prot + static_cast<size_t>(e) * N;
       if (vec) {
+        // batches of QB quads per lane: every load of a batch is issued
+        // before the first is used (one memory round trip per batch)
+        constexpr int QB = 8;
         const int nq = N / 4;
         const uint32_t* pflag4 = reinterpret_cast<const uint32_t*>(L.in_p);
-#pragma unroll 8
-        for (int q = sub; q < nq; q += LPE) {
-          const float4 s4 = *reinterpret_cast<const float4*>(srow + 4 * q);
-          const uint32_t p4 = *reinterpret_cast<const uint32_t*>(prow + 4 * q);
-          const uint32_t f4 = pflag4[q];
-          const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+        for (int q0 = sub; q0 < nq; q0 += LPE * QB) {
+          float4 s4[QB];
+          uint32_t p4[QB];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint64_t key = rank_key(sv[i], 4 * q + i);
-            if (((f4 >> (8 * i)) & 0xffu) && key > best) {
-              best = key;
-              bprot = (p4 >> (8 * i)) & 0xffu;
+          for (int b = 0; b < QB; ++b) {
+            const int q = q0 + b * LPE;
+            if (q < nq) {
+              s4[b] = *reinterpret_cast<const float4*>(srow + 4 * q);
+              p4[b] = *reinterpret_cast<const uint32_t*>(prow + 4 * q);
+            }
+          }
+#pragma unroll
+          for (int b = 0; b < QB; ++b) {
+            const int q = q0 + b * LPE;
+            if (q < nq) {
+              const uint32_t f4 = pflag4[q];
+              const float sv[4] = {s4[b].x, s4[b].y, s4[b].z, s4[b].w};
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const uint64_t key = rank_key(sv[i], 4 * q + i);
+                if (((f4 >> (8 * i)) & 0xffu) && key > best) {
+                  best = key;
+                  bprot = (p4[b] >> (8 * i)) & 0xffu;
+                }
+              }
             }
           }
         }
