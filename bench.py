@@ -45,9 +45,9 @@ GEMM_SOURCES = ("mixture_experts_layer_macs_amd/csrc/ffn.hip",
                 "mixture_experts_layer_macs_amd/csrc/common.h")
 HBM_COUNTERS = {
     "qwen3_decode_b128": dict(
-        kernel="gate_up_swiglu", fetch_kib=131704.0, write_kib=1536.0,
+        kernel="gate_up_swiglu", fetch_kib=131808.3, write_kib=1536.0,
         fetch_scale=2.0, write_scale=1.0,
-        sources_sha256="ce1c48eff0fc13bf10b30ddd238d1aaa1ea4160642fe286bb479f419811bd1b2"),
+        sources_sha256="5b19f78cd58f440dfdb4f976b681256e7ae64a0f221e78cf0e765450eb95e2bb"),
 }
 
 
@@ -84,6 +84,10 @@ def parse():
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="only copy a buffer of this many MiB device to device "
                         "three times and exit (calibrates HBM byte counters)")
+    p.add_argument("--sweep", action="store_true",
+                   help="the 48-layer decode sweep: batch x visual fraction x "
+                        "SERE setting, one JSON line with the whole table")
+    p.add_argument("--layers", type=int, default=48)
     p.add_argument("--separate-routing", action="store_true",
                    help="route with the four separate calls instead of the "
                         "single fused launch")
@@ -122,12 +126,110 @@ def cpu_baseline(inp, budget_s):
                         f"{t_ffn / n:.3f} s/step fp64 numpy"))
 
 
+
+def run_sweep(args):
+    """48 MoE layers of the Qwen3-30B-A3B shape (T <= 256, H 2048, N 128,
+    top-8, I 768, bf16), each with its own seeded router logits (Zipf
+    popularity permutation), similarity and protection matrices (16
+    protected experts) and random-init expert weights; MACS gamma 1.25,
+    lam 1, R 8.  For every point of batch x visual fraction x SERE setting
+    the whole 48-layer step is captured in one HIP graph and replayed."""
+    import torch
+    from mixture_experts_layer_macs_amd import binding as B
+    from mixture_experts_layer_macs_amd import configs, synth
+    from mixture_experts_layer_macs_amd.staging import elem_tensor, to_device
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    base = configs.SWEEP_LAYER
+    H, N, k, I, R = base.H, base.N, base.k, base.I, base.R
+    L = args.layers
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    print(f"[sweep] random-init weights for {L} layers on the GPU", file=sys.stderr,
+          flush=True)
+    w13 = [torch.empty((N, 2 * I, H), dtype=torch.bfloat16, device=dev).normal_(
+        0.0, 0.02, generator=gen) for _ in range(L)]
+    w2 = [torch.empty((N, H, I), dtype=torch.bfloat16, device=dev).normal_(
+        0.0, 0.02, generator=gen) for _ in range(L)]
+    rows = []
+    for T in (1, 8, 32, 64, 128, 256):
+        x = elem_tensor(synth.activations(base.with_(T=T), args.seed), "bf16", dev)
+        lay = B.Layer(T, H, N, k, I, R, torch.bfloat16, dev)
+        h = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
+        for frac in (0.1, 0.5, 0.9):
+            for kp in (0, 1, 2):
+                wl = base.with_(T=T, visual=f"frac:{frac}", kprime=kp)
+                inps = [to_device(synth.make_inputs(wl, args.seed, layer=l,
+                                                    weights=False), dev, weights=False)
+                        for l in range(L)]
+
+                def layer(l):
+                    d = inps[l]
+                    lay.routing(d["logits"], d["is_visual"], d["entropy_w"],
+                                d["modality"], d["sim"], d["prot"], kp, wl.rho,
+                                wl.gamma, wl.lam, wl.group)
+                    B.moe_ffn_gate_up(x, lay.disp["row_token"],
+                                      lay.disp["expert_offsets"], w13[l], k, h)
+                    B.moe_ffn_down(h, lay.disp["expert_offsets"], w2[l], T, k,
+                                   lay.out_rows)
+                    B.moe_combine(lay.out_rows, lay.disp["slot_row"],
+                                  lay.topk_gates, lay.y)
+
+                # union sizes and weight bytes, layer by layer (untimed)
+                ub = us = uf = 0
+                for l in range(L):
+                    layer(l)
+                    torch.cuda.synchronize()
+                    ub += int(torch.unique(lay.topk_ids).numel())
+                    us += int(torch.unique(lay.slot_sere if kp else lay.topk_ids).numel())
+                    uf += int((torch.diff(lay.disp["expert_offsets"]) > 0).sum().item())
+                g = torch.cuda.CUDAGraph()
+                cs = torch.cuda.Stream()
+                with torch.cuda.graph(g, stream=cs):
+                    for l in range(L):
+                        layer(l)
+                for _ in range(2):
+                    g.replay()
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                reps = max(3, args.steps // 10)
+                e0.record()
+                for _ in range(reps):
+                    g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / reps
+                wbytes = uf * 3 * H * I * 2
+                rows.append(dict(batch=T, visual_frac=frac,
+                                 sere="off" if kp == 0 else f"K'={kp}",
+                                 union_baseline=round(ub / L, 2),
+                                 union_sere=round(us / L, 2),
+                                 union_final=round(uf / L, 2),
+                                 weight_GB_per_step=round(wbytes / 1e9, 3),
+                                 us_per_step=round(ms * 1e3, 1),
+                                 weight_GBps=round(wbytes / (ms * 1e-3) / 1e9, 1)))
+                print(f"[sweep] {rows[-1]}", file=sys.stderr, flush=True)
+                del g, inps
+    print(json.dumps({"metric": "48-layer decode sweep: union size, weight bytes "
+                                "moved and us per 48-layer step",
+                      "unit": "us", "higher_is_better": False, "n_gpus": 1,
+                      "layers": L, "dtype": "bf16",
+                      "data": "synthetic (seeded; random-init weights)",
+                      "config": {"workload": "sweep_layer x 48", "H": H, "N": N,
+                                 "k": k, "I": I, "gamma": base.gamma,
+                                 "lam": base.lam, "R": R, "rho": base.rho},
+                      "sweep": rows}), flush=True)
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.sweep:
+        run_sweep(args)
+        return
     import torch
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20

@@ -170,20 +170,25 @@ __device__ void propose_round(const Args& a, int r, int g, int t0, int t1,
 
 // Admit or refuse the proposals of round r (decided against base and drem
 // from the global step of round r).
+// pending (may be null): LDS count of overflowed slots not yet placed;
+// round 0 adds its overflows, later rounds subtract their admissions.
 __device__ void apply(const Args& a, int r, int g, int t0, int t1,
-                      unsigned long long* amax) {
+                      unsigned long long* amax, int* pending) {
   const int tid = threadIdx.x, nthr = blockDim.x, k = a.k, N = a.N;
   for (int e = tid; e < N; e += nthr) amax[e] = 0ull;
   __syncthreads();
   const int64_t* base = a.base + static_cast<size_t>(g) * N;
+  int moved = 0;
   if (r == 0) {
     for (int i = t0 * k + tid; i < t1 * k; i += nthr) {
       const int e = a.cur[i];
       const int64_t v = base[e] + a.incl_slot[i];
-      if (v <= a.drem[e])
+      if (v <= a.drem[e]) {
         atomicMax(&amax[e], static_cast<unsigned long long>(v));
-      else
+      } else {
         a.st[i] = (a.st[i] & ST_SERE) | ST_OVER;
+        ++moved;
+      }
     }
   } else {
     for (int t = t0 + tid; t < t1; t += nthr) {
@@ -196,8 +201,13 @@ __device__ void apply(const Args& a, int r, int g, int t0, int t1,
         a.st[i] = (a.st[i] & ST_SERE) | ST_PLACED;
         a.cur[i] = c;
         atomicMax(&amax[c], static_cast<unsigned long long>(v));
+        --moved;
       }
     }
+  }
+  if (pending) {  // one LDS atomic per wave
+    const int w = wave_sum(moved);
+    if (lane_id() == 0 && w != 0) atomicAdd(pending, w);
   }
   __syncthreads();
   for (int e = tid; e < N; e += nthr)
@@ -314,11 +324,24 @@ __device__ void cap_rounds(const Args& a, int g, int r_first, int r_last,
   int32_t* run = reinterpret_cast<int32_t*>(smem + sizeof(unsigned long long) * a.N);
   __shared__ uint32_t act_bits[32];
   __shared__ int64_t red[32];
+  __shared__ int s_pending;
   const int t0 = g * a.TB, t1 = min(a.T, t0 + a.TB);
+  // One workgroup running every round can stop re-routing as soon as no
+  // overflowed slot is left unplaced: the overflow set only shrinks, so the
+  // remaining rounds could admit nothing.
+  const bool track = a.G == 1 && r_first == 0 && r_last == a.R + 1;
+  if (threadIdx.x == 0) s_pending = 0;
   for (int r = r_first; r <= r_last; ++r) {
     if (r >= 1) {
-      apply(a, r - 1, g, t0, t1, amax);
+      apply(a, r - 1, g, t0, t1, amax, track ? &s_pending : nullptr);
       __syncthreads();
+      if (track && r <= a.R && s_pending == 0) {
+        finalize_slots(a, g, t0, t1, red);
+        __syncthreads();
+        global_step(a, a.R + 1, red, run);
+        __syncthreads();
+        return;
+      }
     }
     if (r == 0)
       propose0(a, g, t0, t1, run, act_bits, red);
