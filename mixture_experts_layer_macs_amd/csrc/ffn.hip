@@ -463,14 +463,26 @@ using namespace moe::ffn;
 #ifndef MOE_DN_CFG
 #define MOE_DN_CFG 256, 256, 32, 2, 2
 #endif
+#ifndef MOE_DN_STAGES
+#define MOE_DN_STAGES 4
+#endif
+#ifndef MOE_DN_WPE
+#define MOE_DN_WPE 1
+#endif
 #ifndef MOE_STAGES
 #define MOE_STAGES 4
 #endif
-// Decode tiles: 32 token rows x 256 weight rows (1 x 4 waves), K slices of
-// 64 through a 2-stage ring, two workgroups per CU so one streams its next
-// slice while the other multiplies.  When even 256-row tiles would leave
-// CUs idle (few experts, e.g. 8), 128-row tiles double the workgroup count.
-constexpr int DEC_BK = 64, DEC_S = 2;
+// Decode tiles: 32 token rows x 128 or 256 weight rows (1 x 4 waves), K
+// through a 2-stage ring.  Measured on MI355X (qwen3 and Mixtral decode
+// shapes, weights rotated so HBM is read every step):
+//   gate-up: 128-row tiles always (twice the tiles of 256-row ones, so the
+//            uneven split of a few hundred tiles over 256 CUs costs less),
+//            K slices of 64 with four workgroups per CU, or of 128 with two
+//            when K >= 4096;
+//   down:    256-row tiles with K slices of 64 and two workgroups per CU,
+//            unless that leaves CUs idle (few experts), then 128-row tiles;
+//            K slices of 128 when K >= 4096.
+constexpr int DEC_S = 2;
 constexpr int GU_CFG[] = {MOE_GU_CFG};
 constexpr int DN_CFG[] = {MOE_DN_CFG};
 constexpr int GU_BM = GU_CFG[0], GU_BN = GU_CFG[1], GU_BK = GU_CFG[2],
@@ -481,8 +493,8 @@ constexpr int DN_BM = DN_CFG[0], DN_BN = DN_CFG[1], DN_BK = DN_CFG[2],
 // splits into whole column tiles and whole K slices
 static_assert(128 % (GU_BN / 2) == 0, "h column tiles");
 static_assert(256 % DN_BN == 0, "output column tiles");
-static_assert(256 % GU_BK == 0 && 256 % DEC_BK == 0, "gate-up K slices");
-static_assert(128 % DN_BK == 0 && 128 % DEC_BK == 0, "down K slices");
+static_assert(256 % GU_BK == 0, "gate-up K slices");
+static_assert(128 % DN_BK == 0, "down K slices");
 
 // Decode-sized batches (at most 32 rows per expert on average) use 32-row
 // tiles so the weight panels stream with little padding work; larger
@@ -562,13 +574,11 @@ extern "C" int moe_ffn_gate_up(const void* x, const int32_t* row_token,
   g.w_stride = 2L * I * H;
   if (decode_tiles(T, N, k)) {
     int st;
-    if (narrow_decode_tiles(T, N, k, I / 128)) {
-      g.n_tiles = I / 64;
-      st = launch_gemm_dma<GATEUP, 32, 128, DEC_BK, 1, 4, DEC_S, 2>(g, rows_cap, s);
-    } else {
-      g.n_tiles = I / 128;
-      st = launch_gemm_dma<GATEUP, 32, 256, DEC_BK, 1, 4, DEC_S, 2>(g, rows_cap, s);
-    }
+    g.n_tiles = I / 64;
+    if (H >= 4096)
+      st = launch_gemm_dma<GATEUP, 32, 128, 128, 1, 4, DEC_S, 2>(g, rows_cap, s);
+    else
+      st = launch_gemm_dma<GATEUP, 32, 128, 64, 1, 4, DEC_S, 4>(g, rows_cap, s);
     if (st != MOE_OK) return MOE_EHIP;
   } else {
     g.n_tiles = I / (GU_BN / 2);
@@ -609,17 +619,18 @@ extern "C" int moe_ffn_down(const void* h, const int32_t* expert_offsets,
   d.w_stride = static_cast<long>(H) * I;
   if (decode_tiles(T, N, k)) {
     int st;
-    if (narrow_decode_tiles(T, N, k, H / 256)) {
-      d.n_tiles = H / 128;
-      st = launch_gemm_dma<DOWN, 32, 128, DEC_BK, 1, 4, DEC_S, 2>(d, rows_cap, s);
-    } else {
-      d.n_tiles = H / 256;
-      st = launch_gemm_dma<DOWN, 32, 256, DEC_BK, 1, 4, DEC_S, 2>(d, rows_cap, s);
-    }
+    const bool narrow = narrow_decode_tiles(T, N, k, H / 256);
+    d.n_tiles = narrow ? H / 128 : H / 256;
+    if (I >= 4096)
+      st = narrow ? launch_gemm_dma<DOWN, 32, 128, 128, 1, 4, DEC_S, 2>(d, rows_cap, s)
+                  : launch_gemm_dma<DOWN, 32, 256, 128, 1, 4, DEC_S, 1>(d, rows_cap, s);
+    else
+      st = narrow ? launch_gemm_dma<DOWN, 32, 128, 64, 1, 4, DEC_S, 4>(d, rows_cap, s)
+                  : launch_gemm_dma<DOWN, 32, 256, 64, 1, 4, DEC_S, 2>(d, rows_cap, s);
     if (st != MOE_OK) return MOE_EHIP;
   } else {
     d.n_tiles = H / DN_BN;
-    if (launch_gemm_dma<DOWN, DN_BM, DN_BN, DN_BK, DN_WM, DN_WN, MOE_STAGES, 1>(
+    if (launch_gemm_dma<DOWN, DN_BM, DN_BN, DN_BK, DN_WM, DN_WN, MOE_DN_STAGES, MOE_DN_WPE>(
             d, rows_cap, s) != MOE_OK)
       return MOE_EHIP;
   }
