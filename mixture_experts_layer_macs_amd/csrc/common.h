@@ -43,6 +43,7 @@ enum : int {
   DPP_ROW_SHR2 = 0x112,
   DPP_ROW_SHR4 = 0x114,
   DPP_ROW_SHR8 = 0x118,
+  DPP_ROW_HALF_MIRROR = 0x141,  // lane 7-i inside each half-row of 8
   DPP_ROW_BCAST15 = 0x142,  // lane 15 of each row into the next row
   DPP_ROW_BCAST31 = 0x143,  // lane 31 into rows 2 and 3
 };

@@ -7,13 +7,13 @@
 //      that appear as secondaries become LDS byte flags (plain stores of 1:
 //      no atomics, so no serialisation on popular experts);
 //   2. the re-route target depends only on the source expert, so it is
-//      computed once per secondary expert e outside P: a quad of lanes
-//      reads the similarity row of e and the protection row of e with
-//      16-byte and 4-byte vector loads (all issued before any is used, so
-//      the row costs one memory round trip), keeps the best primary p by
-//      (S[e][p] desc, p asc) together with its protection byte, and the
-//      quad combines its candidates with two DPP quad permutes; a blocked p*
-//      keeps e;
+//      computed once per secondary expert e outside P: 8 lanes read the
+//      similarity row of e and the protection row of e with 16-byte and
+//      4-byte vector loads (all issued before any is used, so the row costs
+//      one memory round trip), keep the best primary p by (S[e][p] desc,
+//      p asc) together with its protection byte, and combine their
+//      candidates with two DPP quad permutes and one half-row mirror; a
+//      blocked p* keeps e;
 //   3. every slot is rewritten through the per-expert target table in LDS.
 // Similarity and protection share one [N][N] row-major layout, so the lane
 // that holds S[e][p] also holds Prot[e][p]: the protection bit is checked
@@ -55,7 +55,7 @@ __device__ void sere_block(const int32_t* __restrict__ topk, int T, int N,
   }
   __syncthreads();
 
-  constexpr int LPE = 4;  // lanes per source expert: one quad
+  constexpr int LPE = 8;  // lanes per source expert: half a DPP row
   const int sub = tid % LPE;
   const bool vec = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(sim) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(prot) & 3) == 0;
@@ -114,7 +114,8 @@ __device__ void sere_block(const int32_t* __restrict__ topk, int T, int N,
         }
       }
     }
-    // combine the quad: partner lane ^ 1, then ^ 2 (all lanes take part)
+    // combine the 8 lanes: partner lane ^ 1, ^ 2, then the mirrored lane
+    // of the other quad (all lanes take part)
     {
       const uint64_t o = dpp64<DPP_QUAD_1032>(0ull, best);
       const uint32_t op = dpp<DPP_QUAD_1032>(0u, bprot);
@@ -126,6 +127,14 @@ __device__ void sere_block(const int32_t* __restrict__ topk, int T, int N,
     {
       const uint64_t o = dpp64<DPP_QUAD_2301>(0ull, best);
       const uint32_t op = dpp<DPP_QUAD_2301>(0u, bprot);
+      if (o > best) {
+        best = o;
+        bprot = op;
+      }
+    }
+    {
+      const uint64_t o = dpp64<DPP_ROW_HALF_MIRROR>(0ull, best);
+      const uint32_t op = dpp<DPP_ROW_HALF_MIRROR>(0u, bprot);
       if (o > best) {
         best = o;
         bprot = op;
