@@ -64,6 +64,13 @@ independently implemented, by the GPU path):
   R11 expert FFN: E_j(x) = W2_j (silu(W1_j x) * (W3_j x)), no biases,
       W13_j = [W1_j; W3_j] (gate rows first), silu(a) = a / (1 + e^-a).
   R12 combine: y_t = sum over kept slots, in slot order, of gate * E(x_t).
+  R14 entropy weights (MACS §3.2 Eq. 4-5; the page calls the normalisation
+      image-level but defines mu and sigma over the batch): z = the token's
+      layer input x_t (D = H); H(x) = Shannon entropy (natural log) of
+      softmax(z); mu and sigma = mean and population standard deviation of
+      H over the batch's visual tokens; H~ = (H - mu) / (sigma + eps);
+      w = sigmoid(-delta * H~) for visual tokens, 1 for text tokens.  delta
+      and eps are not given by the page: parameters (defaults 1 and 1e-6).
 """
 from __future__ import annotations
 
@@ -89,6 +96,41 @@ def decode(a: np.ndarray, dtype: str) -> np.ndarray:
         bits = np.asarray(a, dtype=np.uint16).astype(np.uint32) << 16
         return bits.view(np.float32).astype(np.float64)
     raise ValueError(dtype)
+
+
+# --------------------------------------------------------------------------
+# entropy-weighted token load  [MACS §3.2 Eq. 4-5; R14]
+# --------------------------------------------------------------------------
+def token_entropy(x: np.ndarray, dtype: str) -> np.ndarray:
+    """H(x_t) = -sum_i p_i ln p_i with p = softmax(x_t), per token, in fp64
+    from the exact stored values."""
+    z = decode(x, dtype)
+    H = np.zeros(z.shape[0])
+    for t in range(z.shape[0]):
+        row = z[t] - z[t].max()
+        e = np.exp(row)
+        p = e / e.sum()
+        nz = p > 0
+        H[t] = -float(np.sum(p[nz] * np.log(p[nz])))
+    return H
+
+
+def entropy_weights(x: np.ndarray, is_visual: np.ndarray, dtype: str,
+                    delta: float = 1.0, eps: float = 1e-6):
+    """Semantic token weights w (Eq. 5) from the entropy z-score over the
+    batch's visual tokens (Eq. 4).  Returns (w float64[T], H float64[T],
+    mu, sigma)."""
+    H = token_entropy(x, dtype)
+    vis = np.asarray(is_visual) != 0
+    w = np.ones(len(H))
+    mu = sigma = 0.0
+    if vis.any():
+        hv = H[vis]
+        mu = float(hv.mean())
+        sigma = float(np.sqrt(np.mean((hv - mu) ** 2)))
+        ht = (hv - mu) / (sigma + eps)
+        w[vis] = 1.0 / (1.0 + np.exp(delta * ht))
+    return w, H, mu, sigma
 
 
 # --------------------------------------------------------------------------

@@ -413,3 +413,63 @@ def test_bf16_decode_exact():
     assert vals[0] == 1.0 and vals[1] == -1.0 and vals[4] == 0.25
     assert math.copysign(1.0, vals[3]) == -1.0
     assert vals[5] == float(np.float32(3.3895313892515355e38))
+
+
+# ---------------------------------------------------------------- entropy
+# MACS §3.2 Eq. 4-5 (reading R14): the oracle's entropy weights against
+# library routines and closed forms.
+def _entropy_inputs(seed, T=40, D=96):
+    rng = np.random.default_rng(seed)
+    scale = rng.uniform(0.2, 4.0, size=(T, 1))
+    x = (rng.standard_normal((T, D)) * scale).astype(np.float32)
+    vis = (rng.uniform(size=T) < 0.6).astype(np.uint8)
+    return x, vis
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_entropy_matches_scipy(seed):
+    from scipy.special import softmax
+    from scipy.stats import entropy
+    x, vis = _entropy_inputs(seed)
+    H = O.token_entropy(x, "f32")
+    ref = entropy(softmax(x.astype(np.float64), axis=1), axis=1)
+    np.testing.assert_allclose(H, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_entropy_closed_forms():
+    D = 64
+    # uniform logits: ln D; one dominant logit: ~0; shift invariance
+    x = np.zeros((3, D), dtype=np.float32)
+    x[1, 5] = 200.0
+    x[2] = np.arange(D, dtype=np.float32) * 0.125   # exact, so is x + 8
+    H = O.token_entropy(x, "f32")
+    assert abs(H[0] - math.log(D)) < 1e-12
+    assert H[1] < 1e-60
+    H2 = O.token_entropy(x[2:3] + np.float32(8.0), "f32")
+    assert abs(H2[0] - H[2]) < 1e-12
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_entropy_weight_properties(seed):
+    x, vis = _entropy_inputs(seed)
+    w, H, mu, sigma = O.entropy_weights(x, vis, "f32", delta=2.0, eps=1e-6)
+    v = vis != 0
+    assert (w[~v] == 1.0).all()                     # text tokens: full weight
+    assert ((w[v] > 0) & (w[v] < 1)).all()
+    assert abs(mu - H[v].mean()) < 1e-12
+    assert abs(sigma - H[v].std()) < 1e-12          # population std
+    order = np.argsort(H[v])                         # higher entropy, lower weight
+    assert (np.diff(w[v][order]) <= 1e-15).all()
+    # sigmoid of a z-score: z-scores are centred, and w(+a) + w(-a) = 1
+    ht = (H[v] - mu) / (sigma + 1e-6)
+    np.testing.assert_allclose(w[v], 1.0 / (1.0 + np.exp(2.0 * ht)), rtol=1e-14)
+    assert abs(ht.mean()) < 1e-9
+
+
+def test_entropy_weight_degenerate_batches():
+    x, vis = _entropy_inputs(3, T=5)
+    w, *_ = O.entropy_weights(x, np.zeros(5, np.uint8), "f32")
+    assert (w == 1.0).all()                         # no visual token
+    one = np.zeros(5, np.uint8); one[2] = 1
+    w, *_ = O.entropy_weights(x, one, "f32")
+    assert w[2] == 0.5 and (np.delete(w, 2) == 1.0).all()  # sigma = 0: H~ = 0
