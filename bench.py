@@ -88,6 +88,9 @@ def parse():
                    help="the 48-layer decode sweep: batch x visual fraction x "
                         "SERE setting, one JSON line with the whole table")
     p.add_argument("--layers", type=int, default=48)
+    p.add_argument("--entropy", action="store_true",
+                   help="time the entropy-weight producer on the multimodal "
+                        "prefill batch (T=8192, H=2048, bf16) and exit")
     p.add_argument("--separate-routing", action="store_true",
                    help="route with the four separate calls instead of the "
                         "single fused launch")
@@ -221,6 +224,46 @@ def run_sweep(args):
                                  "lam": base.lam, "R": R, "rho": base.rho},
                       "sweep": rows}), flush=True)
 
+
+def run_entropy(args):
+    """Entropy-weight producer (MACS §3.2 Eq. 4-5) on the 8192-token
+    multimodal prefill batch: one read of every token row, HBM-bound."""
+    import torch
+    from mixture_experts_layer_macs_amd import binding as B
+    from mixture_experts_layer_macs_amd import configs, synth
+    from mixture_experts_layer_macs_amd.staging import elem_tensor
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = configs.MM_PREFILL
+    T, H = wl.T, wl.H
+    xs = [elem_tensor(synth.visual_features(T, H, "bf16", args.seed + c), "bf16", dev)
+          for c in range(2)]
+    vis = torch.from_numpy(synth.visual_mask(wl, args.seed)).to(dev)
+    ws = B.new_workspace(B.moe_entropy_workspace_size(T), dev)
+    w = torch.empty(T, dtype=torch.float32, device=dev)
+    for i in range(args.warmup):
+        B.moe_entropy_weights(xs[i % 2], vis, 1.0, 1e-6, ws, w)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        B.moe_entropy_weights(xs[i % 2], vis, 1.0, 1e-6, ws, w)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = T * H * 2 + T * (1 + 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({"metric": "entropy-weight producer throughput",
+                      "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s",
+                      "us_per_call": round(ms * 1e3, 2), "n_gpus": 1,
+                      "dtype": "bf16", "data": "synthetic (seeded)",
+                      "config": {"workload": "entropy_t8192_h2048", "T": T, "H": H},
+                      "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                   "bytes_per_launch": nbytes}}), flush=True)
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -229,6 +272,9 @@ def main():
         sys.exit(2)
     if args.sweep:
         run_sweep(args)
+        return
+    if args.entropy:
+        run_entropy(args)
         return
     import torch
     if args.copy_probe_mib:

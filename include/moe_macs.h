@@ -180,6 +180,30 @@ int moe_dispatch(const int32_t* slot_expert, int T, int N, int k,
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * moe_entropy_weights -- semantic token weights from the entropy of each
+ * visual token's features (MACS §3.2 Eq. 4-5): H(x_t) = Shannon entropy
+ * (natural log) of softmax(x_t); H~ = (H - mu) / (sigma + eps) with mu and
+ * the population standard deviation sigma of H over the batch's visual
+ * tokens; w = 1 / (1 + exp(delta * H~)) for visual tokens, 1 for text
+ * tokens.  The result is the entropy_w input of moe_capacity_assign.
+ *
+ * x          [T,H] element type `dtype` (the token features, e.g. the
+ *            layer input).
+ * is_visual  u8[T]   nonzero = visual token.
+ * delta, eps finite, eps >= 0 (the page leaves both open).
+ * entropy_w  f32[T]  out: w.
+ * entropy    f32[T]  out: H per token; may be NULL.
+ * Workspace of moe_entropy_workspace_size(T) bytes (scratch only; no
+ * initialisation needed).  Two launches on `stream`.  Sums over tokens are
+ * taken in a fixed order: results are deterministic.
+ */
+size_t moe_entropy_workspace_size(int T);
+int moe_entropy_weights(const void* x, const uint8_t* is_visual, int T, int H,
+                        int dtype, float delta, float eps, float* entropy_w,
+                        float* entropy, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
  * moe_routing_fused -- moe_route, moe_sere_reroute (when kprime > 0),
  * moe_capacity_assign and moe_dispatch in ONE launch, for decode-sized
  * batches.  SERE write-up §4.3: the re-route operator is a

@@ -45,6 +45,8 @@ _SIGS = {
     "moe_dispatch_workspace_size": (_SZ, [_I, _I, _I]),
     "moe_dispatch": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_routing_workspace_size": (_SZ, [_I, _I, _I, _I]),
+    "moe_entropy_workspace_size": (_SZ, [_I]),
+    "moe_entropy_weights": (_I, [_P, _P, _I, _I, _I, _F, _F, _P, _P, _P, _SZ, _P]),
     "moe_routing_fused": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F,
                                _I, _D, _D, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -162,6 +164,26 @@ def moe_routing_workspace_size(T, N, k, R) -> int:
     """Workspace bytes of moe_routing_fused; 0 = shape not covered by the
     fused launch (use the separate calls)."""
     return int(_lib.moe_routing_workspace_size(T, N, k, R))
+
+
+def moe_entropy_workspace_size(T) -> int:
+    return int(_lib.moe_entropy_workspace_size(T))
+
+
+def moe_entropy_weights(x, is_visual, delta, eps, workspace, entropy_w=None,
+                        entropy=None):
+    """Per-token semantic weights (and entropies) from the token features."""
+    T, H = x.shape
+    if entropy_w is None:
+        entropy_w = _empty((T,), torch.float32, x)
+    rc = _lib.moe_entropy_weights(
+        _dev(x, x.dtype, "x"), _dev(is_visual, torch.uint8, "is_visual", (T,)),
+        T, H, _elem(x.dtype), float(delta), float(eps),
+        _dev(entropy_w, torch.float32, "entropy_w", (T,)),
+        _opt(entropy, torch.float32, "entropy", (T,)),
+        _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
+    _check(rc, "moe_entropy_weights")
+    return entropy_w
 
 
 def moe_ffn_workspace_size(T, N, k, H, I, dtype) -> int:

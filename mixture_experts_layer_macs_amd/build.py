@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_macs.so")
 SOURCES = ["route.hip", "sere.hip", "capacity.hip", "dispatch.hip",
-           "routing_fused.hip", "ffn.hip", "combine.hip"]
+           "routing_fused.hip", "ffn.hip", "combine.hip", "entropy.hip"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 

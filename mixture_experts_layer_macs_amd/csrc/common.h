@@ -191,6 +191,19 @@ __device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
   return static_cast<int64_t>(readlane64(u, 63));
 }
 
+// Full-wave sum of doubles in a fixed lane order (deterministic).
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  auto step = [](double x, uint64_t y) { return x + __longlong_as_double(static_cast<long long>(y)); };
+  auto bits = [](double x) { return static_cast<uint64_t>(__double_as_longlong(x)); };
+  v = step(v, dpp64<DPP_QUAD_1032>(0ull, bits(v)));
+  v = step(v, dpp64<DPP_QUAD_2301>(0ull, bits(v)));
+  v = step(v, dpp64<DPP_ROW_SHR4>(0ull, bits(v)));
+  v = step(v, dpp64<DPP_ROW_SHR8>(0ull, bits(v)));
+  v = step(v, dpp64<DPP_ROW_BCAST15, 0xa>(0ull, bits(v)));
+  v = step(v, dpp64<DPP_ROW_BCAST31, 0xc>(0ull, bits(v)));
+  return __longlong_as_double(static_cast<long long>(readlane64(bits(v), 63)));
+}
+
 // Block-wide sum of one int64 per thread; result valid in every thread.
 __device__ inline int64_t block_sum_i64(int64_t v, int64_t* red) {
   const int wave = threadIdx.x / MOE_WAVE, W = blockDim.x / MOE_WAVE;

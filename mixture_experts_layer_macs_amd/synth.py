@@ -39,7 +39,7 @@ from .configs import ZIPF_BETA, Workload
 
 # stream ids
 _S_LOGITS, _S_RANK, _S_STRAG, _S_VIS, _S_VISW, _S_MOD, _S_SIM, _S_PROT, \
-    _S_X, _S_W13, _S_W2 = range(1, 12)
+    _S_X, _S_W13, _S_W2, _S_FEAT = range(1, 13)
 
 
 def _rng(seed: int, stream: int, layer: int = 0) -> np.random.Generator:
@@ -158,6 +158,17 @@ def protection(wl: Workload, seed: int, layer: int = 0) -> np.ndarray:
                                                   replace=False)
         p[rows, :] = 1
     return p
+
+
+def visual_features(T: int, H: int, dtype: str, seed: int,
+                    layer: int = 0) -> np.ndarray:
+    """Token features with spread-out softmax entropies: row t is
+    s_t * N(0,1) with a per-row scale s_t ~ U(0.2, 4.0) (sharper rows have
+    lower entropy).  Used for the entropy-weight producer."""
+    rng = _rng(seed, _S_FEAT, layer)
+    s = rng.uniform(0.2, 4.0, size=(T, 1)).astype(np.float32)
+    x = rng.standard_normal((T, H), dtype=np.float32) * s
+    return x if dtype == "f32" else f32_to_bf16_bits(x)
 
 
 def activations(wl: Workload, seed: int, layer: int = 0) -> np.ndarray:

@@ -92,3 +92,37 @@ def test_host_side_argument_errors(lib):
     lib.moe_combine.argtypes = [P, P, P] + [ctypes.c_int] * 4 + [P, P]
     assert lib.moe_combine(fake, fake, fake, 4, 2, 100, 1, fake, None) == -2
     assert lib.moe_combine(None, fake, fake, 4, 2, 64, 1, fake, None) == -1
+
+
+def test_host_side_errors_fused_and_entropy(lib):
+    """The fused routing launch and the entropy producer reject bad
+    arguments on the host and report shapes they do not cover."""
+    P, I_, F, D, SZ = (ctypes.c_void_p, ctypes.c_int, ctypes.c_float,
+                       ctypes.c_double, ctypes.c_size_t)
+    fake = P(0x1000)
+    lib.moe_routing_workspace_size.restype = SZ
+    lib.moe_routing_workspace_size.argtypes = [I_] * 4
+    assert lib.moe_routing_workspace_size(128, 128, 8, 8) > 0
+    assert lib.moe_routing_workspace_size(4096, 128, 8, 8) == 0   # tail too big
+    lib.moe_routing_fused.argtypes = ([P] * 6 + [I_] * 5 + [F, I_, D, D] +
+                                      [P] * 15 + [SZ, P])
+    big = [fake] * 6 + [4096, 128, 8, 8, 2, 0.5, 128, 1.0, 1.0] + [fake] * 15
+    assert lib.moe_routing_fused(*big, 1 << 20, None) == -2       # MOE_EUNSUP
+    bad_kp = [fake] * 6 + [16, 128, 8, 8, 9, 0.5, 128, 1.0, 1.0] + [fake] * 15
+    assert lib.moe_routing_fused(*bad_kp, 1 << 20, None) == -1    # K' > k
+    short = [fake] * 6 + [16, 128, 8, 8, 2, 0.5, 128, 1.0, 1.0] + [fake] * 15
+    assert lib.moe_routing_fused(*short, 0, None) == -1           # workspace
+    lib.moe_entropy_workspace_size.restype = SZ
+    lib.moe_entropy_workspace_size.argtypes = [I_]
+    assert lib.moe_entropy_workspace_size(8192) > 8192 * 4
+    lib.moe_entropy_weights.argtypes = [P, P, I_, I_, I_, F, F, P, P, P, SZ, P]
+    assert lib.moe_entropy_weights(fake, fake, 4, 64, 7, 1.0, 1e-6, fake, None,
+                                   fake, 1 << 20, None) == -2     # dtype
+    assert lib.moe_entropy_weights(fake, fake, 4, 64, 1, 1.0, -1.0, fake, None,
+                                   fake, 1 << 20, None) == -1     # eps < 0
+    assert lib.moe_entropy_weights(fake, None, 4, 64, 1, 1.0, 1e-6, fake, None,
+                                   fake, 1 << 20, None) == -1
+    assert lib.moe_entropy_weights(fake, fake, 4, 64, 1, 1.0, 1e-6, fake, None,
+                                   fake, 8, None) == -1           # workspace
+    assert lib.moe_entropy_weights(None, None, 0, 64, 1, 1.0, 1e-6, None, None,
+                                   None, 0, None) == 0            # T = 0

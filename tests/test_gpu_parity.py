@@ -313,3 +313,45 @@ def test_graph_replay_matches_eager(fused):
         lay.forward(*args)           # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(lay.y, ref_y)
+
+
+ENTROPY_CASES = [
+    ("bf16_t8192_h2048", 8192, 2048, "bf16", "runs70", 1.0, 0),
+    ("bf16_t333_h768_delta3", 333, 768, "bf16", "half", 3.0, 1),
+    ("f32_t256_h128", 256, 128, "f32", "half", 1.0, 2),
+    ("bf16_t50_h203_odd", 50, 203, "bf16", "half", 0.5, 3),
+    ("bf16_one_visual", 9, 256, "bf16", "one", 1.0, 4),
+    ("bf16_all_text", 64, 512, "bf16", "none", 1.0, 5),
+]
+
+
+@pytest.mark.parametrize("name,T,H,dtype,vis,delta,seed", ENTROPY_CASES,
+                         ids=[c[0] for c in ENTROPY_CASES])
+def test_entropy_weights_parity(name, T, H, dtype, vis, delta, seed):
+    """Entropy producer (MACS §3.2 Eq. 4-5) against the fp64 oracle: token
+    entropies within 1e-5 relative, weights within 2e-5 absolute (fp32
+    accumulation over H terms; the z-score divides by sigma, which these
+    features keep near 1)."""
+    import torch
+    from mixture_experts_layer_macs_amd import binding as B
+    from mixture_experts_layer_macs_amd.staging import elem_tensor
+    say(f"entropy weights {name}")
+    x = synth.visual_features(T, H, dtype, seed)
+    if vis == "one":
+        is_vis = np.zeros(T, np.uint8)
+        is_vis[T // 2] = 1
+    else:
+        wl = configs.MM_PREFILL.with_(T=T, H=H, visual=vis)
+        is_vis = synth.visual_mask(wl, seed)
+    w_ref, H_ref, mu, sigma = O.entropy_weights(x, is_vis, dtype, delta, 1e-6)
+    xd = elem_tensor(x, dtype, "cuda")
+    vd = torch.from_numpy(is_vis).cuda()
+    ws = B.new_workspace(B.moe_entropy_workspace_size(T), "cuda")
+    ent = torch.empty(T, dtype=torch.float32, device="cuda")
+    for _ in range(2):  # the workspace is reused without clearing
+        w = B.moe_entropy_weights(xd, vd, delta, 1e-6, ws, entropy=ent)
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(ent.cpu().numpy(), H_ref, rtol=1e-5, atol=1e-6)
+        np.testing.assert_allclose(w.cpu().numpy(), w_ref, rtol=0, atol=2e-5)
+    say(f"mu={mu:.4f} sigma={sigma:.4f} max|dw|="
+        f"{np.abs(w.cpu().numpy() - w_ref).max():.2e}")
