@@ -1,7 +1,7 @@
 // moe_route: router softmax and top-k ("MACS", §3.1 Eq. 1).
 //
 // Workgroups of 256 threads; each token is owned by a group of GT threads
-// (one wave when N <= 64, else four waves) that ranks its experts by direct
+// (one wave when N <= 128, else four waves) that ranks its experts by direct
 // rank counting over LDS keys (route_impl.h).  Ranking compares the fp32
 // logits themselves, so two logits that round to the same exp() value still
 // rank by value.
@@ -37,7 +37,7 @@ extern "C" int moe_route(const float* logits, int T, int N, int k, int R,
   if (!logits || !topk_ids || !topk_gates || (R > 0 && !fallback_ids))
     return MOE_EINVAL;
   hipStream_t s = as_stream(stream);
-  if (N <= 64) {
+  if (N <= 128) {
     const size_t lds = 4 * rt::token_lds_bytes(N, 64);
     hipLaunchKernelGGL(route_kernel<64>, dim3((T + 3) / 4), dim3(256), lds, s,
                        logits, T, N, k, R, topk_ids, topk_gates, fallback_ids);

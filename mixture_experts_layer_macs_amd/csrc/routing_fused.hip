@@ -346,7 +346,7 @@ extern "C" int moe_routing_fused(
   da.TB = T;
   da.G = 1;
 
-  const int GT = N <= 64 ? 64 : 256;
+  const int GT = N <= 128 ? 64 : 256;
   const int TPB = 1024 / GT;
   const size_t lds = fused::kernel_lds(T, N, k, R, GT);
   const void* fn = GT == 64 ? reinterpret_cast<const void*>(fused::routing_kernel<64>)
