@@ -355,10 +355,17 @@ __device__ void column_scan(const int32_t* in, OutT* excl, OutT* tot, int G,
     __syncthreads();
     for (int c = tid; c < ec; c += nthr) {
       OutT acc = 0;
-      for (int g = 0; g < G; ++g) {
-        const int32_t p = lds[g * ec + c];
-        if (excl) excl[static_cast<size_t>(g) * N + e0 + c] = acc;
-        acc += p;
+      for (int g0 = 0; g0 < G; g0 += 8) {  // 8 reads in flight per step
+        int32_t p[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) p[u] = g0 + u < G ? lds[(g0 + u) * ec + c] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (g0 + u < G) {
+            if (excl) excl[static_cast<size_t>(g0 + u) * N + e0 + c] = acc;
+            acc += p[u];
+          }
+        }
       }
       if (tot) tot[e0 + c] = acc;
     }
