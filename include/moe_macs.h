@@ -262,8 +262,9 @@ int moe_routing_fused(const float* logits, const uint8_t* is_visual,
  * dtype           MOE_F32 (fp32 FMA) or MOE_BF16 (bf16 MFMA with fp32
  *                 accumulation; h and out_rows are rounded to bf16).
  * The workspace holds h ([T*k, I] of dtype).
- * Shapes: MOE_BF16 needs H % 256 == 0 and I % 128 == 0; MOE_F32 needs
- * H % 4 == 0 and I % 4 == 0; otherwise MOE_EUNSUP.
+ * Shapes: MOE_BF16 needs H % 256 == 0, I % 128 == 0, x under 4 GiB
+ * (T*H*2 < 2^32 bytes) and one expert's w13 under 4 GiB (I*H*4 < 2^32
+ * bytes); MOE_F32 needs H % 4 == 0 and I % 4 == 0; otherwise MOE_EUNSUP.
  *
  * moe_ffn_gate_up and moe_ffn_down are the two halves of moe_expert_ffn
  * (same arguments, h passed explicitly, [T*k, I] of dtype), for callers that

@@ -35,6 +35,7 @@ constexpr int NT = 256;
 
 struct Args {
   const uint16_t* a;       // GATEUP: x [T,H]; DOWN: h [T*k, I]
+  int a_rows;              // rows of a (GATEUP: T; DOWN: T*k)
   const int32_t* row_token;
   const int32_t* offsets;  // [N+1]
   const uint16_t* w;       // GATEUP: w13 [N,2I,H]; DOWN: w2 [N,H,I]
@@ -108,14 +109,33 @@ __device__ bool find_tile(const Args& a, int* cum, int& j, int& m0, int& nt,
 // The swizzle is applied on the global side: the lane that fills LDS slot
 // (row, s) fetches chunk s ^ ((row >> SWS) & SWZ) of that row.
 
-// Issued as inline assembly so the compiler's automatic wait insertion
-// does not treat later LDS reads as dependent on it: completion is tracked
-// explicitly (wait_vmcnt + barrier) by the pipeline below.
-__device__ __forceinline__ void lds_dma16(const void* g, void* lds_wave_base) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>(
-          (__attribute__((address_space(3))) unsigned char*)(lds_wave_base))));
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+// The loads are buffer loads: a 128-bit resource (base address, byte size)
+// in scalar registers, a per-lane 32-bit byte offset fixed for the whole K
+// loop, and the K position in a scalar offset, so one request costs a
+// scalar add for M0 (the LDS destination of the wave's 1 KB) and the load
+// itself.  Issued as inline assembly so the compiler's automatic wait
+// insertion does not treat later LDS reads as dependent on it: completion is
+// tracked explicitly (wait_vmcnt + barrier) by the pipeline below.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource: no stride, no swizzle, byte range [0, bytes); word 3
+// is the gfx9 raw-buffer format word (32-bit data format, no type
+// conversion).  Addresses outside the range read as zero.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(b & 0xffffffffu));
+  r.y = __builtin_amdgcn_readfirstlane(static_cast<int32_t>((b >> 32) & 0xffffu));
+  r.z = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(bytes));
+  r.w = 0x00020000;
+  return r;
+}
+
+__device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t voff, uint32_t soff,
+                                          uint32_t m0) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc),
+               "s"(soff), "{m0}"(m0)
+               : "memory");
 }
 
 // s_waitcnt with only the vector-memory counter limited (gfx9 encoding:
@@ -160,56 +180,78 @@ void gemm_dma_kernel(Args a) {
 
   int j, m0, nt, Mj, row0;
   if (!find_tile<BM>(a, cum, j, m0, nt, Mj, row0)) return;
+  // the same in every lane; kept in scalar registers
+  j = __builtin_amdgcn_readfirstlane(j);
+  m0 = __builtin_amdgcn_readfirstlane(m0);
+  nt = __builtin_amdgcn_readfirstlane(nt);
+  Mj = __builtin_amdgcn_readfirstlane(Mj);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
 
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / MOE_WAVE;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / MOE_WAVE);
   const int wm = wave / WN, wn = wave % WN;
   const int K = a.K;
+  const uint32_t row_bytes = static_cast<uint32_t>(K) * 2;
 
-  // per-lane source pointers of this wave's DMA instructions
+  // A: gate-up gathers x rows by token (resource over all of x); down reads
+  // the tile's own rows of h (resource from the tile's first row).  B: the
+  // expert's weight block.  Byte offsets fit 32 bits (checked on the host).
+  const int tile_rows = min(BM, Mj - m0);
+  const i32x4 rsrc_a =
+      MODE == GATEUP
+          ? buffer_rsrc(a.a, static_cast<uint32_t>(a.a_rows) * row_bytes)
+          : buffer_rsrc(a.a + static_cast<size_t>(row0 + m0) * K,
+                        static_cast<uint32_t>(tile_rows) * row_bytes);
+  const i32x4 rsrc_b = buffer_rsrc(a.w + static_cast<size_t>(j) * a.w_stride,
+                                   static_cast<uint32_t>(a.w_stride) * 2);
+
+  // per-lane byte offsets of this wave's loads (fixed over the K loop)
   const int lrow = lane / CPR, lslot = lane % CPR;
-  const uint16_t* ga[QA];
-  const uint16_t* gb[QB];
+  uint32_t va[QA], vb[QB];
 #pragma unroll
   for (int q = 0; q < QA; ++q) {
     const int row = (wave * QA + q) * RPJ + lrow;
     const int ch = lslot ^ ((row >> SWS) & SWZ);
-    const int rr = min(m0 + row, Mj - 1);
-    size_t src_row;
-    if (MODE == GATEUP)
-      src_row = static_cast<size_t>(a.row_token[row0 + rr]);
-    else
-      src_row = static_cast<size_t>(row0 + rr);
-    ga[q] = a.a + src_row * K + ch * 8;
+    const int rr = min(row, tile_rows - 1);
+    const uint32_t src_row = MODE == GATEUP
+                                 ? static_cast<uint32_t>(a.row_token[row0 + m0 + rr])
+                                 : static_cast<uint32_t>(rr);
+    va[q] = src_row * row_bytes + ch * 16;
   }
-  const uint16_t* wj = a.w + static_cast<size_t>(j) * a.w_stride;
 #pragma unroll
   for (int q = 0; q < QB; ++q) {
     const int row = (wave * QB + q) * RPJ + lrow;
     const int ch = lslot ^ ((row >> SWS) & SWZ);
-    size_t wrow;
+    uint32_t wrow;
     if (MIX) {
       const int hc = nt * (BN / 2) + (row / 32) * 16 + (row % 16);
-      wrow = (row % 32) < 16 ? static_cast<size_t>(hc) : static_cast<size_t>(a.I + hc);
+      wrow = (row % 32) < 16 ? hc : a.I + hc;
     } else if (MODE == GATEUP) {
-      wrow = row < BN / 2 ? static_cast<size_t>(nt * (BN / 2) + row)
-                          : static_cast<size_t>(a.I + nt * (BN / 2) + (row - BN / 2));
+      wrow = row < BN / 2 ? nt * (BN / 2) + row : a.I + nt * (BN / 2) + (row - BN / 2);
     } else {
-      wrow = static_cast<size_t>(nt * BN + row);
+      wrow = nt * BN + row;
     }
-    gb[q] = wj + wrow * K + ch * 8;
+    vb[q] = wrow * row_bytes + ch * 16;
   }
+  // LDS byte address of the dynamic LDS block (M0 wants it as 32 bits)
+  const uint32_t lds_base = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char*)(smem))));
   // Slice kslice goes to ring stage kslice % S.  Requests past the last
   // slice re-fetch the last slice into a stage that is never read again, so
-  // every iteration issues the same number of loads.
+  // every iteration issues the same number of loads.  Load d < QA of a
+  // slice is the wave's A row group d, the rest its B row groups.
   const int nk = K / BK;
+  auto dma = [&](int kslice, int d) {
+    const uint32_t st = lds_base + (kslice % S) * STAGE;
+    const uint32_t k0 = static_cast<uint32_t>(min(kslice, nk - 1) * BK * 2);
+    if (d < QA)
+      lds_dma16(rsrc_a, va[d], k0, st + (wave * QA + d) * 1024);
+    else
+      lds_dma16(rsrc_b, vb[d - QA], k0, st + A_BYTES + (wave * QB + d - QA) * 1024);
+  };
   auto issue = [&](int kslice) {
-    unsigned char* st = smem + (kslice % S) * STAGE;
-    const int k0 = min(kslice, nk - 1) * BK;
 #pragma unroll
-    for (int q = 0; q < QA; ++q) lds_dma16(ga[q] + k0, st + (wave * QA + q) * 1024);
-#pragma unroll
-    for (int q = 0; q < QB; ++q)
-      lds_dma16(gb[q] + k0, st + A_BYTES + (wave * QB + q) * 1024);
+    for (int d = 0; d < LPW; ++d) dma(kslice, d);
   };
 
   f32x16 acc[FM][FN];
@@ -254,6 +296,23 @@ void gemm_dma_kernel(Args a) {
 #pragma unroll
     for (int y = 0; y < FN; ++y)
       pb[y] = *(lds_frag*)(B_ + (b_lane + brow_rel(y) * BK) * 2 + sw);
+  };
+  // The same reads, with the DMA requests of slice kslice spread over them
+  // (load d after fragment read d * NFR / LPW), so that no run of requests
+  // holds up the MFMAs that the scheduler places between the reads.
+  auto read_frags_dma = [&](int stage, int kk, bf16x8* pa, bf16x8* pb, int kslice) {
+    lds_byte* A_ = lds0 + stage * STAGE;
+    lds_byte* B_ = A_ + A_BYTES;
+    const int sw = ((kk * 2 + fhalf) ^ ((frow >> SWS) & SWZ)) << 4;  // bytes
+#pragma unroll
+    for (int f = 0; f < NFR; ++f) {
+      if (f < FM)
+        pa[f] = *(lds_frag*)(A_ + (a_lane + f * 32 * BK) * 2 + sw);
+      else
+        pb[f - FM] = *(lds_frag*)(B_ + (b_lane + brow_rel(f - FM) * BK) * 2 + sw);
+#pragma unroll
+      for (int d = f * LPW / NFR; d < (f + 1) * LPW / NFR; ++d) dma(kslice, d);
+    }
   };
   auto mma = [&](const bf16x8* pa, const bf16x8* pb) {
 #pragma unroll
@@ -310,12 +369,11 @@ void gemm_dma_kernel(Args a) {
       }
       wait_vmcnt<(D - 1) * LPW>();
       wg_barrier();
-      issue(kt + 1 + D);
-      // last sub-slice of kt, reading slice kt+1's first fragments meanwhile
-      // (on the last slice those reads fetch stale data that nobody uses)
-      read_frags(nxt, 0, fa[KK & 1], fb[KK & 1]);
+      // last sub-slice of kt, reading slice kt+1's first fragments and
+      // requesting slice kt+1+D meanwhile (on the last slice those reads
+      // fetch stale data that nobody uses)
+      read_frags_dma(nxt, 0, fa[KK & 1], fb[KK & 1], kt + 1 + D);
       mma(fa[(KK - 1) & 1], fb[(KK - 1) & 1]);
-      __builtin_amdgcn_sched_group_barrier(0x0020, LPW, 0);  // VMEM (DMA)
       interleave();
       if (KK & 1) {  // keep set 0 as "current" at the top of the loop
   #pragma unroll
@@ -530,6 +588,11 @@ static int check_ffn_shape(int T, int N, int k, int H, int I, int dtype) {
     return MOE_EINVAL;
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_EUNSUP;
   if (dtype == MOE_BF16 && (H % 256 != 0 || I % 128 != 0)) return MOE_EUNSUP;
+  // bf16 loads address x and one expert's weight block with 32-bit byte
+  // offsets
+  if (dtype == MOE_BF16 && (static_cast<uint64_t>(T) * H * 2 >= (1ull << 32) ||
+                            static_cast<uint64_t>(I) * H * 4 >= (1ull << 32)))
+    return MOE_EUNSUP;
   if (dtype == MOE_F32 && (H % 4 != 0 || I % 4 != 0)) return MOE_EUNSUP;
   return MOE_OK;
 }
@@ -563,6 +626,7 @@ extern "C" int moe_ffn_gate_up(const void* x, const int32_t* row_token,
   }
   Args g{};
   g.a = static_cast<const uint16_t*>(x);
+  g.a_rows = T;
   g.row_token = row_token;
   g.offsets = expert_offsets;
   g.w = static_cast<const uint16_t*>(w13);
@@ -608,6 +672,7 @@ extern "C" int moe_ffn_down(const void* h, const int32_t* expert_offsets,
   }
   Args d{};
   d.a = static_cast<const uint16_t*>(h);
+  d.a_rows = rows_cap;
   d.row_token = nullptr;
   d.offsets = expert_offsets;
   d.w = static_cast<const uint16_t*>(w2);
