@@ -68,6 +68,14 @@ def counted_traffic(workload):
                rec["write_kib"] * 1024 * rec["write_scale"])
 
 
+def hold_gpu(seconds):
+    """Occupy the current stream for about `seconds` (a spin kernel), so the
+    host can queue work behind it."""
+    import torch
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(int(seconds * 2.5e9))
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -336,6 +344,10 @@ def main():
     stop = torch.cuda.Event(enable_timing=True)
     print("[bench] timed steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
+    # Hold the stream with a spin kernel while the host enqueues every timed
+    # step, so that the steps then run back to back and each event pair
+    # brackets GPU work only (no host launch latency inside an interval).
+    hold_gpu(args.steps * 1e-4 + 2e-3)
     t_wall = time.perf_counter()
     start.record()
     for i in range(args.steps):

@@ -118,6 +118,9 @@ __device__ bool find_tile(const Args& a, int* cum, int& j, int& m0, int& nt,
 // tracked explicitly (wait_vmcnt + barrier) by the pipeline below.
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
+// A byte offset past every gate-up resource (x is under 2^31 bytes).
+constexpr uint32_t OOB_OFF = 0x80000000u;
+
 // Raw buffer resource: no stride, no swizzle, byte range [0, bytes); word 3
 // is the gfx9 raw-buffer format word (32-bit data format, no type
 // conversion).  Addresses outside the range read as zero.
@@ -153,7 +156,8 @@ __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "mem
 template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WPE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, WPE)))
 void gemm_dma_kernel(Args a) {
-  static_assert(S >= 2 && S <= 5, "pipeline depth");
+  static_assert(S >= 2 && S <= 8, "pipeline depth");
+  static_assert(BM < 256 || S > 2, "prefill tiles use the interleaved ring");
   static_assert(WM * WN == NT / MOE_WAVE, "4 waves");
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
@@ -205,18 +209,23 @@ void gemm_dma_kernel(Args a) {
   const i32x4 rsrc_b = buffer_rsrc(a.w + static_cast<size_t>(j) * a.w_stride,
                                    static_cast<uint32_t>(a.w_stride) * 2);
 
-  // per-lane byte offsets of this wave's loads (fixed over the K loop)
+  // per-lane byte offsets of this wave's loads (fixed over the K loop).
+  // Rows past the tile's last row get an offset outside their resource's
+  // range, so their loads fill LDS with zeros and fetch nothing: for down
+  // that is any offset past the tile's rows, for gate-up OOB_OFF (x spans
+  // at most 2^31 bytes, checked on the host).
   const int lrow = lane / CPR, lslot = lane % CPR;
   uint32_t va[QA], vb[QB];
 #pragma unroll
   for (int q = 0; q < QA; ++q) {
     const int row = (wave * QA + q) * RPJ + lrow;
     const int ch = lslot ^ ((row >> SWS) & SWZ);
-    const int rr = min(row, tile_rows - 1);
-    const uint32_t src_row = MODE == GATEUP
-                                 ? static_cast<uint32_t>(a.row_token[row0 + m0 + rr])
-                                 : static_cast<uint32_t>(rr);
-    va[q] = src_row * row_bytes + ch * 16;
+    if (MODE == GATEUP)
+      va[q] = row < tile_rows
+                  ? static_cast<uint32_t>(a.row_token[row0 + m0 + row]) * row_bytes + ch * 16
+                  : OOB_OFF;
+    else
+      va[q] = static_cast<uint32_t>(row) * row_bytes + ch * 16;
   }
 #pragma unroll
   for (int q = 0; q < QB; ++q) {
@@ -329,15 +338,19 @@ void gemm_dma_kernel(Args a) {
     }
   };
 
-  if constexpr (S == 2) {
-    // Two stages: slice kt+1 is requested at the top of iteration kt (its
-    // stage was last read in iteration kt-1, before this barrier).
-    issue(0);
+  if constexpr (BM < 256) {
+    // Streaming ring (decode tiles): S - 1 slices are requested ahead.  At
+    // the top of iteration kt a wave waits until its loads of slice kt have
+    // landed (the S - 2 newer slices stay in flight), the barrier publishes
+    // everyone's, and slice kt + S - 1 is requested into the stage of slice
+    // kt - 1, which every wave finished reading before the barrier.
+  #pragma unroll
+    for (int t = 0; t + 1 < S; ++t) issue(t);
     for (int kt = 0; kt < nk; ++kt) {
-      wait_vmcnt<0>();
+      wait_vmcnt<(S - 2) * LPW>();
       wg_barrier();
-      issue(kt + 1);
-      const int cur = kt & 1;
+      issue(kt + S - 1);
+      const int cur = kt % S;
       read_frags(cur, 0, fa[0], fb[0]);
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
@@ -530,17 +543,49 @@ using namespace moe::ffn;
 #ifndef MOE_STAGES
 #define MOE_STAGES 4
 #endif
-// Decode tiles: 32 token rows x 128 or 256 weight rows (1 x 4 waves), K
-// through a 2-stage ring.  Measured on MI355X (qwen3 and Mixtral decode
-// shapes, weights rotated so HBM is read every step):
-//   gate-up: 128-row tiles always (twice the tiles of 256-row ones, so the
-//            uneven split of a few hundred tiles over 256 CUs costs less),
-//            K slices of 64 with four workgroups per CU, or of 128 with two
-//            when K >= 4096;
-//   down:    256-row tiles with K slices of 64 and two workgroups per CU,
-//            unless that leaves CUs idle (few experts), then 128-row tiles;
-//            K slices of 128 when K >= 4096.
-constexpr int DEC_S = 2;
+// Decode tiles: 32 or 128 token rows x 128 or 256 weight rows (1 x 4
+// waves), K through a streaming ring.  Measured on MI355X (qwen3 and
+// Mixtral decode shapes, weights rotated so HBM is read every step;
+// interleaved repeats, medians):
+//   gate-up: 128-row weight tiles; reductions under 4096: 128 token rows
+//            (one tile streams an expert's weight panel once for all its
+//            rows), K slices of 64, 2 stages; reductions of 4096 or more:
+//            32 token rows, K slices of 128, 3 stages;
+//   down:    256-row weight tiles unless that leaves CUs idle (few experts),
+//            then 128-row ones; 32 token rows; K slices of 64 with 2 stages,
+//            or of 128 with 3 stages for reductions of 4096 or more.
+//   K slices of 32 (64-byte row segments) stream worse than 64 or 128.
+// Decode tile configurations {token rows, K slice, ring stages}; the _WIDE
+// ones serve reductions of 4096 or more.
+#ifndef MOE_DEC_GU
+#define MOE_DEC_GU 128, 64, 2
+#endif
+#ifndef MOE_DEC_GU_WIDE
+#define MOE_DEC_GU_WIDE 32, 128, 3
+#endif
+#ifndef MOE_DEC_DN
+#define MOE_DEC_DN 32, 64, 2
+#endif
+#ifndef MOE_DEC_DN_WIDE
+#define MOE_DEC_DN_WIDE 32, 128, 3
+#endif
+struct DecCfg {
+  int bm, bk, s;
+};
+constexpr DecCfg DEC_GU = {MOE_DEC_GU}, DEC_GU_WIDE = {MOE_DEC_GU_WIDE},
+                 DEC_DN = {MOE_DEC_DN}, DEC_DN_WIDE = {MOE_DEC_DN_WIDE};
+// LDS of a decode workgroup with bn weight rows: the ring plus the static
+// tile-count table
+constexpr int dec_lds(DecCfg c, int bn) { return c.s * (c.bm + bn) * c.bk * 2 + 1025 * 4; }
+// workgroups per CU that the LDS allows (160 KB per CU), at most 4
+constexpr int dec_wpe(DecCfg c, int bn) {
+  return (160 * 1024) / dec_lds(c, bn) < 4 ? (160 * 1024) / dec_lds(c, bn) : 4;
+}
+static_assert(dec_wpe(DEC_GU, 128) >= 1 && dec_wpe(DEC_GU_WIDE, 128) >= 1 &&
+                  dec_wpe(DEC_DN, 128) >= 1 && dec_wpe(DEC_DN_WIDE, 128) >= 1,
+              "decode tiles fit the LDS");
+// 256-row down tiles only where their ring fits
+constexpr bool DN_256 = dec_wpe(DEC_DN, 256) >= 1, DN_256_WIDE = dec_wpe(DEC_DN_WIDE, 256) >= 1;
 constexpr int GU_CFG[] = {MOE_GU_CFG};
 constexpr int DN_CFG[] = {MOE_DN_CFG};
 constexpr int GU_BM = GU_CFG[0], GU_BN = GU_CFG[1], GU_BK = GU_CFG[2],
@@ -554,26 +599,13 @@ static_assert(256 % DN_BN == 0, "output column tiles");
 static_assert(256 % GU_BK == 0, "gate-up K slices");
 static_assert(128 % DN_BK == 0, "down K slices");
 
-// Decode-sized batches (at most 32 rows per expert on average) use 32-row
-// tiles so the weight panels stream with little padding work; larger
-// batches use the 256 x 256 prefill tiles.
+// Decode-sized batches (at most 32 rows per expert on average) use the
+// weight-streaming decode tiles; larger batches use the 256 x 256 prefill
+// tiles.
 static bool decode_tiles(int T, int N, int k) {
   return static_cast<long>(T) * k <= 32L * N;
 }
 
-static int cu_count() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
 
 // Decode weight-tile height: 256 rows unless that gives fewer tiles than
 // two per CU (the number of experts with rows is at most min(N, T*k)).
@@ -589,8 +621,8 @@ static int check_ffn_shape(int T, int N, int k, int H, int I, int dtype) {
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_EUNSUP;
   if (dtype == MOE_BF16 && (H % 256 != 0 || I % 128 != 0)) return MOE_EUNSUP;
   // bf16 loads address x and one expert's weight block with 32-bit byte
-  // offsets
-  if (dtype == MOE_BF16 && (static_cast<uint64_t>(T) * H * 2 >= (1ull << 32) ||
+  // offsets; x stays under 2^31 bytes so that OOB_OFF lies outside it
+  if (dtype == MOE_BF16 && (static_cast<uint64_t>(T) * H * 2 > (1ull << 31) ||
                             static_cast<uint64_t>(I) * H * 4 >= (1ull << 32)))
     return MOE_EUNSUP;
   if (dtype == MOE_F32 && (H % 4 != 0 || I % 4 != 0)) return MOE_EUNSUP;
@@ -639,10 +671,13 @@ extern "C" int moe_ffn_gate_up(const void* x, const int32_t* row_token,
   if (decode_tiles(T, N, k)) {
     int st;
     g.n_tiles = I / 64;
-    if (H >= 4096)
-      st = launch_gemm_dma<GATEUP, 32, 128, 128, 1, 4, DEC_S, 2>(g, rows_cap, s);
-    else
-      st = launch_gemm_dma<GATEUP, 32, 128, 64, 1, 4, DEC_S, 4>(g, rows_cap, s);
+    if (H >= 4096) {
+      constexpr DecCfg c = DEC_GU_WIDE;
+      st = launch_gemm_dma<GATEUP, c.bm, 128, c.bk, 1, 4, c.s, dec_wpe(c, 128)>(g, rows_cap, s);
+    } else {
+      constexpr DecCfg c = DEC_GU;
+      st = launch_gemm_dma<GATEUP, c.bm, 128, c.bk, 1, 4, c.s, dec_wpe(c, 128)>(g, rows_cap, s);
+    }
     if (st != MOE_OK) return MOE_EHIP;
   } else {
     g.n_tiles = I / (GU_BN / 2);
@@ -685,13 +720,27 @@ extern "C" int moe_ffn_down(const void* h, const int32_t* expert_offsets,
   if (decode_tiles(T, N, k)) {
     int st;
     const bool narrow = narrow_decode_tiles(T, N, k, H / 256);
-    d.n_tiles = narrow ? H / 128 : H / 256;
-    if (I >= 4096)
-      st = narrow ? launch_gemm_dma<DOWN, 32, 128, 128, 1, 4, DEC_S, 2>(d, rows_cap, s)
-                  : launch_gemm_dma<DOWN, 32, 256, 128, 1, 4, DEC_S, 1>(d, rows_cap, s);
-    else
-      st = narrow ? launch_gemm_dma<DOWN, 32, 128, 64, 1, 4, DEC_S, 4>(d, rows_cap, s)
-                  : launch_gemm_dma<DOWN, 32, 256, 64, 1, 4, DEC_S, 2>(d, rows_cap, s);
+    if (I >= 4096) {
+      constexpr DecCfg c = DEC_DN_WIDE;
+      const bool nar = narrow || !DN_256_WIDE;
+      d.n_tiles = nar ? H / 128 : H / 256;
+      if constexpr (DN_256_WIDE) {
+        st = nar ? launch_gemm_dma<DOWN, c.bm, 128, c.bk, 1, 4, c.s, dec_wpe(c, 128)>(d, rows_cap, s)
+                 : launch_gemm_dma<DOWN, c.bm, 256, c.bk, 1, 4, c.s, dec_wpe(c, 256)>(d, rows_cap, s);
+      } else {
+        st = launch_gemm_dma<DOWN, c.bm, 128, c.bk, 1, 4, c.s, dec_wpe(c, 128)>(d, rows_cap, s);
+      }
+    } else {
+      constexpr DecCfg c = DEC_DN;
+      const bool nar = narrow || !DN_256;
+      d.n_tiles = nar ? H / 128 : H / 256;
+      if constexpr (DN_256) {
+        st = nar ? launch_gemm_dma<DOWN, c.bm, 128, c.bk, 1, 4, c.s, dec_wpe(c, 128)>(d, rows_cap, s)
+                 : launch_gemm_dma<DOWN, c.bm, 256, c.bk, 1, 4, c.s, dec_wpe(c, 256)>(d, rows_cap, s);
+      } else {
+        st = launch_gemm_dma<DOWN, c.bm, 128, c.bk, 1, 4, c.s, dec_wpe(c, 128)>(d, rows_cap, s);
+      }
+    }
     if (st != MOE_OK) return MOE_EHIP;
   } else {
     d.n_tiles = H / DN_BN;

@@ -65,12 +65,25 @@ __device__ void route_token(const float* __restrict__ logits, int N, int k,
       rank[j] = 0;
       mx = fmaxf(mx, v);
     }
-  mx = group_reduce<GT, true>(mx, red);
+  mx = group_reduce<GT, true>(mx, red);  // exact: the order does not matter
+  // The softmax denominator is summed in one fixed order whatever GT is:
+  // lane l of the group's first wave adds the experts j = l (mod 64) in
+  // increasing j, then the wave tree combines the 64 partial sums.  The
+  // gates are therefore the same bits for every group size.  (The keys are
+  // visible to the whole group: the max reduction synchronised it.)
   float se = 0.f;
-  if (live)
-    for (int j = g; j < N; j += GT) se += expf(rank_key_value(key[j]) - mx);
-  se = group_reduce<GT, false>(se, red);
-  __syncthreads();  // every key and zeroed rank visible to the whole group
+  if (g < MOE_WAVE) {
+    if (live)
+      for (int j = g; j < N; j += MOE_WAVE) se += expf(rank_key_value(key[j]) - mx);
+    se = wave_sum(se);
+  }
+  if constexpr (GT > MOE_WAVE) {
+    if (g == 0) red[0] = se;
+    __syncthreads();
+    se = red[0];
+  } else {
+    __syncthreads();  // every key and zeroed rank visible to the whole group
+  }
 
   if (live) {
     if (N <= GT) {

@@ -42,6 +42,9 @@ struct TailLayout {
   int lds_scan;
 };
 
+// Dynamic LDS the tail may use (the static LDS of the kernel comes on top).
+constexpr size_t TAIL_LDS_MAX = 150 * 1024;
+
 __host__ __device__ inline TailLayout tail_layout(int T, int N, int k, int R,
                                                   int waves) {
   TailLayout L{};
@@ -85,9 +88,6 @@ __host__ __device__ inline TailLayout tail_layout(int T, int N, int k, int R,
   L.bytes = static_cast<unsigned>(o);
   return L;
 }
-
-// Dynamic LDS the tail may use (the static LDS of the kernel comes on top).
-constexpr size_t TAIL_LDS_MAX = 150 * 1024;
 
 struct Args {
   const float* logits;
@@ -242,9 +242,9 @@ __global__ __launch_bounds__(1024) void routing_kernel(Args f, cap::Args ca,
 }
 
 // Dynamic LDS of the kernel: the larger of the routing groups and the tail.
-inline size_t kernel_lds(int T, int N, int k, int R, int GT) {
+inline size_t kernel_lds(const TailLayout& L, int N, int GT) {
   const size_t route = static_cast<size_t>(1024 / GT) * rt::token_lds_bytes(N, GT);
-  return std::max(route, static_cast<size_t>(tail_layout(T, N, k, R, 16).bytes));
+  return std::max(route, static_cast<size_t>(L.bytes));
 }
 
 inline bool supported(int T, int N, int k, int R) {
@@ -346,11 +346,19 @@ extern "C" int moe_routing_fused(
   da.TB = T;
   da.G = 1;
 
-  const int GT = N <= 128 ? 64 : 256;
+  // Threads per token: a whole workgroup per token while that still leaves
+  // at most one token per CU (the route phase then spreads over T CUs
+  // instead of T/16), else one wave (N <= 128) or four per token.
+#ifndef MOE_FUSED_GT
+#define MOE_FUSED_GT 0
+#endif
+  const int GT = MOE_FUSED_GT ? MOE_FUSED_GT
+                              : (T <= cu_count() ? 1024 : (N <= 128 ? 64 : 256));
   const int TPB = 1024 / GT;
-  const size_t lds = fused::kernel_lds(T, N, k, R, GT);
-  const void* fn = GT == 64 ? reinterpret_cast<const void*>(fused::routing_kernel<64>)
-                            : reinterpret_cast<const void*>(fused::routing_kernel<256>);
+  const size_t lds = fused::kernel_lds(f.tl, N, GT);
+  const void* fn = GT == 64    ? reinterpret_cast<const void*>(fused::routing_kernel<64>)
+                   : GT == 256 ? reinterpret_cast<const void*>(fused::routing_kernel<256>)
+                               : reinterpret_cast<const void*>(fused::routing_kernel<1024>);
   if (lds > 65536 &&
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                           static_cast<int>(lds)) != hipSuccess)
@@ -359,7 +367,9 @@ extern "C" int moe_routing_fused(
   const dim3 grid((T + TPB - 1) / TPB), block(1024);
   if (GT == 64)
     hipLaunchKernelGGL(fused::routing_kernel<64>, grid, block, lds, s, f, ca, da);
-  else
+  else if (GT == 256)
     hipLaunchKernelGGL(fused::routing_kernel<256>, grid, block, lds, s, f, ca, da);
+  else
+    hipLaunchKernelGGL(fused::routing_kernel<1024>, grid, block, lds, s, f, ca, da);
   return launch_status();
 }
