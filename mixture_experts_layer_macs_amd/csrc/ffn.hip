@@ -20,6 +20,7 @@
 // L2.  The grid is an upper bound sized on the host (no device read-back);
 // surplus workgroups exit after reading the expert offsets.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -31,7 +32,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 enum { GATEUP = 0, DOWN = 1 };
-constexpr int NT = 256;
 
 struct Args {
   const uint16_t* a;       // GATEUP: x [T,H]; DOWN: h [T*k, I]
@@ -45,13 +45,21 @@ struct Args {
   int n_tiles;
 };
 
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);  // round to nearest even (finite inputs)
-  return static_cast<uint16_t>(u >> 16);
+// Two fp32 values to a packed bf16 pair (round to nearest even), one
+// v_cvt_pk_bf16_f32 on gfx950; the first value lands in the low half.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  const bf16x2 b = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, b);
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.f + __expf(-g)); }
+// silu(g) = g / (1 + e^-g), with the hardware exponential and reciprocal
+// (about 1 ulp each; the result is rounded to bf16 afterwards).
+__device__ __forceinline__ float silu(float g) {
+  return g * __builtin_amdgcn_rcpf(1.f + __expf(-g));
+}
 
 // Locate the tile of this workgroup.  cum: LDS [N+1] cumulative tile counts.
 // Returns false for surplus workgroups.
@@ -153,12 +161,25 @@ __device__ __forceinline__ void wait_vmcnt() {
 // only by the DMA loads, whose completion each wave has already waited for.
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// Scheduling groups of one sub-slice: its NMF MFMAs split as evenly as
+// possible over its NFR fragment reads, one read after each group.
+template <int NMF, int NFR, int I = 0>
+__device__ __forceinline__ void interleave_groups() {
+  if constexpr (I < NFR) {
+    __builtin_amdgcn_sched_group_barrier(0x0008, NMF / NFR + (I < NMF % NFR ? 1 : 0), 0);
+    __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);  // DS read
+    interleave_groups<NMF, NFR, I + 1>();
+  }
+}
+
+// WM x WN waves per workgroup (4 or 8); WPE workgroups per CU.
 template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WPE>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, WPE)))
+__global__ __launch_bounds__(WM * WN * MOE_WAVE)
+__attribute__((amdgpu_waves_per_eu(WM * WN / 4, WPE * WM * WN / 4)))
 void gemm_dma_kernel(Args a) {
   static_assert(S >= 2 && S <= 8, "pipeline depth");
-  static_assert(BM < 256 || S > 2, "prefill tiles use the interleaved ring");
-  static_assert(WM * WN == NT / MOE_WAVE, "4 waves");
+  constexpr int W = WM * WN, NTH = W * MOE_WAVE;  // waves, threads
+  static_assert(W == 4 || W == 8, "4 or 8 waves");
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
   // Gate-up pairing: with an even number of fragment columns per wave, the
@@ -173,8 +194,8 @@ void gemm_dma_kernel(Args a) {
   constexpr int SWS = BK == 64 ? 1 : (BK == 32 ? 2 : 0);  // 256-byte bank rows
   constexpr int RPJ = MOE_WAVE / CPR;         // rows per DMA instruction
   constexpr int NA = BM / RPJ, NB = BN / RPJ; // instructions per stage
-  static_assert(NA % 4 == 0 && NB % 4 == 0, "split over 4 waves");
-  constexpr int QA = NA / 4, QB = NB / 4;     // per wave
+  static_assert(NA % W == 0 && NB % W == 0, "split over the waves");
+  constexpr int QA = NA / W, QB = NB / W;     // per wave
   constexpr int LPW = QA + QB;                // DMA loads per wave per stage
   constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
   constexpr int STAGE = A_BYTES + B_BYTES;
@@ -330,40 +351,61 @@ void gemm_dma_kernel(Args a) {
       for (int y = 0; y < FN; ++y)
         acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb[y], pa[x], acc[x][y], 0, 0, 0);
   };
-  auto interleave = [&]() {  // MFMAs of one sub-slice paired with DS reads
-#pragma unroll
-    for (int i = 0; i < NFR; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x0008, NMF / NFR, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);          // DS read
-    }
-  };
+  auto interleave = [&]() { interleave_groups<NMF, NFR>(); };
 
-  if constexpr (BM < 256) {
-    // Streaming ring (decode tiles): S - 1 slices are requested ahead.  At
-    // the top of iteration kt a wave waits until its loads of slice kt have
-    // landed (the S - 2 newer slices stay in flight), the barrier publishes
-    // everyone's, and slice kt + S - 1 is requested into the stage of slice
-    // kt - 1, which every wave finished reading before the barrier.
-  #pragma unroll
-    for (int t = 0; t + 1 < S; ++t) issue(t);
-    for (int kt = 0; kt < nk; ++kt) {
-      wait_vmcnt<(S - 2) * LPW>();
-      wg_barrier();
-      issue(kt + S - 1);
-      const int cur = kt % S;
-      read_frags(cur, 0, fa[0], fb[0]);
+  if constexpr (BM < 256 || S == 2) {
+    // Streaming ring (decode tiles, and prefill tiles with two stages): S - 1
+    // slices are requested ahead.  At the top of iteration kt a wave waits
+    // until its loads of slice kt have landed (the S - 2 newer slices stay
+    // in flight), the barrier publishes everyone's, and slice kt + S - 1 is
+    // requested into the stage of slice kt - 1, which every wave finished
+    // reading before the barrier.
+    //
+    // A short last tile of an expert leaves some of a wave's 32-row
+    // fragments without tile rows; such a wave runs a copy of the loop that
+    // skips their MFMAs (same loads and barriers), so the tile costs MFMA
+    // time in proportion to its rows.
+    const int nfrag = min(FM, max(0, (tile_rows - wm * TM + 31) / 32));
+    auto stream = [&](auto full) {
+      constexpr bool FULL = decltype(full)::value;
+      auto mma_rows = [&](const bf16x8* pa, const bf16x8* pb) {
+        if constexpr (FULL) {
+          mma(pa, pb);
+        } else {
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        if (kk + 1 < KK) read_frags(cur, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
-        mma(fa[kk & 1], fb[kk & 1]);
-        if (kk == 0) {
-          __builtin_amdgcn_sched_group_barrier(0x0020, LPW, 0);  // VMEM (DMA)
-          __builtin_amdgcn_sched_group_barrier(0x0100, NFR, 0);  // first reads
+          for (int x = 0; x < FM; ++x)
+            if (x < nfrag)
+#pragma unroll
+              for (int y = 0; y < FN; ++y)
+                acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb[y], pa[x], acc[x][y],
+                                                                   0, 0, 0);
         }
-        if (kk + 1 < KK) interleave();
-        else __builtin_amdgcn_sched_group_barrier(0x0008, NMF, 0);
+      };
+#pragma unroll
+      for (int t = 0; t + 1 < S; ++t) issue(t);
+      for (int kt = 0; kt < nk; ++kt) {
+        wait_vmcnt<(S - 2) * LPW>();
+        wg_barrier();
+        issue(kt + S - 1);
+        const int cur = kt % S;
+        read_frags(cur, 0, fa[0], fb[0]);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          if (kk + 1 < KK) read_frags(cur, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+          mma_rows(fa[kk & 1], fb[kk & 1]);
+          if (kk == 0) {
+            __builtin_amdgcn_sched_group_barrier(0x0020, LPW, 0);  // VMEM (DMA)
+            __builtin_amdgcn_sched_group_barrier(0x0100, NFR, 0);  // first reads
+          }
+          if (kk + 1 < KK) interleave();
+          else __builtin_amdgcn_sched_group_barrier(0x0008, NMF, 0);
+        }
       }
-    }
+    };
+    if (nfrag == FM)
+      stream(std::true_type{});
+    else
+      stream(std::false_type{});
   } else {
   #pragma unroll
     for (int t = 0; t <= D; ++t) issue(t);
@@ -412,10 +454,8 @@ void gemm_dma_kernel(Args a) {
         for (int i = 0; i < 4; ++i)
           v[i] = silu(acc[x][0][4 * q + i]) * acc[x][0][4 * q + i + 8];
         uint2 pk;
-        pk.x = static_cast<uint32_t>(f32_to_bf16(v[0])) |
-               (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-        pk.y = static_cast<uint32_t>(f32_to_bf16(v[2])) |
-               (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+        pk.x = pack_bf16x2(v[0], v[1]);
+        pk.y = pack_bf16x2(v[2], v[3]);
         if (m0 + row < Mj)
           *reinterpret_cast<uint2*>(&a.out[orow + c0 + 8 * q + 4 * fhalf]) = pk;
       }
@@ -423,32 +463,77 @@ void gemm_dma_kernel(Args a) {
     return;
   }
   constexpr int OUT_FN = MODE == GATEUP ? FN / 2 : FN;
+  if constexpr (MODE == GATEUP) {
+    // gate-up: 128 h columns per tile row; each lane stores its 4-column
+    // groups directly (8-byte stores), which measured slightly faster than
+    // staging these narrow rows through LDS
 #pragma unroll
-  for (int x = 0; x < FM; ++x) {
-    const int row = wm * TM + x * 32 + fr;
-    const bool live = m0 + row < Mj;
-    const size_t orow = static_cast<size_t>(row0 + m0 + row) * a.NC;
+    for (int x = 0; x < FM; ++x) {
+      const int row = wm * TM + x * 32 + fr;
+      const bool live = m0 + row < Mj;
+      const size_t orow = static_cast<size_t>(row0 + m0 + row) * a.NC;
 #pragma unroll
-    for (int y = 0; y < OUT_FN; ++y) {
-      const int c0 = MODE == GATEUP ? nt * (BN / 2) + wn * (TN / 2) + y * 32
-                                    : nt * BN + wn * TN + y * 32;
+      for (int y = 0; y < OUT_FN; ++y) {
+        const int c0 = nt * (BN / 2) + wn * (TN / 2) + y * 32;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float v[4];
+        for (int q = 0; q < 4; ++q) {
+          float v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * q + i;
-          v[i] = MODE == GATEUP ? silu(acc[x][y][r]) * acc[x][y + FN / 2][r]
-                                : acc[x][y][r];
+          for (int i = 0; i < 4; ++i)
+            v[i] = silu(acc[x][y][4 * q + i]) * acc[x][y + FN / 2][4 * q + i];
+          uint2 pk;
+          pk.x = pack_bf16x2(v[0], v[1]);
+          pk.y = pack_bf16x2(v[2], v[3]);
+          if (live)
+            *reinterpret_cast<uint2*>(&a.out[orow + c0 + 8 * q + 4 * fhalf]) = pk;
         }
-        uint2 pk;
-        pk.x = static_cast<uint32_t>(f32_to_bf16(v[0])) |
-               (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-        pk.y = static_cast<uint32_t>(f32_to_bf16(v[2])) |
-               (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
-        if (live)
-          *reinterpret_cast<uint2*>(&a.out[orow + c0 + 8 * q + 4 * fhalf]) = pk;
       }
+    }
+  } else {
+    // down: the output tile is staged through LDS (the ring is free once
+    // every wave has passed the barrier): each lane writes its 4-column groups
+    // of bf16 results into a [BM][OUTC] tile whose row pitch is padded by 16
+    // bytes (rows start 16 banks apart), then the workgroup stores whole tile
+    // rows with 16-byte vector stores, consecutive lanes on consecutive
+    // addresses.
+    constexpr int OUTC = BN;  // output columns of the tile
+    constexpr int PITCH = OUTC * 2 + 16;  // bytes per LDS row
+    __syncthreads();
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(3))) u32x2 lds_u2;
+    typedef __attribute__((address_space(3))) const u32x4 lds_u4;
+    typedef __attribute__((address_space(3))) unsigned char lds_wbyte;
+    lds_wbyte* ot = (lds_wbyte*)(smem);
+#pragma unroll
+    for (int x = 0; x < FM; ++x) {
+      const int row = wm * TM + x * 32 + fr;
+#pragma unroll
+      for (int y = 0; y < OUT_FN; ++y) {
+        const int c0 = wn * TN + y * 32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * q + i;
+            v[i] = acc[x][y][r];
+          }
+          u32x2 pk;
+          pk.x = pack_bf16x2(v[0], v[1]);
+          pk.y = pack_bf16x2(v[2], v[3]);
+          *(lds_u2*)(ot + row * PITCH + (c0 + 8 * q + 4 * fhalf) * 2) = pk;
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int CH = OUTC / 8;  // 16-byte chunks per tile row
+    const int col0 = nt * BN;
+    const int rows = min(BM, Mj - m0);
+    for (int i = tid; i < rows * CH; i += NTH) {
+      const int r = i / CH, c = i % CH;
+      const u32x4 v = *(lds_u4*)(ot + r * PITCH + c * 16);
+      *reinterpret_cast<u32x4*>(
+          &a.out[static_cast<size_t>(row0 + m0 + r) * a.NC + col0 + c * 8]) = v;
     }
   }
 }
@@ -501,7 +586,9 @@ __global__ __launch_bounds__(256) void down_f32(
 // ------------------------------------------------------------------ host
 template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WPE = 1>
 static int launch_gemm_dma(const Args& a, int rows_cap, hipStream_t s) {
-  constexpr size_t lds = static_cast<size_t>(S) * (BM + BN) * BK * 2;
+  constexpr size_t ring = static_cast<size_t>(S) * (BM + BN) * BK * 2;
+  constexpr size_t epi = MODE == DOWN ? static_cast<size_t>(BM) * (BN * 2 + 16) : 0;
+  constexpr size_t lds = ring > epi ? ring : epi;
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute(
@@ -514,7 +601,7 @@ static int launch_gemm_dma(const Args& a, int rows_cap, hipStream_t s) {
   long grid = static_cast<long>(mt_ub) * a.n_tiles;
   grid = (grid + 7) / 8 * 8;
   hipLaunchKernelGGL((gemm_dma_kernel<MODE, BM, BN, BK, WM, WN, S, WPE>), dim3(grid),
-                     dim3(NT), lds, s, a);
+                     dim3(WM * WN * MOE_WAVE), lds, s, a);
   return MOE_OK;
 }
 
@@ -524,24 +611,27 @@ static int launch_gemm_dma(const Args& a, int rows_cap, hipStream_t s) {
 using namespace moe;
 using namespace moe::ffn;
 
-// Prefill tiles: 256 rows x 256 columns of C per workgroup (2 x 2 waves,
-// each a 128 x 128 block of 4 x 4 fragments), K slices of 32 through a
-// 4-stage direct-to-LDS ring.  The gate-up tile covers 128 h columns (128
-// gate rows + 128 up rows of W13), the down tile 256 output columns.
+// Prefill tiles: 256 rows x 256 columns of C per workgroup of 8 waves (2 x
+// 4, each a 128 x 64 block of 4 x 2 fragments, two waves per SIMD), K slices
+// of 64 (whole 128-byte row segments per load) through a 2-stage
+// direct-to-LDS ring.  The gate-up tile covers 128 h columns (128 gate rows
+// + 128 up rows of W13), the down tile 256 output columns.  Measured on
+// MI355X against 4 waves with K slices of 32 in 4 stages: 3-6 % faster on
+// the multimodal and Mixtral prefill shapes.
 #ifndef MOE_GU_CFG
-#define MOE_GU_CFG 256, 256, 32, 2, 2
+#define MOE_GU_CFG 256, 256, 64, 2, 4
 #endif
 #ifndef MOE_DN_CFG
-#define MOE_DN_CFG 256, 256, 32, 2, 2
+#define MOE_DN_CFG 256, 256, 64, 2, 4
 #endif
 #ifndef MOE_DN_STAGES
-#define MOE_DN_STAGES 4
+#define MOE_DN_STAGES 2
 #endif
 #ifndef MOE_DN_WPE
 #define MOE_DN_WPE 1
 #endif
 #ifndef MOE_STAGES
-#define MOE_STAGES 4
+#define MOE_STAGES 2
 #endif
 // Decode tiles: 32 or 128 token rows x 128 or 256 weight rows (1 x 4
 // waves), K through a streaming ring.  Measured on MI355X (qwen3 and
