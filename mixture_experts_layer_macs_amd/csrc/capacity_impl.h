@@ -39,6 +39,8 @@ namespace cap {
 enum : uint8_t { ST_KEPT = 0, ST_OVER = 1, ST_PLACED = 2, ST_MASK = 3,
                  ST_SERE = 4 };
 
+enum : unsigned { PH_RUN = 0, PH_FINISH = 1, PH_DONE = 2 };
+
 constexpr int64_t CAP_CLAMP = int64_t(1) << 62;
 
 struct Args {
@@ -72,6 +74,11 @@ struct Args {
   uint8_t* active;     // [N]
   // control words: zero between calls (each is cleared after its last use)
   unsigned* ticket;                 // [1]
+  // progress of a multi-launch call, set by the first launch: PH_RUN, then
+  // PH_FINISH once no overflowed slot is left unplaced, PH_DONE once the
+  // slots are final; pending counts the unplaced overflowed slots
+  unsigned* phase;                  // [1]
+  unsigned long long* pending;      // [1] (two's complement sum)
   uint32_t* act_bits;               // [32]  experts with a round-0 proposer
   unsigned long long* adm;          // [N]   max admitted running weight
   unsigned long long* total;        // [N]   proposal weight (capacity off)
@@ -272,6 +279,10 @@ __device__ void global_step(const Args& a, int r, int64_t* red, int32_t* lds) {
     }
     __syncthreads();
     if (tid < 32) a.act_bits[tid] = 0u;
+    if (G > 1 && tid == 0) {
+      *a.phase = PH_RUN;
+      *a.pending = 0ull;
+    }
   } else {
     for (int e = tid; e < N; e += nthr) {
       const int64_t m = static_cast<int64_t>(a.adm[e]);
@@ -281,6 +292,10 @@ __device__ void global_step(const Args& a, int r, int64_t* red, int32_t* lds) {
       if (r > a.R) a.load_q[e] = a.capv[e] - d;
     }
   }
+  // every workgroup added its change of the pending count before the
+  // ticket: none left after round r - 1 means rounds r .. R offer nothing
+  if (G > 1 && r >= 1 && r <= a.R && tid == 0 && atomicAdd(a.pending, 0ull) == 0ull)
+    *a.phase = PH_FINISH;
   if (r <= a.R) {
     column_scan<int64_t>(a.part, a.base, nullptr, G, N, lds, a.lds_scan);
   } else {
@@ -330,11 +345,29 @@ __device__ void cap_rounds(const Args& a, int g, int r_first, int r_last,
   // overflowed slot is left unplaced: the overflow set only shrinks, so the
   // remaining rounds could admit nothing.
   const bool track = a.G == 1 && r_first == 0 && r_last == a.R + 1;
+  const bool multi = a.G > 1;
   if (threadIdx.x == 0) s_pending = 0;
+  if (multi && r_first >= 1) {
+    // a launch after the first: skip the rounds that can place nothing
+    __shared__ unsigned s_phase;
+    if (threadIdx.x == 0) s_phase = *a.phase;  // set by an earlier launch
+    __syncthreads();
+    const unsigned ph = s_phase;
+    if (ph == PH_DONE) return;
+    if (ph == PH_FINISH) {
+      finalize_slots(a, g, t0, t1, red);
+      if (!last_block(a)) return;
+      global_step(a, a.R + 1, red, run);
+      if (threadIdx.x == 0) *a.phase = PH_DONE;
+      return;
+    }
+  }
   for (int r = r_first; r <= r_last; ++r) {
     if (r >= 1) {
-      apply(a, r - 1, g, t0, t1, amax, track ? &s_pending : nullptr);
+      apply(a, r - 1, g, t0, t1, amax, (track || multi) ? &s_pending : nullptr);
       __syncthreads();
+      if (multi && threadIdx.x == 0 && s_pending != 0)
+        atomicAdd(a.pending, static_cast<unsigned long long>(static_cast<long long>(s_pending)));
       if (track && r <= a.R && s_pending == 0) {
         finalize_slots(a, g, t0, t1, red);
         __syncthreads();
@@ -424,7 +457,10 @@ __device__ void cap_off(const Args& a, int g, unsigned char* smem) {
 
 // ------------------------------------------------------------------ host
 // Workspace: a fixed control block (zero between calls, independent of T so
-// one workspace serves any batch size), then the per-call arrays.
+// one workspace serves any batch size), then the per-call arrays.  The
+// ticket's 256-byte block also holds the phase (byte 64) and pending count
+// (byte 128) of a multi-launch call; the first launch sets both, so they
+// need not be zero between calls.
 constexpr size_t CTRL_TICKET = 0;
 constexpr size_t CTRL_ACT = 256;
 constexpr size_t CTRL_ADM = 512;
@@ -521,6 +557,8 @@ inline Args make_args(const int32_t* topk_ids, const int32_t* slot_in,
   a.drem = reinterpret_cast<int64_t*>(ws + L.drem);
   a.active = reinterpret_cast<uint8_t*>(ws + L.active);
   a.ticket = reinterpret_cast<unsigned*>(ws + CTRL_TICKET);
+  a.phase = reinterpret_cast<unsigned*>(ws + CTRL_TICKET + 64);
+  a.pending = reinterpret_cast<unsigned long long*>(ws + CTRL_TICKET + 128);
   a.act_bits = reinterpret_cast<uint32_t*>(ws + CTRL_ACT);
   a.adm = reinterpret_cast<unsigned long long*>(ws + CTRL_ADM);
   a.total = reinterpret_cast<unsigned long long*>(ws + CTRL_TOTAL);
