@@ -45,9 +45,9 @@ GEMM_SOURCES = ("mixture_experts_layer_macs_amd/csrc/ffn.hip",
                 "mixture_experts_layer_macs_amd/csrc/common.h")
 HBM_COUNTERS = {
     "qwen3_decode_b128": dict(
-        kernel="gate_up_swiglu", fetch_kib=131808.3, write_kib=1536.0,
+        kernel="gate_up_swiglu", fetch_kib=130542.9, write_kib=1536.0,
         fetch_scale=2.0, write_scale=1.0,
-        sources_sha256="5b19f78cd58f440dfdb4f976b681256e7ae64a0f221e78cf0e765450eb95e2bb"),
+        sources_sha256="b681bd82ee652bd24aebd801321f582c1fea99c84b669be0e785f2c6c84fc37d"),
 }
 
 
@@ -317,20 +317,22 @@ def main():
 
     fused = lay.can_fuse and not args.separate_routing
 
-    def step(i, ev=None):
-        w13, w2 = w13s[i % len(w13s)], w2s[i % len(w2s)]
+    def gate_up(i):
+        B.moe_ffn_gate_up(d["x"], lay.disp["row_token"],
+                          lay.disp["expert_offsets"], w13s[i % len(w13s)], k, h)
+
+    def down(i):
+        B.moe_ffn_down(h, lay.disp["expert_offsets"], w2s[i % len(w2s)], T, k,
+                       lay.out_rows)
+
+    def step(i, skip=()):
         lay.routing(d["logits"], d["is_visual"], d["entropy_w"], d["modality"],
                     d["sim"], d["prot"], wl.kprime, wl.rho, wl.gamma, wl.lam,
                     wl.group, fused=fused)
-        if ev is not None:
-            ev[0].record()
-        B.moe_ffn_gate_up(d["x"], lay.disp["row_token"],
-                          lay.disp["expert_offsets"], w13, k, h)
-        if ev is not None:
-            ev[1].record()
-        B.moe_ffn_down(h, lay.disp["expert_offsets"], w2, T, k, lay.out_rows)
-        if ev is not None:
-            ev[2].record()
+        if "gate_up" not in skip:
+            gate_up(i)
+        if "down" not in skip:
+            down(i)
         B.moe_combine(lay.out_rows, lay.disp["slot_row"], lay.topk_gates, lay.y)
 
     print("[bench] warmup", file=sys.stderr, flush=True)
@@ -338,49 +340,54 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
-           for _ in range(args.steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    print("[bench] timed steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    # Hold the stream with a spin kernel while the host enqueues every timed
-    # step, so that the steps then run back to back and each event pair
-    # brackets GPU work only (no host launch latency inside an interval).
-    hold_gpu(args.steps * 1e-4 + 2e-3)
-    t_wall = time.perf_counter()
-    start.record()
-    for i in range(args.steps):
-        step(i, evs[i])
-    stop.record()
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms = start.elapsed_time(stop) / args.steps
-    gu_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    dn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    def timed(skip=(), graph=False):
+        """Mean ms per step over `steps` steps, HIP events at the two ends of
+        the region only.  Eager: the stream is held by a spin kernel while
+        the host queues the steps, so they then run back to back.  Graph: the
+        step is captured once per weight copy and replayed."""
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        if graph:
+            graphs = []
+            cap_stream = torch.cuda.Stream()
+            for c in range(len(w13s)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap_stream):
+                    step(c, skip)
+                graphs.append(g)
+            for i in range(args.warmup):
+                graphs[i % len(graphs)].replay()
+            torch.cuda.synchronize()
+            e0.record()
+            for i in range(args.steps):
+                graphs[i % len(graphs)].replay()
+            e1.record()
+        else:
+            torch.cuda.synchronize()
+            hold_gpu(args.steps * 1e-4 + 2e-3)
+            e0.record()
+            for i in range(args.steps):
+                step(i, skip)
+            e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
 
-    # second timed region: the same step captured once per weight copy in a
-    # HIP graph and replayed (no host launch overhead between kernels)
-    graph_ms = None
-    if not args.no_graph:
-        graphs = []
-        cap_stream = torch.cuda.Stream()
-        for c in range(len(w13s)):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=cap_stream):
-                step(c)
-            graphs.append(g)
-        for i in range(args.warmup):
-            graphs[i % len(graphs)].replay()
-        torch.cuda.synchronize()
-        g0 = torch.cuda.Event(enable_timing=True)
-        g1 = torch.cuda.Event(enable_timing=True)
-        g0.record()
-        for i in range(args.steps):
-            graphs[i % len(graphs)].replay()
-        g1.record()
-        torch.cuda.synchronize()
-        graph_ms = g0.elapsed_time(g1) / args.steps
+    print("[bench] timed steps", file=sys.stderr, flush=True)
+    t_wall = time.perf_counter()
+    ms = timed()
+    t_wall = time.perf_counter() - t_wall
+    # second timed region: the same step replayed from HIP graphs (no host
+    # launch overhead between kernels)
+    graph_ms = None if args.no_graph else timed(graph=True)
+
+    # In-step duration of each expert GEMM: the step time minus the time of
+    # the same step with that kernel left out (same timing mode).  An event
+    # pair around a single kernel would add the dispatch gap after the first
+    # event to the interval.
+    use_graph = not args.no_graph
+    full_ms = graph_ms if use_graph else ms
+    gu_ms = full_ms - timed(("gate_up",), use_graph)
+    dn_ms = full_ms - timed(("down",), use_graph)
 
     off = lay.disp["expert_offsets"].cpu().numpy()
     counts = np.diff(off)
