@@ -43,6 +43,7 @@ struct Args {
   int N, K, NC, I;         // K: reduction length; NC: output columns
   long w_stride;           // weight elements per expert
   int n_tiles;
+  int dual_limit;          // gemm_dual_kernel: most tiles of the first height
 };
 
 // Two fp32 values to a packed bf16 pair (round to nearest even), one
@@ -172,11 +173,10 @@ __device__ __forceinline__ void interleave_groups() {
   }
 }
 
-// WM x WN waves per workgroup (4 or 8); WPE workgroups per CU.
-template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WPE>
-__global__ __launch_bounds__(WM * WN * MOE_WAVE)
-__attribute__((amdgpu_waves_per_eu(WM * WN / 4, WPE * WM * WN / 4)))
-void gemm_dma_kernel(Args a) {
+// One tile of WM x WN waves (4 or 8).  smem: the dynamic LDS block; cum:
+// LDS [N + 1] for the tile search.
+template <int MODE, int BM, int BN, int BK, int WM, int WN, int S>
+__device__ __forceinline__ void gemm_tile(const Args& a, unsigned char* smem, int* cum) {
   static_assert(S >= 2 && S <= 8, "pipeline depth");
   constexpr int W = WM * WN, NTH = W * MOE_WAVE;  // waves, threads
   static_assert(W == 4 || W == 8, "4 or 8 waves");
@@ -199,9 +199,6 @@ void gemm_dma_kernel(Args a) {
   constexpr int LPW = QA + QB;                // DMA loads per wave per stage
   constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
   constexpr int STAGE = A_BYTES + B_BYTES;
-
-  extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int cum[1025];
 
   int j, m0, nt, Mj, row0;
   if (!find_tile<BM>(a, cum, j, m0, nt, Mj, row0)) return;
@@ -538,6 +535,44 @@ void gemm_dma_kernel(Args a) {
   }
 }
 
+// WM x WN waves per workgroup; WPE workgroups per CU.
+template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WPE>
+__global__ __launch_bounds__(WM * WN * MOE_WAVE)
+__attribute__((amdgpu_waves_per_eu(WM * WN / 4, WPE * WM * WN / 4)))
+void gemm_dma_kernel(Args a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int cum[1025];
+  gemm_tile<MODE, BM, BN, BK, WM, WN, S>(a, smem, cum);
+}
+
+// Decode gate-up with the tile height chosen on the device: tiles of BMA
+// token rows (S_A stages) when they number at most a.dual_limit, i.e. when
+// every tile gets a workgroup slot at once, else tiles of BMB rows (S_B
+// stages).  Every workgroup reads the same offsets, so all take the same
+// branch; the grid covers the larger tile count.
+template <int MODE, int BN, int BK, int BMA, int SA, int BMB, int SB, int WPE>
+__global__ __launch_bounds__(4 * MOE_WAVE)
+__attribute__((amdgpu_waves_per_eu(1, WPE)))
+void gemm_dual_kernel(Args a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int cum[1025];
+  __shared__ int s_tiles;
+  if (threadIdx.x < MOE_WAVE) {
+    int acc = 0;
+    for (int j0 = 0; j0 < a.N; j0 += MOE_WAVE) {
+      const int e = j0 + lane_id();
+      const int m = e < a.N ? a.offsets[e + 1] - a.offsets[e] : 0;
+      acc += wave_sum((m + BMA - 1) / BMA);
+    }
+    if (threadIdx.x == 0) s_tiles = acc * a.n_tiles;
+  }
+  __syncthreads();
+  if (s_tiles <= a.dual_limit)
+    gemm_tile<MODE, BMA, BN, BK, 1, 4, SA>(a, smem, cum);
+  else
+    gemm_tile<MODE, BMB, BN, BK, 1, 4, SB>(a, smem, cum);
+}
+
 // ------------------------------------------------------------- fp32 path
 // Plain fp32 FMA kernels (small fp32 layers); one thread per output value.
 __device__ __forceinline__ int expert_of_row(const int32_t* off, int N, int row) {
@@ -605,6 +640,30 @@ static int launch_gemm_dma(const Args& a, int rows_cap, hipStream_t s) {
   return MOE_OK;
 }
 
+template <int MODE, int BN, int BK, int BMA, int SA, int BMB, int SB, int WPE>
+static int launch_gemm_dual(Args a, int rows_cap, hipStream_t s) {
+  constexpr size_t la = static_cast<size_t>(SA) * (BMA + BN) * BK * 2;
+  constexpr size_t lb = static_cast<size_t>(SB) * (BMB + BN) * BK * 2;
+  constexpr size_t lds = la > lb ? la : lb;
+  static bool attr_set = false;
+  const void* fn =
+      reinterpret_cast<const void*>(gemm_dual_kernel<MODE, BN, BK, BMA, SA, BMB, SB, WPE>);
+  if (!attr_set) {
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(lds)) != hipSuccess)
+      return MOE_EHIP;
+    attr_set = true;
+  }
+  a.dual_limit = WPE * cu_count();
+  constexpr int BMIN = BMA < BMB ? BMA : BMB;
+  const int mt_ub = (rows_cap + BMIN - 1) / BMIN + a.N;
+  long grid = static_cast<long>(mt_ub) * a.n_tiles;
+  grid = (grid + 7) / 8 * 8;
+  hipLaunchKernelGGL((gemm_dual_kernel<MODE, BN, BK, BMA, SA, BMB, SB, WPE>), dim3(grid),
+                     dim3(4 * MOE_WAVE), lds, s, a);
+  return MOE_OK;
+}
+
 }  // namespace ffn
 }  // namespace moe
 
@@ -646,9 +705,15 @@ using namespace moe::ffn;
 //            or of 128 with 3 stages for reductions of 4096 or more.
 //   K slices of 32 (64-byte row segments) stream worse than 64 or 128.
 // Decode tile configurations {token rows, K slice, ring stages}; the _WIDE
-// ones serve reductions of 4096 or more.
+// ones serve reductions of 4096 or more.  Gate-up below that picks on the
+// device between DEC_GU (one tile per expert and weight panel, when those
+// tiles fit the workgroup slots at once) and DEC_GU_MANY (32-row tiles and
+// a deeper ring, when many experts are active).
 #ifndef MOE_DEC_GU
 #define MOE_DEC_GU 128, 64, 2
+#endif
+#ifndef MOE_DEC_GU_MANY
+#define MOE_DEC_GU_MANY 32, 64, 3
 #endif
 #ifndef MOE_DEC_GU_WIDE
 #define MOE_DEC_GU_WIDE 32, 128, 3
@@ -662,7 +727,8 @@ using namespace moe::ffn;
 struct DecCfg {
   int bm, bk, s;
 };
-constexpr DecCfg DEC_GU = {MOE_DEC_GU}, DEC_GU_WIDE = {MOE_DEC_GU_WIDE},
+constexpr DecCfg DEC_GU = {MOE_DEC_GU}, DEC_GU_MANY = {MOE_DEC_GU_MANY},
+                 DEC_GU_WIDE = {MOE_DEC_GU_WIDE},
                  DEC_DN = {MOE_DEC_DN}, DEC_DN_WIDE = {MOE_DEC_DN_WIDE};
 // LDS of a decode workgroup with bn weight rows: the ring plus the static
 // tile-count table
@@ -765,8 +831,12 @@ extern "C" int moe_ffn_gate_up(const void* x, const int32_t* row_token,
       constexpr DecCfg c = DEC_GU_WIDE;
       st = launch_gemm_dma<GATEUP, c.bm, 128, c.bk, 1, 4, c.s, dec_wpe(c, 128)>(g, rows_cap, s);
     } else {
-      constexpr DecCfg c = DEC_GU;
-      st = launch_gemm_dma<GATEUP, c.bm, 128, c.bk, 1, 4, c.s, dec_wpe(c, 128)>(g, rows_cap, s);
+      // one wave of DEC_GU tiles when they fit the workgroup slots (few
+      // active experts, e.g. after SERE), else the DEC_GU_MANY tiles
+      constexpr DecCfg c = DEC_GU, m = DEC_GU_MANY;
+      static_assert(c.bk == m.bk, "one K slice for both tile heights");
+      constexpr int wpe = dec_wpe(c, 128) < dec_wpe(m, 128) ? dec_wpe(c, 128) : dec_wpe(m, 128);
+      st = launch_gemm_dual<GATEUP, 128, c.bk, c.bm, c.s, m.bm, m.s, wpe>(g, rows_cap, s);
     }
     if (st != MOE_OK) return MOE_EHIP;
   } else {
