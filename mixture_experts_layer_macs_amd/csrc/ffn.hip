@@ -62,12 +62,12 @@ __device__ __forceinline__ float silu(float g) {
   return g * __builtin_amdgcn_rcpf(1.f + __expf(-g));
 }
 
-// Locate the tile of this workgroup.  cum: LDS [N+1] cumulative tile counts.
-// Returns false for surplus workgroups.
+// Locate the tile of this workgroup.  cum: LDS [N+2], the cumulative tile
+// counts and then the total.  Returns false for surplus workgroups.
 template <int BM>
 __device__ bool find_tile(const Args& a, int* cum, int& j, int& m0, int& nt,
                           int& Mj, int& row0) {
-  __shared__ int s_total;
+  int* s_total = cum + a.N + 1;
   if (threadIdx.x < MOE_WAVE) {
     int acc = 0;
     for (int j0 = 0; j0 < a.N; j0 += MOE_WAVE) {
@@ -83,11 +83,11 @@ __device__ bool find_tile(const Args& a, int* cum, int& j, int& m0, int& nt,
     }
     if (threadIdx.x == 0) {
       cum[0] = 0;
-      s_total = acc;
+      *s_total = acc;
     }
   }
   __syncthreads();
-  const int total = s_total;
+  const int total = *s_total;
   const int p = blockIdx.x;
   const int q = (total + 7) / 8;  // tiles per XCD
   const int slot = p / 8;
@@ -173,10 +173,13 @@ __device__ __forceinline__ void interleave_groups() {
   }
 }
 
-// One tile of WM x WN waves (4 or 8).  smem: the dynamic LDS block; cum:
-// LDS [N + 1] for the tile search.
+// The tile of expert j, rows m0 .. m0 + BM - 1 of its Mj rows (dispatch rows
+// from row0), column tile nt, computed by WM x WN waves (4 or 8) with an
+// S-stage ring in smem (the dynamic LDS block).  All five values are the
+// same in every lane.
 template <int MODE, int BM, int BN, int BK, int WM, int WN, int S>
-__device__ __forceinline__ void gemm_tile(const Args& a, unsigned char* smem, int* cum) {
+__device__ __forceinline__ void gemm_body(const Args& a, unsigned char* smem, int j, int m0,
+                                          int nt, int Mj, int row0) {
   static_assert(S >= 2 && S <= 8, "pipeline depth");
   constexpr int W = WM * WN, NTH = W * MOE_WAVE;  // waves, threads
   static_assert(W == 4 || W == 8, "4 or 8 waves");
@@ -199,15 +202,6 @@ __device__ __forceinline__ void gemm_tile(const Args& a, unsigned char* smem, in
   constexpr int LPW = QA + QB;                // DMA loads per wave per stage
   constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
   constexpr int STAGE = A_BYTES + B_BYTES;
-
-  int j, m0, nt, Mj, row0;
-  if (!find_tile<BM>(a, cum, j, m0, nt, Mj, row0)) return;
-  // the same in every lane; kept in scalar registers
-  j = __builtin_amdgcn_readfirstlane(j);
-  m0 = __builtin_amdgcn_readfirstlane(m0);
-  nt = __builtin_amdgcn_readfirstlane(nt);
-  Mj = __builtin_amdgcn_readfirstlane(Mj);
-  row0 = __builtin_amdgcn_readfirstlane(row0);
 
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / MOE_WAVE);
@@ -535,14 +529,41 @@ __device__ __forceinline__ void gemm_tile(const Args& a, unsigned char* smem, in
   }
 }
 
+// Tile search (BM-row tiles) into scalar registers; false for surplus
+// workgroups.  cum: LDS [N + 1].
+template <int BM>
+__device__ __forceinline__ bool find_tile_s(const Args& a, int* cum, int& j, int& m0, int& nt,
+                                            int& Mj, int& row0) {
+  const bool live = find_tile<BM>(a, cum, j, m0, nt, Mj, row0);
+  // cum lives at the start of the ring, which the first loads overwrite:
+  // every wave must be done with the search first (surplus workgroups
+  // return together, all their waves having found no tile)
+  __syncthreads();
+  if (!live) return false;
+  j = __builtin_amdgcn_readfirstlane(j);
+  m0 = __builtin_amdgcn_readfirstlane(m0);
+  nt = __builtin_amdgcn_readfirstlane(nt);
+  Mj = __builtin_amdgcn_readfirstlane(Mj);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  return true;
+}
+
+template <int MODE, int BM, int BN, int BK, int WM, int WN, int S>
+__device__ __forceinline__ void gemm_tile(const Args& a, unsigned char* smem, int* cum) {
+  int j, m0, nt, Mj, row0;
+  if (find_tile_s<BM>(a, cum, j, m0, nt, Mj, row0))
+    gemm_body<MODE, BM, BN, BK, WM, WN, S>(a, smem, j, m0, nt, Mj, row0);
+}
+
 // WM x WN waves per workgroup; WPE workgroups per CU.
 template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WPE>
 __global__ __launch_bounds__(WM * WN * MOE_WAVE)
 __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WPE * WM * WN / 4)))
 void gemm_dma_kernel(Args a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int cum[1025];
-  gemm_tile<MODE, BM, BN, BK, WM, WN, S>(a, smem, cum);
+  // the tile search table shares the dynamic block with the ring, so the
+  // kernel has no static LDS and workgroups pack the CU's 160 KB exactly
+  gemm_tile<MODE, BM, BN, BK, WM, WN, S>(a, smem, reinterpret_cast<int*>(smem));
 }
 
 // Decode gate-up with the tile height chosen on the device: tiles of BMA
@@ -555,22 +576,47 @@ __global__ __launch_bounds__(4 * MOE_WAVE)
 __attribute__((amdgpu_waves_per_eu(1, WPE)))
 void gemm_dual_kernel(Args a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int cum[1025];
-  __shared__ int s_tiles;
+  int* cum = reinterpret_cast<int*>(smem);  // [N + 2], then the tile count
+  int* s_stat = cum + a.N + 2;               // tiles of BMA rows, most rows
   if (threadIdx.x < MOE_WAVE) {
-    int acc = 0;
+    int acc = 0, mx = 0;
     for (int j0 = 0; j0 < a.N; j0 += MOE_WAVE) {
       const int e = j0 + lane_id();
       const int m = e < a.N ? a.offsets[e + 1] - a.offsets[e] : 0;
       acc += wave_sum((m + BMA - 1) / BMA);
+      mx = max(mx, wave_max(m));
     }
-    if (threadIdx.x == 0) s_tiles = acc * a.n_tiles;
+    if (threadIdx.x == 0) {
+      s_stat[0] = acc * a.n_tiles;
+      s_stat[1] = mx;
+    }
   }
   __syncthreads();
-  if (s_tiles <= a.dual_limit)
+  const bool one_wave = s_stat[0] <= a.dual_limit;
+  const int most_rows = s_stat[1];
+  __syncthreads();  // the tile search below rewrites the table
+  if (one_wave) {
+    // One tile per expert and weight panel.  When no expert has more than
+    // 32 (64) rows, every tile runs with a 32 (64)-row A block, which
+    // leaves LDS for more ring stages: more weight bytes in flight for the
+    // same weight stream.  (Deepening only the small tiles of a launch that
+    // also has large ones made the large ones finish later.)
+    constexpr int RING = SA * (BMA + BN) * BK * 2;  // the LDS of the launch
+    constexpr int S32 = RING / ((32 + BN) * BK * 2), S64 = RING / ((64 + BN) * BK * 2);
+    if constexpr (BMA > 64 && S32 > SA && S64 >= SA) {
+      if (most_rows <= 32) {
+        gemm_tile<MODE, 32, BN, BK, 1, 4, (S32 < 8 ? S32 : 8)>(a, smem, cum);
+        return;
+      }
+      if (most_rows <= 64) {
+        gemm_tile<MODE, 64, BN, BK, 1, 4, (S64 < 8 ? S64 : 8)>(a, smem, cum);
+        return;
+      }
+    }
     gemm_tile<MODE, BMA, BN, BK, 1, 4, SA>(a, smem, cum);
-  else
+  } else {
     gemm_tile<MODE, BMB, BN, BK, 1, 4, SB>(a, smem, cum);
+  }
 }
 
 // ------------------------------------------------------------- fp32 path
@@ -730,9 +776,9 @@ struct DecCfg {
 constexpr DecCfg DEC_GU = {MOE_DEC_GU}, DEC_GU_MANY = {MOE_DEC_GU_MANY},
                  DEC_GU_WIDE = {MOE_DEC_GU_WIDE},
                  DEC_DN = {MOE_DEC_DN}, DEC_DN_WIDE = {MOE_DEC_DN_WIDE};
-// LDS of a decode workgroup with bn weight rows: the ring plus the static
-// tile-count table
-constexpr int dec_lds(DecCfg c, int bn) { return c.s * (c.bm + bn) * c.bk * 2 + 1025 * 4; }
+// LDS of a decode workgroup with bn weight rows: the ring (the tile-count
+// table shares it)
+constexpr int dec_lds(DecCfg c, int bn) { return c.s * (c.bm + bn) * c.bk * 2; }
 // workgroups per CU that the LDS allows (160 KB per CU), at most 4
 constexpr int dec_wpe(DecCfg c, int bn) {
   return (160 * 1024) / dec_lds(c, bn) < 4 ? (160 * 1024) / dec_lds(c, bn) : 4;
