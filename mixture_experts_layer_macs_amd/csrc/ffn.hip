@@ -177,7 +177,7 @@ __device__ __forceinline__ void interleave_groups() {
 // from row0), column tile nt, computed by WM x WN waves (4 or 8) with an
 // S-stage ring in smem (the dynamic LDS block).  All five values are the
 // same in every lane.
-template <int MODE, int BM, int BN, int BK, int WM, int WN, int S>
+template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int SB = S>
 __device__ __forceinline__ void gemm_body(const Args& a, unsigned char* smem, int j, int m0,
                                           int nt, int Mj, int row0) {
   static_assert(S >= 2 && S <= 8, "pipeline depth");
@@ -202,6 +202,15 @@ __device__ __forceinline__ void gemm_body(const Args& a, unsigned char* smem, in
   constexpr int LPW = QA + QB;                // DMA loads per wave per stage
   constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
   constexpr int STAGE = A_BYTES + B_BYTES;
+  // Ring layout.  Symmetric (SB == S): stage s holds slice A then slice B.
+  // Asymmetric: S stages of A, then SB stages of B, so the weights can be
+  // requested further ahead than the token rows.
+  constexpr bool ASYM = SB != S;
+  static_assert(!ASYM || (S == 2 && SB == 3) || (S == 3 && SB == 2),
+                "asymmetric ring: 2 and 3 stages");
+  constexpr int A_STRIDE = ASYM ? A_BYTES : STAGE;
+  constexpr int B_BASE = ASYM ? S * A_BYTES : A_BYTES;
+  constexpr int B_STRIDE = ASYM ? B_BYTES : STAGE;
 
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / MOE_WAVE);
@@ -263,16 +272,25 @@ __device__ __forceinline__ void gemm_body(const Args& a, unsigned char* smem, in
   // slice is the wave's A row group d, the rest its B row groups.
   const int nk = K / BK;
   auto dma = [&](int kslice, int d) {
-    const uint32_t st = lds_base + (kslice % S) * STAGE;
     const uint32_t k0 = static_cast<uint32_t>(min(kslice, nk - 1) * BK * 2);
     if (d < QA)
-      lds_dma16(rsrc_a, va[d], k0, st + (wave * QA + d) * 1024);
+      lds_dma16(rsrc_a, va[d], k0,
+                lds_base + (kslice % S) * A_STRIDE + (wave * QA + d) * 1024);
     else
-      lds_dma16(rsrc_b, vb[d - QA], k0, st + A_BYTES + (wave * QB + d - QA) * 1024);
+      lds_dma16(rsrc_b, vb[d - QA], k0,
+                lds_base + B_BASE + (kslice % SB) * B_STRIDE + (wave * QB + d - QA) * 1024);
   };
   auto issue = [&](int kslice) {
 #pragma unroll
     for (int d = 0; d < LPW; ++d) dma(kslice, d);
+  };
+  auto issue_a = [&](int kslice) {
+#pragma unroll
+    for (int d = 0; d < QA; ++d) dma(kslice, d);
+  };
+  auto issue_b = [&](int kslice) {
+#pragma unroll
+    for (int d = QA; d < LPW; ++d) dma(kslice, d);
   };
 
   f32x16 acc[FM][FN];
@@ -307,9 +325,9 @@ __device__ __forceinline__ void gemm_body(const Args& a, unsigned char* smem, in
   typedef __attribute__((address_space(3))) const unsigned char lds_byte;
   lds_byte* lds0 = (lds_byte*)(smem);
   bf16x8 fa[2][FM], fb[2][FN];
-  auto read_frags = [&](int stage, int kk, bf16x8* pa, bf16x8* pb) {
-    lds_byte* A_ = lds0 + stage * STAGE;
-    lds_byte* B_ = A_ + A_BYTES;
+  auto read_frags = [&](int kslice, int kk, bf16x8* pa, bf16x8* pb) {
+    lds_byte* A_ = lds0 + (kslice % S) * A_STRIDE;
+    lds_byte* B_ = lds0 + B_BASE + (kslice % SB) * B_STRIDE;
     const int sw = ((kk * 2 + fhalf) ^ ((frow >> SWS) & SWZ)) << 4;  // bytes
 #pragma unroll
     for (int x = 0; x < FM; ++x)
@@ -321,9 +339,9 @@ __device__ __forceinline__ void gemm_body(const Args& a, unsigned char* smem, in
   // The same reads, with the DMA requests of slice kslice spread over them
   // (load d after fragment read d * NFR / LPW), so that no run of requests
   // holds up the MFMAs that the scheduler places between the reads.
-  auto read_frags_dma = [&](int stage, int kk, bf16x8* pa, bf16x8* pb, int kslice) {
-    lds_byte* A_ = lds0 + stage * STAGE;
-    lds_byte* B_ = A_ + A_BYTES;
+  auto read_frags_dma = [&](int rslice, int kk, bf16x8* pa, bf16x8* pb, int kslice) {
+    lds_byte* A_ = lds0 + (rslice % S) * A_STRIDE;
+    lds_byte* B_ = lds0 + B_BASE + (rslice % SB) * B_STRIDE;
     const int sw = ((kk * 2 + fhalf) ^ ((frow >> SWS) & SWZ)) << 4;  // bytes
 #pragma unroll
     for (int f = 0; f < NFR; ++f) {
@@ -372,17 +390,41 @@ __device__ __forceinline__ void gemm_body(const Args& a, unsigned char* smem, in
                                                                    0, 0, 0);
         }
       };
+      if constexpr (ASYM && SB == 3) {
+        // A(0), B(0), B(1) ahead; iteration kt requests A(kt+1) then
+        // B(kt+2), so A(kt) has landed once at most the last group's B
+        // loads are outstanding, and B(kt), requested before it, too
+        issue_a(0);
+        issue_b(0);
+        issue_b(1);
+      } else if constexpr (ASYM) {  // the same with A and B exchanged
+        issue_b(0);
+        issue_a(0);
+        issue_a(1);
+      } else {
 #pragma unroll
-      for (int t = 0; t + 1 < S; ++t) issue(t);
+        for (int t = 0; t + 1 < S; ++t) issue(t);
+      }
       for (int kt = 0; kt < nk; ++kt) {
-        wait_vmcnt<(S - 2) * LPW>();
-        wg_barrier();
-        issue(kt + S - 1);
-        const int cur = kt % S;
-        read_frags(cur, 0, fa[0], fb[0]);
+        if constexpr (ASYM && SB == 3) {
+          wait_vmcnt<QB>();
+          wg_barrier();
+          issue_a(kt + 1);
+          issue_b(kt + 2);
+        } else if constexpr (ASYM) {
+          wait_vmcnt<QA>();
+          wg_barrier();
+          issue_b(kt + 1);
+          issue_a(kt + 2);
+        } else {
+          wait_vmcnt<(S - 2) * LPW>();
+          wg_barrier();
+          issue(kt + S - 1);
+        }
+        read_frags(kt, 0, fa[0], fb[0]);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          if (kk + 1 < KK) read_frags(cur, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+          if (kk + 1 < KK) read_frags(kt, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
           mma_rows(fa[kk & 1], fb[kk & 1]);
           if (kk == 0) {
             __builtin_amdgcn_sched_group_barrier(0x0020, LPW, 0);  // VMEM (DMA)
@@ -404,12 +446,10 @@ __device__ __forceinline__ void gemm_body(const Args& a, unsigned char* smem, in
     wg_barrier();
     read_frags(0, 0, fa[0], fb[0]);
     for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt % S;
-      const int nxt = (kt + 1) % S;
       // sub-slices 0 .. KK-2 of slice kt (fragment set kk & 1)
   #pragma unroll
       for (int kk = 0; kk + 1 < KK; ++kk) {
-        read_frags(cur, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+        read_frags(kt, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
         mma(fa[kk & 1], fb[kk & 1]);
         interleave();
       }
@@ -418,7 +458,7 @@ __device__ __forceinline__ void gemm_body(const Args& a, unsigned char* smem, in
       // last sub-slice of kt, reading slice kt+1's first fragments and
       // requesting slice kt+1+D meanwhile (on the last slice those reads
       // fetch stale data that nobody uses)
-      read_frags_dma(nxt, 0, fa[KK & 1], fb[KK & 1], kt + 1 + D);
+      read_frags_dma(kt + 1, 0, fa[KK & 1], fb[KK & 1], kt + 1 + D);
       mma(fa[(KK - 1) & 1], fb[(KK - 1) & 1]);
       interleave();
       if (KK & 1) {  // keep set 0 as "current" at the top of the loop
@@ -548,22 +588,23 @@ __device__ __forceinline__ bool find_tile_s(const Args& a, int* cum, int& j, int
   return true;
 }
 
-template <int MODE, int BM, int BN, int BK, int WM, int WN, int S>
+template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int SB = S>
 __device__ __forceinline__ void gemm_tile(const Args& a, unsigned char* smem, int* cum) {
   int j, m0, nt, Mj, row0;
   if (find_tile_s<BM>(a, cum, j, m0, nt, Mj, row0))
-    gemm_body<MODE, BM, BN, BK, WM, WN, S>(a, smem, j, m0, nt, Mj, row0);
+    gemm_body<MODE, BM, BN, BK, WM, WN, S, SB>(a, smem, j, m0, nt, Mj, row0);
 }
 
-// WM x WN waves per workgroup; WPE workgroups per CU.
-template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WPE>
+// WM x WN waves per workgroup; WPE workgroups per CU; S stages of A and SB
+// of B.
+template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WPE, int SB>
 __global__ __launch_bounds__(WM * WN * MOE_WAVE)
 __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WPE * WM * WN / 4)))
 void gemm_dma_kernel(Args a) {
   extern __shared__ __align__(16) unsigned char smem[];
   // the tile search table shares the dynamic block with the ring, so the
   // kernel has no static LDS and workgroups pack the CU's 160 KB exactly
-  gemm_tile<MODE, BM, BN, BK, WM, WN, S>(a, smem, reinterpret_cast<int*>(smem));
+  gemm_tile<MODE, BM, BN, BK, WM, WN, S, SB>(a, smem, reinterpret_cast<int*>(smem));
 }
 
 // Decode gate-up with the tile height chosen on the device: tiles of BMA
@@ -665,15 +706,15 @@ __global__ __launch_bounds__(256) void down_f32(
 }
 
 // ------------------------------------------------------------------ host
-template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WPE = 1>
+template <int MODE, int BM, int BN, int BK, int WM, int WN, int S, int WPE = 1, int SB = S>
 static int launch_gemm_dma(const Args& a, int rows_cap, hipStream_t s) {
-  constexpr size_t ring = static_cast<size_t>(S) * (BM + BN) * BK * 2;
+  constexpr size_t ring = (static_cast<size_t>(S) * BM + static_cast<size_t>(SB) * BN) * BK * 2;
   constexpr size_t epi = MODE == DOWN ? static_cast<size_t>(BM) * (BN * 2 + 16) : 0;
   constexpr size_t lds = ring > epi ? ring : epi;
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute(
-            reinterpret_cast<const void*>(gemm_dma_kernel<MODE, BM, BN, BK, WM, WN, S, WPE>),
+            reinterpret_cast<const void*>(gemm_dma_kernel<MODE, BM, BN, BK, WM, WN, S, WPE, SB>),
             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)) != hipSuccess)
       return MOE_EHIP;
     attr_set = true;
@@ -681,7 +722,7 @@ static int launch_gemm_dma(const Args& a, int rows_cap, hipStream_t s) {
   const int mt_ub = (rows_cap + BM - 1) / BM + a.N;
   long grid = static_cast<long>(mt_ub) * a.n_tiles;
   grid = (grid + 7) / 8 * 8;
-  hipLaunchKernelGGL((gemm_dma_kernel<MODE, BM, BN, BK, WM, WN, S, WPE>), dim3(grid),
+  hipLaunchKernelGGL((gemm_dma_kernel<MODE, BM, BN, BK, WM, WN, S, WPE, SB>), dim3(grid),
                      dim3(WM * WN * MOE_WAVE), lds, s, a);
   return MOE_OK;
 }
@@ -718,8 +759,8 @@ using namespace moe::ffn;
 
 // Prefill tiles: 256 rows x 256 columns of C per workgroup of 8 waves (2 x
 // 4, each a 128 x 64 block of 4 x 2 fragments, two waves per SIMD), K slices
-// of 64 (whole 128-byte row segments per load) through a 2-stage
-// direct-to-LDS ring.  The gate-up tile covers 128 h columns (128 gate rows
+// of 64 (whole 128-byte row segments per load) through a direct-to-LDS ring
+// of 2 token-row stages and 3 weight stages.  The gate-up tile covers 128 h columns (128 gate rows
 // + 128 up rows of W13), the down tile 256 output columns.  Measured on
 // MI355X against 4 waves with K slices of 32 in 4 stages: 3-6 % faster on
 // the multimodal and Mixtral prefill shapes.
@@ -737,6 +778,16 @@ using namespace moe::ffn;
 #endif
 #ifndef MOE_STAGES
 #define MOE_STAGES 2
+#endif
+// B (weight) ring depth of the prefill tiles: 3 stages of weights beside the
+// 2 of token rows fill the 160 KB exactly (down 5 % faster on the multimodal
+// prefill shape, the rest unchanged; 3 stages of token rows instead were
+// slower)
+#ifndef MOE_STAGES_B
+#define MOE_STAGES_B 3
+#endif
+#ifndef MOE_DN_STAGES_B
+#define MOE_DN_STAGES_B 3
 #endif
 // Decode tiles: 32 or 128 token rows x 128 or 256 weight rows (1 x 4
 // waves), K through a streaming ring.  Measured on MI355X (qwen3 and
@@ -887,8 +938,8 @@ extern "C" int moe_ffn_gate_up(const void* x, const int32_t* row_token,
     if (st != MOE_OK) return MOE_EHIP;
   } else {
     g.n_tiles = I / (GU_BN / 2);
-    if (launch_gemm_dma<GATEUP, GU_BM, GU_BN, GU_BK, GU_WM, GU_WN, MOE_STAGES, 1>(
-            g, rows_cap, s) != MOE_OK)
+    if (launch_gemm_dma<GATEUP, GU_BM, GU_BN, GU_BK, GU_WM, GU_WN, MOE_STAGES, 1,
+                        MOE_STAGES_B>(g, rows_cap, s) != MOE_OK)
       return MOE_EHIP;
   }
   return launch_status();
@@ -950,8 +1001,8 @@ extern "C" int moe_ffn_down(const void* h, const int32_t* expert_offsets,
     if (st != MOE_OK) return MOE_EHIP;
   } else {
     d.n_tiles = H / DN_BN;
-    if (launch_gemm_dma<DOWN, DN_BM, DN_BN, DN_BK, DN_WM, DN_WN, MOE_DN_STAGES, MOE_DN_WPE>(
-            d, rows_cap, s) != MOE_OK)
+    if (launch_gemm_dma<DOWN, DN_BM, DN_BN, DN_BK, DN_WM, DN_WN, MOE_DN_STAGES, MOE_DN_WPE,
+                        MOE_DN_STAGES_B>(d, rows_cap, s) != MOE_OK)
       return MOE_EHIP;
   }
   return launch_status();
