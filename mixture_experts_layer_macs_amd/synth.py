@@ -21,7 +21,9 @@ Recipe (per workload, see ``configs.py`` for the knobs):
 * similarity matrix: fp32, symmetric, off-diagonal U(0,1), diagonal 1;
 * protection matrix: u8, all-ones rows for ``n_protected`` seeded experts;
 * x ~ N(0,1) and expert weights ~ N(0,0.02), stored as fp32 or as bf16 bit
-  patterns (uint16) rounded to nearest-even.
+  patterns (uint16) rounded to nearest-even;
+* router weights W_g [N,H] ~ N(0, 1/H) (so x W_g^T has unit variance, like
+  the drawn logits), stored the same way.
 
 Every stream has its own ``numpy.random.SeedSequence`` key, so one input does
 not shift when another changes size.  Expert weights use one child seed per
@@ -39,7 +41,7 @@ from .configs import ZIPF_BETA, Workload
 
 # stream ids
 _S_LOGITS, _S_RANK, _S_STRAG, _S_VIS, _S_VISW, _S_MOD, _S_SIM, _S_PROT, \
-    _S_X, _S_W13, _S_W2, _S_FEAT = range(1, 13)
+    _S_X, _S_W13, _S_W2, _S_FEAT, _S_GATE = range(1, 14)
 
 
 def _rng(seed: int, stream: int, layer: int = 0) -> np.random.Generator:
@@ -127,6 +129,13 @@ def router_logits(wl: Workload, seed: int, layer: int = 0,
         raise ValueError(wl.logits)
     bias[0] += wl.skew_expert0
     return (z + bias[None, :]).astype(np.float32)
+
+
+def router_weights(wl: Workload, seed: int, layer: int = 0) -> np.ndarray:
+    """W_g [N,H] ~ N(0, 1/H): one row of H weights per expert."""
+    w = _rng(seed, _S_GATE, layer).standard_normal((wl.N, wl.H), dtype=np.float32)
+    w *= np.float32(1.0 / math.sqrt(wl.H))
+    return w if wl.dtype == "f32" else f32_to_bf16_bits(w)
 
 
 def expert_modality(wl: Workload, seed: int, layer: int = 0) -> np.ndarray:

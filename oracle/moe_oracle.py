@@ -71,6 +71,11 @@ independently implemented, by the GPU path):
       H over the batch's visual tokens; H~ = (H - mu) / (sigma + eps);
       w = sigmoid(-delta * H~) for visual tokens, 1 for text tokens.  delta
       and eps are not given by the page: parameters (defaults 1 and 1e-6).
+  R17 router scores (MACS §3.1: a router network G scores every expert; its
+      form is not given): a bias-free linear map z_t = W_g x_t with W_g
+      stored [N, H], one row of H weights per expert, in the activation
+      type; the scores are fp32 (the route step's input type).  Here z is
+      the exact fp64 product, rounded once to fp32 where the route needs it.
 """
 from __future__ import annotations
 
@@ -159,6 +164,23 @@ def route(logits: np.ndarray, k: int, R: int):
         for r in range(R):
             fallback[t, r] = order[k + r]
     return topk, gates, fallback
+
+
+# --------------------------------------------------------------------------
+# router scores  [MACS §3.1, the router network G; R17]
+# --------------------------------------------------------------------------
+def router_logits(x: np.ndarray, w_gate: np.ndarray, dtype: str) -> np.ndarray:
+    """z[t, j] = sum_h W_g[j, h] * x[t, h] in fp64 from the exact stored
+    values.  x [T,H], w_gate [N,H]; returns float64[T,N]."""
+    return decode(x, dtype) @ decode(w_gate, dtype).T
+
+
+def router_topk(x: np.ndarray, w_gate: np.ndarray, dtype: str, k: int,
+                R: int):
+    """route() over the router scores rounded once to fp32.  Returns
+    (logits float32[T,N], topk_ids, gates, fallback_ids)."""
+    z = router_logits(x, w_gate, dtype).astype(np.float32)
+    return (z, *route(z, k, R))
 
 
 # --------------------------------------------------------------------------

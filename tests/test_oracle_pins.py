@@ -473,3 +473,62 @@ def test_entropy_weight_degenerate_batches():
     one = np.zeros(5, np.uint8); one[2] = 1
     w, *_ = O.entropy_weights(x, one, "f32")
     assert w[2] == 0.5 and (np.delete(w, 2) == 1.0).all()  # sigma = 0: H~ = 0
+
+
+# ---------------------------------------------------------------- router
+# MACS §3.1, the router network G (reading R17: z_t = W_g x_t, W_g stored
+# [N, H]).  The scores are pinned by special inputs whose products are known
+# without a matrix product: one-hot tokens pick one weight column, an all-ones
+# token sums each expert's row, and sums of tokens give sums of scores.
+def _router_case(seed, T=12, H=40, N=7):
+    rng = np.random.default_rng(seed)
+    x = rng.integers(-4, 5, size=(T, H)).astype(np.float32)
+    w = rng.integers(-3, 4, size=(N, H)).astype(np.float32)
+    return x, w
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_router_onehot_tokens_pick_weight_columns(seed):
+    _, w = _router_case(seed)
+    N, H = w.shape
+    hot = [3, 0, H - 1, 17]
+    x = np.zeros((len(hot), H), dtype=np.float32)
+    for t, i in enumerate(hot):
+        x[t, i] = 2.0 ** (t - 1)
+    z = O.router_logits(x, w, "f32")
+    assert z.shape == (len(hot), N)
+    for t, i in enumerate(hot):
+        assert (z[t] == (2.0 ** (t - 1)) * w[:, i].astype(np.float64)).all()
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_router_ones_token_sums_rows_and_is_additive(seed):
+    x, w = _router_case(seed)
+    ones = np.ones((1, w.shape[1]), dtype=np.float32)
+    z1 = O.router_logits(ones, w, "f32")[0]
+    assert (z1 == w.astype(np.float64).sum(axis=1)).all()
+    # integer inputs: every product and sum is exact in fp64
+    a, b = x[:6], x[6:]
+    za, zb = O.router_logits(a, w, "f32"), O.router_logits(b, w, "f32")
+    assert (O.router_logits(a + b, w, "f32") == za + zb).all()
+    assert (O.router_logits(x, 3.0 * w, "f32") == 3.0 * O.router_logits(x, w, "f32")).all()
+
+
+def test_router_bf16_inputs_and_expert_permutation():
+    x, w = _router_case(5)
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)   # small integers: exact
+    wb = (w.view(np.uint32) >> 16).astype(np.uint16)
+    assert (O.router_logits(xb, wb, "bf16") == O.router_logits(x, w, "f32")).all()
+    # permuting the experts' weight rows permutes the scores and the ranking
+    rng = np.random.default_rng(9)
+    xr = rng.standard_normal((16, 40)).astype(np.float32)
+    wr = rng.standard_normal((7, 40)).astype(np.float32)
+    perm = rng.permutation(7)
+    z, ids, g, fb = O.router_topk(xr, wr, "f32", 3, 2)
+    zp, idsp, gp, fbp = O.router_topk(xr, wr[perm], "f32", 3, 2)
+    assert (zp == z[:, perm]).all()
+    assert (perm[idsp] == ids).all() and (perm[fbp] == fb).all()
+    np.testing.assert_allclose(gp, g, rtol=1e-14)  # the sum's order moves
+    # the ranking is the lexsort order of the rounded fp32 scores
+    order = np.lexsort((np.arange(7)[None, :].repeat(16, 0), -z.astype(np.float64)), axis=1)
+    assert (order[:, :3] == ids).all() and (order[:, 3:5] == fb).all()
