@@ -99,6 +99,9 @@ def parse():
     p.add_argument("--entropy", action="store_true",
                    help="time the entropy-weight producer on the multimodal "
                         "prefill batch (T=8192, H=2048, bf16) and exit")
+    p.add_argument("--router", action="store_true",
+                   help="time the router scores fused with top-k on the "
+                        "prefill (T=8192) and decode (T=128) batches and exit")
     p.add_argument("--separate-routing", action="store_true",
                    help="route with the four separate calls instead of the "
                         "single fused launch")
@@ -272,6 +275,66 @@ def run_entropy(args):
                                    "frac": round(gbs / HBM_PEAK_GBS, 4),
                                    "bytes_per_launch": nbytes}}), flush=True)
 
+def run_router(args):
+    """Router scores fused with the route step (MACS §3.1): the multimodal
+    prefill batch (T=8192) and the decode batch (T=128), H=2048, N=128,
+    top-8 with R=8 fallbacks, bf16, scores not written out.  Eight copies
+    of x and W_g rotate between calls so that the stream is not served from
+    the 256 MB Infinity Cache.  HBM-bound: one read of x and W_g plus the
+    routing outputs."""
+    import torch
+    from mixture_experts_layer_macs_amd import binding as B
+    from mixture_experts_layer_macs_amd import configs, synth
+    from mixture_experts_layer_macs_amd.staging import elem_tensor
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    res = {}
+    for name, T in (("prefill_t8192", 8192), ("decode_t128", 128)):
+        wl = configs.MM_PREFILL.with_(T=T)
+        H, N, k, R = wl.H, wl.N, wl.k, wl.R
+        xs = [elem_tensor(synth.activations(wl, args.seed + c), "bf16", dev) for c in range(8)]
+        wsg = [elem_tensor(synth.router_weights(wl, args.seed + c), "bf16", dev) for c in range(8)]
+        ws = B.new_workspace(B.moe_router_workspace_size(T, N, H, torch.bfloat16), dev)
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        g = torch.empty((T, k), dtype=torch.float32, device=dev)
+        fb = torch.empty((T, R), dtype=torch.int32, device=dev)
+
+        def call(i):
+            B.moe_router_topk(xs[i % 8], wsg[i % 8], k, R, ws, topk_ids=ids,
+                              topk_gates=g, fallback_ids=fb, want_logits=False)
+        for i in range(args.warmup):
+            call(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        hold_gpu(0.02)
+        e0.record()
+        for i in range(args.steps):
+            call(i)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / args.steps * 1e3
+        nbytes = T * H * 2 + N * H * 2 + T * k * 8 + T * R * 4
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[name] = dict(T=T, us_per_call=round(us, 2),
+                         tokens_per_s=round(T / (us * 1e-6), 1),
+                         bytes_per_call=nbytes, GBps=round(gbs, 1),
+                         hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
+        print(f"[router] {name}: {res[name]}", file=sys.stderr, flush=True)
+    p = res["prefill_t8192"]
+    print(json.dumps({"metric": "router scores + top-k throughput",
+                      "value": p["tokens_per_s"], "unit": "tokens/s",
+                      "us_per_call": p["us_per_call"], "n_gpus": 1,
+                      "dtype": "bf16", "data": "synthetic (seeded)",
+                      "config": {"workload": "router_t8192_h2048_n128", "T": 8192,
+                                 "H": 2048, "N": 128, "k": 8, "R": 8},
+                      "roofline": {"bound": "hbm", "achieved": p["GBps"],
+                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": p["hbm_frac"],
+                                   "bytes_per_launch": p["bytes_per_call"]},
+                      "decode_t128": res["decode_t128"]}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -283,6 +346,9 @@ def main():
         return
     if args.entropy:
         run_entropy(args)
+        return
+    if args.router:
+        run_router(args)
         return
     import torch
     if args.copy_probe_mib:

@@ -42,10 +42,10 @@
  *     reductions only where order cannot matter.
  *
  * Workspaces
- *   moe_capacity_assign, moe_dispatch, moe_routing_fused and moe_expert_ffn
- *   take a workspace of at least the size their *_workspace_size() query
- *   returns.  The capacity, dispatch and fused-routing workspaces hold a
- *   few control words: they must be filled
+ *   moe_router_topk, moe_capacity_assign, moe_dispatch, moe_routing_fused
+ *   and moe_expert_ffn take a workspace of at least the size their
+ *   *_workspace_size() query returns.  The router, capacity, dispatch and
+ *   fused-routing workspaces hold a few control words: they must be filled
  *   with zero bytes once, before their first use (e.g. allocated zeroed);
  *   every call leaves those words zero again.  A workspace must not be
  *   shared by calls that may run concurrently.
@@ -87,6 +87,37 @@ enum { MOE_FLAG_SERE = 1, MOE_FLAG_MACS = 2, MOE_FLAG_DROP = 4 };
 int moe_route(const float* logits, int T, int N, int k, int R,
               int32_t* topk_ids, float* topk_gates, int32_t* fallback_ids,
               void* stream);
+
+/*
+ * moe_router_topk -- the router network's scores and moe_route over them in
+ * one launch (MACS §3.1: the router G scores every expert and Eq. 1 takes
+ * the top k; the form of G is not given there: a bias-free linear map).
+ *
+ *   logits[t][j] = sum_h w_gate[j][h] * x[t][h]
+ *
+ * x             [T,H]  token features (dtype).
+ * w_gate        [N,H]  router weights (dtype), one row of H per expert.
+ * dtype         MOE_BF16: bf16 MFMA with fp32 accumulation; H must be a
+ *               multiple of 64 and x and w_gate under 2^31 bytes each.
+ *               MOE_F32: fp32 fused multiply-add in increasing h; H must be
+ *               a multiple of 4.  Otherwise, and for N > 256, MOE_EUNSUP.
+ * logits        f32[T,N]  out: the scores; may be NULL.
+ * topk_ids, topk_gates, fallback_ids: as moe_route, and bit for bit what
+ *               moe_route returns when given these scores.
+ * Workspace of moe_router_workspace_size(T, N, H, dtype) bytes: holds one
+ * control word per 32-token tile, which must be zero before the first use
+ * (e.g. allocated zeroed); every call leaves them zero again.  For short
+ * batches the H axis is split over several workgroups whose partial scores
+ * are added in a fixed order; the split depends on the shape only, so the
+ * scores are deterministic for a given shape, and may differ in the last
+ * bits between batch sizes.
+ * One launch on `stream`.
+ */
+size_t moe_router_workspace_size(int T, int N, int H, int dtype);
+int moe_router_topk(const void* x, const void* w_gate, int T, int N, int H,
+                    int k, int R, int dtype, float* logits, int32_t* topk_ids,
+                    float* topk_gates, int32_t* fallback_ids, void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 /*
  * moe_sere_reroute -- SERE similarity-guided re-routing (multi-image QA
@@ -262,8 +293,8 @@ int moe_routing_fused(const float* logits, const uint8_t* is_visual,
  * dtype           MOE_F32 (fp32 FMA) or MOE_BF16 (bf16 MFMA with fp32
  *                 accumulation; h and out_rows are rounded to bf16).
  * The workspace holds h ([T*k, I] of dtype).
- * Shapes: MOE_BF16 needs H % 256 == 0, I % 128 == 0, x under 4 GiB
- * (T*H*2 < 2^32 bytes) and one expert's w13 under 4 GiB (I*H*4 < 2^32
+ * Shapes: MOE_BF16 needs H % 256 == 0, I % 128 == 0, x of at most 2 GiB
+ * (T*H*2 <= 2^31 bytes) and one expert's w13 under 4 GiB (I*H*4 < 2^32
  * bytes); MOE_F32 needs H % 4 == 0 and I % 4 == 0; otherwise MOE_EUNSUP.
  *
  * moe_ffn_gate_up and moe_ffn_down are the two halves of moe_expert_ffn

@@ -38,6 +38,9 @@ _F = ctypes.c_float
 
 _SIGS = {
     "moe_route": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P]),
+    "moe_router_workspace_size": (_SZ, [_I, _I, _I, _I]),
+    "moe_router_topk": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P,
+                             _P, _SZ, _P]),
     "moe_sere_reroute": (_I, [_P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P]),
     "moe_capacity_workspace_size": (_SZ, [_I, _I, _I]),
     "moe_capacity_assign": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
@@ -135,6 +138,34 @@ def moe_route(logits, k, R, topk_ids=None, topk_gates=None, fallback_ids=None):
                         _stream())
     _check(rc, "moe_route")
     return topk_ids, topk_gates, fallback_ids
+
+
+def moe_router_workspace_size(T, N, H, dtype) -> int:
+    return int(_lib.moe_router_workspace_size(T, N, H, _elem(dtype)))
+
+
+def moe_router_topk(x, w_gate, k, R, workspace, logits=None, topk_ids=None,
+                    topk_gates=None, fallback_ids=None, want_logits=True):
+    """Router scores x W_g^T and the route step over them, one launch.
+    Returns (logits or None, topk_ids, topk_gates, fallback_ids)."""
+    T, H = x.shape
+    N = w_gate.shape[0]
+    if logits is None and want_logits:
+        logits = _empty((T, N), torch.float32, x)
+    topk_ids = _empty((T, k), torch.int32, x) if topk_ids is None else topk_ids
+    topk_gates = _empty((T, k), torch.float32, x) if topk_gates is None else topk_gates
+    if fallback_ids is None:
+        fallback_ids = _empty((T, R), torch.int32, x)
+    rc = _lib.moe_router_topk(
+        _dev(x, x.dtype, "x"), _dev(w_gate, x.dtype, "w_gate", (N, H)),
+        T, N, H, k, R, _elem(x.dtype),
+        _opt(logits, torch.float32, "logits", (T, N)),
+        _dev(topk_ids, torch.int32, "topk_ids", (T, k)),
+        _dev(topk_gates, torch.float32, "topk_gates", (T, k)),
+        _dev(fallback_ids, torch.int32, "fallback_ids", (T, R)) if R > 0 else None,
+        _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
+    _check(rc, "moe_router_topk")
+    return logits, topk_ids, topk_gates, fallback_ids
 
 
 def moe_sere_reroute(topk_ids, N, kprime, rho, sim, prot, slot_expert=None,

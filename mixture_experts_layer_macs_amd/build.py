@@ -19,7 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_macs.so")
 SOURCES = ["route.hip", "sere.hip", "capacity.hip", "dispatch.hip",
-           "routing_fused.hip", "ffn.hip", "combine.hip", "entropy.hip"]
+           "routing_fused.hip", "ffn.hip", "combine.hip", "entropy.hip",
+           "router.hip"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 

@@ -23,6 +23,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "dma.h"
 
 namespace moe {
 namespace ffn {
@@ -118,49 +119,8 @@ __device__ bool find_tile(const Args& a, int* cum, int& j, int& m0, int& nt,
 // The swizzle is applied on the global side: the lane that fills LDS slot
 // (row, s) fetches chunk s ^ ((row >> SWS) & SWZ) of that row.
 
-// The loads are buffer loads: a 128-bit resource (base address, byte size)
-// in scalar registers, a per-lane 32-bit byte offset fixed for the whole K
-// loop, and the K position in a scalar offset, so one request costs a
-// scalar add for M0 (the LDS destination of the wave's 1 KB) and the load
-// itself.  Issued as inline assembly so the compiler's automatic wait
-// insertion does not treat later LDS reads as dependent on it: completion is
-// tracked explicitly (wait_vmcnt + barrier) by the pipeline below.
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-
-// A byte offset past every gate-up resource (x is under 2^31 bytes).
-constexpr uint32_t OOB_OFF = 0x80000000u;
-
-// Raw buffer resource: no stride, no swizzle, byte range [0, bytes); word 3
-// is the gfx9 raw-buffer format word (32-bit data format, no type
-// conversion).  Addresses outside the range read as zero.
-__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  i32x4 r;
-  r.x = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(b & 0xffffffffu));
-  r.y = __builtin_amdgcn_readfirstlane(static_cast<int32_t>((b >> 32) & 0xffffu));
-  r.z = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(bytes));
-  r.w = 0x00020000;
-  return r;
-}
-
-__device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t voff, uint32_t soff,
-                                          uint32_t m0) {
-  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc),
-               "s"(soff), "{m0}"(m0)
-               : "memory");
-}
-
-// s_waitcnt with only the vector-memory counter limited (gfx9 encoding:
-// vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
-
-// Barrier without the memory fence of __syncthreads: LDS here is written
-// only by the DMA loads, whose completion each wave has already waited for.
-__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// The DMA helpers (buffer resource, direct-to-LDS load, counted waits) are
+// in dma.h.
 
 // Scheduling groups of one sub-slice: its NMF MFMAs split as evenly as
 // possible over its NFR fragment reads, one read after each group.

@@ -18,7 +18,7 @@ __global__ __launch_bounds__(256) void route_kernel(
   constexpr int TPB = 256 / GT;
   const int grp = threadIdx.x / GT;
   const int t = blockIdx.x * TPB + grp;
-  rt::route_token<GT>(logits, N, k, R, t, t < T,
+  rt::route_token<GT>(logits + static_cast<size_t>(t) * N, N, k, R, t, t < T,
                       smem + grp * rt::token_lds_bytes(N, GT), topk_ids,
                       topk_gates, fallback_ids);
 }

@@ -42,11 +42,12 @@ __device__ __forceinline__ float group_reduce(float v, float* red) {
   return v;
 }
 
-// Route token t (live == false: a padding group that only joins the
-// workgroup barriers).  Writes topk_ids[t][0..k), topk_gates[t][0..k) and
+// Route token t, whose N logits start at `row` (global memory or LDS;
+// live == false: a padding group that only joins the workgroup barriers and
+// reads nothing).  Writes topk_ids[t][0..k), topk_gates[t][0..k) and
 // fallback_ids[t][0..R) in rank order.
 template <int GT>
-__device__ void route_token(const float* __restrict__ logits, int N, int k,
+__device__ void route_token(const float* __restrict__ row, int N, int k,
                             int R, int t, bool live, unsigned char* lds,
                             int32_t* __restrict__ topk_ids,
                             float* __restrict__ topk_gates,
@@ -55,7 +56,6 @@ __device__ void route_token(const float* __restrict__ logits, int N, int k,
   int* rank = reinterpret_cast<int*>(lds + static_cast<size_t>(N) * 8);
   float* red = reinterpret_cast<float*>(lds + static_cast<size_t>(N) * 12);
   const int g = threadIdx.x % GT;
-  const float* row = logits + static_cast<size_t>(t) * N;
 
   float mx = -INFINITY;
   if (live)
@@ -121,6 +121,98 @@ __device__ void route_token(const float* __restrict__ logits, int N, int k,
         fallback_ids[static_cast<size_t>(t) * R + (r - k)] = e;
       }
     }
+}
+
+// One wave ranks one token whose N <= 64 * KPL logits start at `row`
+// (global memory or LDS), with every key in registers: lane l holds experts
+// l, l + 64, ...  The outputs are route_token's, bit for bit (the same max,
+// the same softmax denominator order, the same gate expression).
+//
+//   1. the (k + R)-th largest order key theta is found by a most-significant-
+//      bit-first search: bit b is kept iff at least k + R keys are >= the
+//      candidate (one ballot per register); the search stops as soon as
+//      exactly k + R keys qualify;
+//   2. the selected set is every key above theta plus the lowest-index keys
+//      equal to theta (ranks of equal logits go to the lower index);
+//   3. the selected keys are compacted into `cand` (LDS, k + R entries of
+//      this wave's own) and each one's rank is the number of selected keys
+//      that beat it.
+// A dead token (live == false) returns at once: the wave takes no part in
+// any workgroup barrier.
+template <int KPL>
+__device__ void route_token_wave(const float* __restrict__ row, int N, int k,
+                                 int R, int t, bool live, uint64_t* cand,
+                                 int32_t* __restrict__ topk_ids,
+                                 float* __restrict__ topk_gates,
+                                 int32_t* __restrict__ fallback_ids) {
+  if (!live) return;
+  const int lane = lane_id();
+  const int M = k + R;
+  float v[KPL];
+  uint32_t u[KPL];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const int j = lane + MOE_WAVE * i;
+    v[i] = j < N ? row[j] : 0.f;
+    u[i] = j < N ? f32_order_key(v[i]) : 0u;  // 0: below every finite key
+    if (j < N) mx = fmaxf(mx, v[i]);
+  }
+  mx = wave_max(mx);
+  // softmax denominator: lane l adds its experts in increasing index, then
+  // the wave tree -- route_token's order
+  float se = 0.f;
+#pragma unroll
+  for (int i = 0; i < KPL; ++i)
+    if (lane + MOE_WAVE * i < N) se += expf(f32_from_order_key(u[i]) - mx);
+  se = wave_sum(se);
+
+  uint32_t theta = 0u;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand_t = theta | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) cnt += __popcll(__ballot(u[i] >= cand_t));
+    if (cnt >= M) {
+      theta = cand_t;
+      if (cnt == M) break;
+    }
+  }
+  int above = 0;
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) above += __popcll(__ballot(u[i] > theta));
+  const int need = M - above;  // keys equal to theta to take, lowest index first
+  const uint64_t lt = lanemask_lt();
+  int ties = 0, base = 0;
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const uint64_t eq = __ballot(u[i] == theta);
+    const bool sel = u[i] > theta || (u[i] == theta && ties + __popcll(eq & lt) < need);
+    ties += __popcll(eq);
+    const uint64_t sb = __ballot(sel);
+    if (sel)
+      cand[base + __popcll(sb & lt)] =
+          (static_cast<uint64_t>(u[i]) << 32) |
+          static_cast<uint32_t>(0xffffffffu - static_cast<uint32_t>(lane + MOE_WAVE * i));
+    base += __popcll(sb);
+  }
+  // the wave's own LDS writes are visible to its later reads
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  for (int c = lane; c < M; c += MOE_WAVE) {
+    const uint64_t kc = cand[c];
+    int r = 0;
+    for (int c2 = 0; c2 < M; ++c2) r += cand[c2] > kc ? 1 : 0;
+    const int e = rank_key_index(kc);
+    if (r < k) {
+      topk_ids[static_cast<size_t>(t) * k + r] = e;
+      topk_gates[static_cast<size_t>(t) * k + r] = expf(rank_key_value(kc) - mx) / se;
+    } else {
+      fallback_ids[static_cast<size_t>(t) * R + (r - k)] = e;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
 }
 
 }  // namespace rt

@@ -231,7 +231,7 @@ __global__ __launch_bounds__(FT) void routing_kernel(Args f, cap::Args ca,
   constexpr int TPB = FT / GT;
   const int grp = threadIdx.x / GT;
   const int t = blockIdx.x * TPB + grp;
-  rt::route_token<GT>(f.logits, f.N, f.k, f.R, t, t < f.T,
+  rt::route_token<GT>(f.logits + static_cast<size_t>(t) * f.N, f.N, f.k, f.R, t, t < f.T,
                       smem + grp * rt::token_lds_bytes(f.N, GT), f.topk_ids,
                       f.topk_gates, f.fallback_ids);
 

@@ -126,3 +126,34 @@ def test_host_side_errors_fused_and_entropy(lib):
                                    fake, 8, None) == -1           # workspace
     assert lib.moe_entropy_weights(None, None, 0, 64, 1, 1.0, 1e-6, None, None,
                                    None, 0, None) == 0            # T = 0
+
+
+def test_router_host_checks_and_workspace(lib):
+    """moe_router_topk: shape limits and the workspace query (the split of
+    the H axis for short batches needs room for the partial scores)."""
+    P, I_, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    f = lib.moe_router_workspace_size
+    f.restype = SZ
+    f.argtypes = [I_] * 4
+    # one control word per 32-token tile; short batches add partial scores
+    assert f(8192, 128, 2048, 1) == 256 * 4
+    assert f(128, 128, 2048, 1) >= 4 * 8 * 32 * 128 * 4
+    assert f(128, 128, 2048, 0) == 256            # fp32: no split
+    assert f(128, 128, 2000, 1) == 0              # bf16 needs H % 64 == 0
+    assert f(-1, 128, 2048, 1) == 0
+    fake = P(0x1000)
+    lib.moe_router_topk.argtypes = [P, P] + [I_] * 6 + [P] * 5 + [SZ, P]
+    def call(T=4, N=128, H=2048, k=8, R=8, dt=1, logits=None, fb=fake, ws=fake,
+             nbytes=1 << 20, x=fake):
+        return lib.moe_router_topk(x, fake, T, N, H, k, R, dt, logits, fake,
+                                   fake, fb, ws, nbytes, None)
+    assert call(N=0) == -1 and call(k=129) == -1 and call(R=121) == -1
+    assert call(N=300) == -2                      # fused top-k covers N <= 256
+    assert call(H=100) == -2                      # bf16: H % 64
+    assert call(H=102, dt=0) == -2                # fp32: H % 4
+    assert call(dt=5) == -2
+    assert call(fb=None) == -1                    # R > 0 needs fallback_ids
+    assert call(ws=None) == -1
+    assert call(nbytes=16) == -1                  # workspace too small
+    assert call(x=None) == -1
+    assert call(T=0, x=None, ws=None) == 0        # T = 0: nothing to do
