@@ -3,7 +3,8 @@
 // §3.3 Eq. 7, §1 and Fig. 1).  The phases live in capacity_impl.h; this
 // file holds the kernels and the entry point.  When the whole batch fits
 // one workgroup (decode) all rounds run in one launch; otherwise each round
-// is one launch over the token blocks.
+// is one launch over the token blocks (up to 128 blocks with no serial
+// step between launches, cap_rounds_dec).
 #include "capacity_impl.h"
 
 namespace moe {
@@ -13,6 +14,11 @@ __global__ __launch_bounds__(1024) void cap_kernel(Args a, int r_first,
                                                    int r_last) {
   extern __shared__ __align__(16) unsigned char smem[];
   cap_rounds(a, blockIdx.x, r_first, r_last, smem);
+}
+
+__global__ __launch_bounds__(256) void cap_dec_kernel(Args a, int r) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  cap_rounds_dec(a, blockIdx.x, r, smem);
 }
 
 __global__ __launch_bounds__(1024) void cap_off_kernel(Args a) {
@@ -59,6 +65,17 @@ extern "C" int moe_capacity_assign(
   const dim3 grid(L.G), block(L.threads);
   if (std::isinf(gamma)) {
     hipLaunchKernelGGL(cap_off_kernel, grid, block, off_lds_bytes(a), s, a);
+    return launch_status();
+  }
+  if (a.dec) {
+    const size_t lds = dec_lds_bytes(a);
+    if (lds > 65536 &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(cap_dec_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(lds)) != hipSuccess)
+      return MOE_EHIP;
+    for (int r = 0; r <= R + 1; ++r)
+      hipLaunchKernelGGL(cap_dec_kernel, grid, block, lds, s, a, r);
     return launch_status();
   }
   const size_t lds = rounds_lds_bytes(a);

@@ -80,9 +80,12 @@ struct Args {
   unsigned* phase;                  // [1]
   unsigned long long* pending;      // [1] (two's complement sum)
   uint32_t* act_bits;               // [32]  experts with a round-0 proposer
-  unsigned long long* adm;          // [N]   max admitted running weight
+  unsigned long long* adm;          // [3][N] max admitted running weight
   unsigned long long* total;        // [N]   proposal weight (capacity off)
-  int TB, G, lds_scan;
+  // decentralised multi-launch call (dec != 0): the launch that finalised
+  // the slots early (0 = none yet)
+  unsigned* fin;                    // [1]
+  int TB, G, lds_scan, dec;
 };
 
 __device__ __forceinline__ int32_t quant_weight(uint8_t vis, float w) {
@@ -107,7 +110,7 @@ __device__ int64_t capacity_of(const Args& a, double rv, int e) {
 // ---------------------------------------------------------------- phases
 // Round-0 proposals: every slot, in (token, slot) order.
 __device__ void propose0(const Args& a, int g, int t0, int t1, int32_t* run,
-                         uint32_t* act_bits, int64_t* red) {
+                         uint32_t* act_bits, int64_t* red, int32_t* part_row) {
   const int tid = threadIdx.x, nthr = blockDim.x, k = a.k;
   int64_t w_all = 0, w_vis = 0;
   for (int t = t0 + tid; t < t1; t += nthr) {
@@ -134,14 +137,16 @@ __device__ void propose0(const Args& a, int g, int t0, int t1, int32_t* run,
                key = cur[idx];
                w = wq[t0 + idx / k];
              },
-             a.incl_slot + static_cast<size_t>(t0) * k,
-             a.part + static_cast<size_t>(g) * a.N, act_bits);
+             a.incl_slot + static_cast<size_t>(t0) * k, part_row, act_bits);
   if (tid < 32 && act_bits[tid]) atomicOr(&a.act_bits[tid], act_bits[tid]);
 }
 
 // Offers of fallback round r >= 1: one per token with an unplaced overflow.
+// An expert is a candidate iff it had a round-0 proposer: active[c], or,
+// when active is null, bit c of the global act_bits.
 __device__ void propose_round(const Args& a, int r, int g, int t0, int t1,
-                              int32_t* run) {
+                              int32_t* run, const uint8_t* active,
+                              int32_t* part_row) {
   const int tid = threadIdx.x, nthr = blockDim.x, k = a.k;
   for (int t = t0 + tid; t < t1; t += nthr) {
     const int32_t* cs = a.cur + static_cast<size_t>(t) * k;
@@ -155,7 +160,8 @@ __device__ void propose_round(const Args& a, int r, int g, int t0, int t1,
     if (s_off >= 0) {
       c = a.fallback[static_cast<size_t>(t) * a.R + (r - 1)];
       const int e = cs[s_off];
-      bool ok = a.active[c] && (c / a.group) == (e / a.group);
+      const bool act = active ? active[c] != 0 : ((a.act_bits[c >> 5] >> (c & 31)) & 1u) != 0;
+      bool ok = act && (c / a.group) == (e / a.group);
       bool held = false;
       for (int s = 0; s < k; ++s) held |= cs[s] == c;
       if (!ok || held) s_off = -1;
@@ -171,26 +177,29 @@ __device__ void propose_round(const Args& a, int r, int g, int t0, int t1,
                key = oc[idx];
                w = wq[idx];
              },
-             a.incl_tok + t0, a.part + static_cast<size_t>(g) * a.N,
-             nullptr);
+             a.incl_tok + t0, part_row, nullptr);
 }
 
-// Admit or refuse the proposals of round r (decided against base and drem
-// from the global step of round r).
+// Admit or refuse the proposals of round r against base (this block's
+// exclusive prefix of round r's proposal weight over the earlier blocks) and
+// drem (capacity left before round r).  amax (LDS) ends with this block's
+// largest admitted running weight per expert, also folded into adm[] with
+// atomicMax unless adm is null.
 // pending (may be null): LDS count of overflowed slots not yet placed;
 // round 0 adds its overflows, later rounds subtract their admissions.
-__device__ void apply(const Args& a, int r, int g, int t0, int t1,
-                      unsigned long long* amax, int* pending) {
+__device__ void apply(const Args& a, int r, int t0, int t1,
+                      unsigned long long* amax, int* pending,
+                      const int64_t* base, const int64_t* drem,
+                      unsigned long long* adm) {
   const int tid = threadIdx.x, nthr = blockDim.x, k = a.k, N = a.N;
   for (int e = tid; e < N; e += nthr) amax[e] = 0ull;
   __syncthreads();
-  const int64_t* base = a.base + static_cast<size_t>(g) * N;
   int moved = 0;
   if (r == 0) {
     for (int i = t0 * k + tid; i < t1 * k; i += nthr) {
       const int e = a.cur[i];
       const int64_t v = base[e] + a.incl_slot[i];
-      if (v <= a.drem[e]) {
+      if (v <= drem[e]) {
         atomicMax(&amax[e], static_cast<unsigned long long>(v));
       } else {
         a.st[i] = (a.st[i] & ST_SERE) | ST_OVER;
@@ -203,7 +212,7 @@ __device__ void apply(const Args& a, int r, int g, int t0, int t1,
       if (s < 0) continue;
       const int c = a.offer_c[t];
       const int64_t v = base[c] + a.incl_tok[t];
-      if (v <= a.drem[c]) {
+      if (v <= drem[c]) {
         const size_t i = static_cast<size_t>(t) * k + s;
         a.st[i] = (a.st[i] & ST_SERE) | ST_PLACED;
         a.cur[i] = c;
@@ -217,12 +226,15 @@ __device__ void apply(const Args& a, int r, int g, int t0, int t1,
     if (lane_id() == 0 && w != 0) atomicAdd(pending, w);
   }
   __syncthreads();
-  for (int e = tid; e < N; e += nthr)
-    if (amax[e]) atomicMax(&a.adm[e], amax[e]);
+  if (adm)
+    for (int e = tid; e < N; e += nthr)
+      if (amax[e]) atomicMax(&adm[e], amax[e]);
 }
 
+// Final slot values and flags of the block; the drop / re-route counts go to
+// wsum (or, with add_stats, straight into stats[2..3] by integer atomics).
 __device__ void finalize_slots(const Args& a, int g, int t0, int t1,
-                               int64_t* red) {
+                               int64_t* red, bool add_stats = false) {
   const int tid = threadIdx.x, nthr = blockDim.x, k = a.k;
   int64_t n_drop = 0, n_macs = 0;
   for (int i = t0 * k + tid; i < t1 * k; i += nthr) {
@@ -242,8 +254,15 @@ __device__ void finalize_slots(const Args& a, int g, int t0, int t1,
   }
   block_sum2_i64(n_drop, n_macs, red);
   if (tid == 0) {
-    a.wsum[g * 4 + 2] = n_drop;
-    a.wsum[g * 4 + 3] = n_macs;
+    if (add_stats) {
+      if (n_drop) atomicAdd(reinterpret_cast<unsigned long long*>(a.stats + 2),
+                            static_cast<unsigned long long>(n_drop));
+      if (n_macs) atomicAdd(reinterpret_cast<unsigned long long*>(a.stats + 3),
+                            static_cast<unsigned long long>(n_macs));
+    } else {
+      a.wsum[g * 4 + 2] = n_drop;
+      a.wsum[g * 4 + 3] = n_macs;
+    }
   }
 }
 
@@ -276,6 +295,7 @@ __device__ void global_step(const Args& a, int r, int64_t* red, int32_t* lds) {
       a.cap_q[e] = c;
       a.drem[e] = c;
       a.active[e] = (a.act_bits[e >> 5] >> (e & 31)) & 1u;
+      a.adm[e] = 0ull;  // a decentralised call may leave one round's maxima
     }
     __syncthreads();
     if (tid < 32) a.act_bits[tid] = 0u;
@@ -364,7 +384,8 @@ __device__ void cap_rounds(const Args& a, int g, int r_first, int r_last,
   }
   for (int r = r_first; r <= r_last; ++r) {
     if (r >= 1) {
-      apply(a, r - 1, g, t0, t1, amax, (track || multi) ? &s_pending : nullptr);
+      apply(a, r - 1, t0, t1, amax, (track || multi) ? &s_pending : nullptr,
+            a.base + static_cast<size_t>(g) * a.N, a.drem, a.adm);
       __syncthreads();
       if (multi && threadIdx.x == 0 && s_pending != 0)
         atomicAdd(a.pending, static_cast<unsigned long long>(static_cast<long long>(s_pending)));
@@ -377,9 +398,9 @@ __device__ void cap_rounds(const Args& a, int g, int r_first, int r_last,
       }
     }
     if (r == 0)
-      propose0(a, g, t0, t1, run, act_bits, red);
+      propose0(a, g, t0, t1, run, act_bits, red, a.part + static_cast<size_t>(g) * a.N);
     else if (r <= a.R)
-      propose_round(a, r, g, t0, t1, run);
+      propose_round(a, r, g, t0, t1, run, a.active, a.part + static_cast<size_t>(g) * a.N);
     else
       finalize_slots(a, g, t0, t1, red);
     if (a.G > 1) {
@@ -390,6 +411,159 @@ __device__ void cap_rounds(const Args& a, int g, int r_first, int r_last,
     global_step(a, r, red, run);
     __syncthreads();
   }
+}
+
+// Multi-launch call with no serial global step (dec: 2 <= G <= DEC_MAX_G).
+// Launch r runs round r in every block; what the last block's global step
+// publishes in the other form, each block derives itself from the earlier
+// launches' results:
+//   - D, the capacity left before round r-1's admissions (LDS): D = C (from
+//     R_v, each block summing the block weight totals) for r = 1, else the
+//     previous launch's D (stored by block 0) minus round r-2's admitted
+//     weight (the atomicMax of every block's largest admitted running
+//     weight);
+//   - its exclusive prefix over the earlier blocks of round r-1's proposal
+//     weight, summed from their per-block totals.
+// Buffers rotate by round so that no block overwrites what another block of
+// the same launch may still read: part by 2, D by 2, adm by 3.  Block 0 of
+// launch 0 clears adm, load_q, the drop and re-route counts and the early
+// finish marker; the launch that finalises clears act_bits.  Once no
+// overflowed slot is left unplaced (pending == 0 at a launch's start, r >= 2)
+// that launch finalises and records itself in fin; later launches return.
+constexpr int DEC_MAX_G = 128;
+
+__device__ void cap_rounds_dec(const Args& a, int g, int r, unsigned char* smem) {
+  const int tid = threadIdx.x, nthr = blockDim.x, N = a.N, G = a.G;
+  // [amax: N u64][D: N i64][prefix: N i64][run / key-prefix staging]
+  unsigned long long* amax = reinterpret_cast<unsigned long long*>(smem);
+  int64_t* dv = reinterpret_cast<int64_t*>(smem + 8 * static_cast<size_t>(N));
+  int64_t* bv = reinterpret_cast<int64_t*>(smem + 16 * static_cast<size_t>(N));
+  int32_t* run = reinterpret_cast<int32_t*>(smem + 24 * static_cast<size_t>(N));
+  __shared__ uint32_t act_bits[32];
+  __shared__ int64_t red[32];
+  __shared__ int s_pending;
+  __shared__ unsigned s_fin;
+  __shared__ unsigned long long s_pend;
+  __shared__ double s_rv;
+  const int t0 = g * a.TB, t1 = min(a.T, t0 + a.TB);
+  const size_t GN = static_cast<size_t>(G) * N;
+  if (r == 0) {
+    if (g == 0) {
+      for (int i = tid; i < 3 * N; i += nthr) a.adm[i] = 0ull;
+      for (int e = tid; e < N; e += nthr) a.load_q[e] = 0;
+      if (tid == 0) {
+        a.stats[2] = 0;
+        a.stats[3] = 0;
+        *a.fin = 0u;
+        *a.pending = 0ull;
+      }
+    }
+    propose0(a, g, t0, t1, run, act_bits, red, a.part + static_cast<size_t>(g) * N);
+    return;
+  }
+  if (tid == 0) {
+    s_fin = *a.fin;
+    s_pend = *a.pending;
+    s_pending = 0;
+  }
+  __syncthreads();
+  if (s_fin != 0u && s_fin < static_cast<unsigned>(r)) return;
+  const bool last = r == a.R + 1;
+  const bool finish = !last && r >= 2 && s_pend == 0ull;
+
+  if (r == 1) {
+    int64_t w_all = 0, w_vis = 0;
+    for (int b = tid; b < G; b += nthr) {
+      w_all += a.wsum[b * 4 + 0];
+      w_vis += a.wsum[b * 4 + 1];
+    }
+    block_sum2_i64(w_all, w_vis, red);
+    if (tid == 0) {
+      const double rv = w_all > 0 ? static_cast<double>(w_vis) /
+                                        static_cast<double>(w_all)
+                                  : 0.5;
+      s_rv = rv;
+      if (g == 0) {
+        a.r_v[0] = rv;
+        a.stats[0] = w_all;
+        a.stats[1] = w_vis;
+      }
+    }
+    __syncthreads();
+    const double rv = s_rv;
+    for (int e = tid; e < N; e += nthr) {
+      const int64_t c = capacity_of(a, rv, e);
+      dv[e] = c;
+      if (g == 0) {
+        a.capv[e] = c;
+        a.cap_q[e] = c;
+        a.drem[e] = c;
+      }
+    }
+  } else {
+    const int64_t* dprev = a.drem + static_cast<size_t>((r - 2) & 1) * N;
+    const unsigned long long* aprev = a.adm + static_cast<size_t>((r - 2) % 3) * N;
+    for (int e = tid; e < N; e += nthr) {
+      const int64_t d = dprev[e] - static_cast<int64_t>(aprev[e]);
+      dv[e] = d;
+      if (g == 0) {
+        a.drem[static_cast<size_t>((r - 1) & 1) * N + e] = d;
+        a.adm[static_cast<size_t>(r % 3) * N + e] = 0ull;
+      }
+    }
+  }
+  if (finish) {
+    __syncthreads();
+    finalize_slots(a, g, t0, t1, red, true);
+    if (g == 0) {
+      for (int e = tid; e < N; e += nthr) a.load_q[e] = a.capv[e] - dv[e];
+      if (tid < 32) a.act_bits[tid] = 0u;
+      if (tid == 0) *a.fin = static_cast<unsigned>(r);
+    }
+    return;
+  }
+  // this block's prefix over the earlier blocks of round r-1's proposals
+  for (int e = tid; e < N; e += nthr) bv[e] = 0;
+  __syncthreads();
+  {
+    const int32_t* pp = a.part + static_cast<size_t>((r - 1) & 1) * GN;
+    const int n = g * N;
+    for (int i0 = tid; i0 < n; i0 += nthr * 8) {
+      int32_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * nthr;
+        v[u] = i < n ? pp[i] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * nthr;
+        if (i < n && v[u])
+          atomicAdd(reinterpret_cast<unsigned long long*>(&bv[i % N]),
+                    static_cast<unsigned long long>(v[u]));
+      }
+    }
+  }
+  __syncthreads();
+  apply(a, r - 1, t0, t1, amax, &s_pending, bv, dv,
+        last ? nullptr : a.adm + static_cast<size_t>((r - 1) % 3) * N);
+  __syncthreads();
+  if (!last) {
+    if (tid == 0 && s_pending != 0)
+      atomicAdd(a.pending, static_cast<unsigned long long>(static_cast<long long>(s_pending)));
+    propose_round(a, r, g, t0, t1, run, nullptr,
+                  a.part + static_cast<size_t>(r & 1) * GN + static_cast<size_t>(g) * N);
+    return;
+  }
+  finalize_slots(a, g, t0, t1, red, true);
+  // load = C - D + the round's admitted weight: the max over the blocks
+  for (int e = tid; e < N; e += nthr) {
+    const int64_t c = r == 1 ? dv[e] : a.capv[e];
+    const int64_t v = c - dv[e] + static_cast<int64_t>(amax[e]);
+    atomicMax(reinterpret_cast<unsigned long long*>(a.load_q + e),
+              static_cast<unsigned long long>(v));
+  }
+  if (g == 0 && tid < 32) a.act_bits[tid] = 0u;
 }
 
 // Capacity off: everything kept; loads are the plain weight totals.
@@ -458,18 +632,18 @@ __device__ void cap_off(const Args& a, int g, unsigned char* smem) {
 // ------------------------------------------------------------------ host
 // Workspace: a fixed control block (zero between calls, independent of T so
 // one workspace serves any batch size), then the per-call arrays.  The
-// ticket's 256-byte block also holds the phase (byte 64) and pending count
-// (byte 128) of a multi-launch call; the first launch sets both, so they
-// need not be zero between calls.
+// ticket's 256-byte block also holds the phase (byte 64), pending count
+// (byte 128) and early-finish launch (byte 192) of a multi-launch call; the
+// first launch sets them, so they need not be zero between calls.
 constexpr size_t CTRL_TICKET = 0;
 constexpr size_t CTRL_ACT = 256;
 constexpr size_t CTRL_ADM = 512;
-constexpr size_t CTRL_TOTAL = CTRL_ADM + 8 * 1024;
+constexpr size_t CTRL_TOTAL = CTRL_ADM + 3 * 8 * 1024;
 constexpr size_t CTRL_BYTES = CTRL_TOTAL + 8 * 1024;
 constexpr int SCAN_LDS = 8192;  // int32 staging for the block-prefix scan
 
 struct Layout {
-  int G, TB, threads;
+  int G, TB, threads, dec;
   size_t wq, cur, st, incl_slot, incl_tok, offer_s, offer_c, part, base, wsum,
       capv, drem, active, bytes;
 };
@@ -488,6 +662,7 @@ inline Layout layout(int T, int N, int k) {
     L.G = (T + L.TB - 1) / L.TB;
     L.threads = 256;
   }
+  L.dec = L.G > 1 && L.G <= DEC_MAX_G;
   size_t o = CTRL_BYTES;
   auto take = [&](size_t n) {
     const size_t at = o;
@@ -502,11 +677,11 @@ inline Layout layout(int T, int N, int k) {
   L.incl_tok = take(sizeof(int32_t) * T);
   L.offer_s = take(sizeof(int32_t) * T);
   L.offer_c = take(sizeof(int32_t) * T);
-  L.part = take(sizeof(int32_t) * GN);
+  L.part = take(sizeof(int32_t) * GN * (L.G > 1 ? 2 : 1));
   L.base = take(sizeof(int64_t) * GN);
   L.wsum = take(sizeof(int64_t) * 4 * L.G);
   L.capv = take(sizeof(int64_t) * N);
-  L.drem = take(sizeof(int64_t) * N);
+  L.drem = take(sizeof(int64_t) * N * 2);
   L.active = take(N);
   L.bytes = o;
   return L;
@@ -559,11 +734,13 @@ inline Args make_args(const int32_t* topk_ids, const int32_t* slot_in,
   a.ticket = reinterpret_cast<unsigned*>(ws + CTRL_TICKET);
   a.phase = reinterpret_cast<unsigned*>(ws + CTRL_TICKET + 64);
   a.pending = reinterpret_cast<unsigned long long*>(ws + CTRL_TICKET + 128);
+  a.fin = reinterpret_cast<unsigned*>(ws + CTRL_TICKET + 192);
   a.act_bits = reinterpret_cast<uint32_t*>(ws + CTRL_ACT);
   a.adm = reinterpret_cast<unsigned long long*>(ws + CTRL_ADM);
   a.total = reinterpret_cast<unsigned long long*>(ws + CTRL_TOTAL);
   a.TB = L.TB;
   a.G = L.G;
+  a.dec = L.dec;
   a.lds_scan = std::max((L.threads / MOE_WAVE) * N, SCAN_LDS);
   return a;
 }
@@ -574,6 +751,9 @@ inline size_t rounds_lds_bytes(const Args& a) {
   return sizeof(unsigned long long) * a.N + sizeof(int32_t) * a.lds_scan;
 }
 inline size_t off_lds_bytes(const Args& a) { return sizeof(unsigned long long) * a.N; }
+inline size_t dec_lds_bytes(const Args& a) {
+  return 24 * static_cast<size_t>(a.N) + sizeof(int32_t) * a.lds_scan;
+}
 
 }  // namespace cap
 }  // namespace moe
