@@ -42,12 +42,13 @@ METRIC = ("MoE-layer tokens/s (prefill) + decode-step µs at B=128; "
 # reads 256 MiB -> x1.0).  A reading holds only for the kernel sources it was
 # taken on (sha256 over GEMM_SOURCES); otherwise traffic is reported as null.
 GEMM_SOURCES = ("mixture_experts_layer_macs_amd/csrc/ffn.hip",
-                "mixture_experts_layer_macs_amd/csrc/common.h")
+                "mixture_experts_layer_macs_amd/csrc/common.h",
+                "mixture_experts_layer_macs_amd/csrc/dma.h")
 HBM_COUNTERS = {
     "qwen3_decode_b128": dict(
-        kernel="gate_up_swiglu", fetch_kib=130542.9, write_kib=1536.0,
+        kernel="gate_up_swiglu", fetch_kib=130579.7, write_kib=1536.0,
         fetch_scale=2.0, write_scale=1.0,
-        sources_sha256="b681bd82ee652bd24aebd801321f582c1fea99c84b669be0e785f2c6c84fc37d"),
+        sources_sha256="92a56e7fff2b6ef319738c83715a52a7ceb8b42553c33faf98a10367c72422b6"),
 }
 
 

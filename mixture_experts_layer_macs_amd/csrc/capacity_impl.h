@@ -332,6 +332,41 @@ __device__ void global_step(const Args& a, int r, int64_t* red, int32_t* lds) {
   }
 }
 
+// Whether an unplaced overflowed slot of the block could still be placed in
+// rounds r..R (call after round r-1's admissions, before round r's offers).
+// Every condition of an offer only tightens from round to round: A and the
+// groups are fixed, a token's held experts only grow, the capacity left
+// only shrinks.  So if no token has a candidate c that passes them all now
+// -- c in A, in the group of one of its overflowed slots, not held, and at
+// least the token's weight of capacity left -- no later round admits
+// anything, and the slots can be finalised at once.
+__device__ bool any_placeable(const Args& a, int r, int t0, int t1) {
+  __shared__ int s_any;
+  const int tid = threadIdx.x, nthr = blockDim.x, k = a.k;
+  if (tid == 0) s_any = 0;
+  __syncthreads();
+  for (int t = t0 + tid; t < t1; t += nthr) {
+    const int32_t* cs = a.cur + static_cast<size_t>(t) * k;
+    const uint8_t* ss = a.st + static_cast<size_t>(t) * k;
+    const int32_t q = a.wq[t];
+    bool found = false;
+    for (int s = 0; s < k && !found; ++s) {
+      if ((ss[s] & ST_MASK) != ST_OVER) continue;
+      const int ge = cs[s] / a.group;
+      for (int rr = r; rr <= a.R && !found; ++rr) {
+        const int c = a.fallback[static_cast<size_t>(t) * a.R + (rr - 1)];
+        if (!a.active[c] || c / a.group != ge) continue;
+        bool held = false;
+        for (int s2 = 0; s2 < k; ++s2) held |= cs[s2] == c;
+        found = !held && a.drem[c] - static_cast<int64_t>(a.adm[c]) >= q;
+      }
+    }
+    if (found) s_any = 1;
+  }
+  __syncthreads();
+  return s_any != 0;
+}
+
 // True in every thread of the workgroup that finished last (G > 1).  An
 // agent-scope fence writes back or invalidates the XCD's L2 on gfx950, so
 // one thread fences for the whole workgroup after every wave has waited for
@@ -362,7 +397,8 @@ __device__ void cap_rounds(const Args& a, int g, int r_first, int r_last,
   __shared__ int s_pending;
   const int t0 = g * a.TB, t1 = min(a.T, t0 + a.TB);
   // One workgroup running every round can stop re-routing as soon as no
-  // overflowed slot is left unplaced: the overflow set only shrinks, so the
+  // overflowed slot is left unplaced (the overflow set only shrinks), or as
+  // soon as none of them has a candidate left that could be admitted: the
   // remaining rounds could admit nothing.
   const bool track = a.G == 1 && r_first == 0 && r_last == a.R + 1;
   const bool multi = a.G > 1;
@@ -389,7 +425,7 @@ __device__ void cap_rounds(const Args& a, int g, int r_first, int r_last,
       __syncthreads();
       if (multi && threadIdx.x == 0 && s_pending != 0)
         atomicAdd(a.pending, static_cast<unsigned long long>(static_cast<long long>(s_pending)));
-      if (track && r <= a.R && s_pending == 0) {
+      if (track && r <= a.R && (s_pending == 0 || !any_placeable(a, r, t0, t1))) {
         finalize_slots(a, g, t0, t1, red);
         __syncthreads();
         global_step(a, a.R + 1, red, run);
@@ -653,7 +689,7 @@ inline size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 inline Layout layout(int T, int N, int k) {
   Layout L{};
   const long items = static_cast<long>(T) * k;
-  if (items <= 8192) {
+  if (items <= 4096) {
     L.G = 1;
     L.TB = T > 0 ? T : 1;
     L.threads = 1024;
