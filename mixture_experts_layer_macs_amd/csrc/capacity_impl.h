@@ -345,23 +345,25 @@ __device__ bool any_placeable(const Args& a, int r, int t0, int t1) {
   const int tid = threadIdx.x, nthr = blockDim.x, k = a.k;
   if (tid == 0) s_any = 0;
   __syncthreads();
-  for (int t = t0 + tid; t < t1; t += nthr) {
+  // one (token, round) pair per step: the pairs are independent, so their
+  // loads overlap
+  const int nr = a.R - r + 1;
+  const int npairs = (t1 - t0) * nr;
+  for (int p = tid; p < npairs; p += nthr) {
+    const int t = t0 + p / nr, rr = r + p % nr;
     const int32_t* cs = a.cur + static_cast<size_t>(t) * k;
     const uint8_t* ss = a.st + static_cast<size_t>(t) * k;
-    const int32_t q = a.wq[t];
-    bool found = false;
-    for (int s = 0; s < k && !found; ++s) {
-      if ((ss[s] & ST_MASK) != ST_OVER) continue;
-      const int ge = cs[s] / a.group;
-      for (int rr = r; rr <= a.R && !found; ++rr) {
-        const int c = a.fallback[static_cast<size_t>(t) * a.R + (rr - 1)];
-        if (!a.active[c] || c / a.group != ge) continue;
-        bool held = false;
-        for (int s2 = 0; s2 < k; ++s2) held |= cs[s2] == c;
-        found = !held && a.drem[c] - static_cast<int64_t>(a.adm[c]) >= q;
-      }
+    const int c = a.fallback[static_cast<size_t>(t) * a.R + (rr - 1)];
+    const int gc = c / a.group;
+    bool held = false, grp = false;
+    for (int s = 0; s < k; ++s) {
+      const int e = cs[s];
+      held |= e == c;
+      grp |= (ss[s] & ST_MASK) == ST_OVER && e / a.group == gc;
     }
-    if (found) s_any = 1;
+    if (grp && !held && a.active[c] &&
+        a.drem[c] - static_cast<int64_t>(a.adm[c]) >= a.wq[t])
+      s_any = 1;
   }
   __syncthreads();
   return s_any != 0;
@@ -420,12 +422,17 @@ __device__ void cap_rounds(const Args& a, int g, int r_first, int r_last,
   }
   for (int r = r_first; r <= r_last; ++r) {
     if (r >= 1) {
+      const int before = s_pending;
       apply(a, r - 1, t0, t1, amax, (track || multi) ? &s_pending : nullptr,
             a.base + static_cast<size_t>(g) * a.N, a.drem, a.adm);
       __syncthreads();
       if (multi && threadIdx.x == 0 && s_pending != 0)
         atomicAdd(a.pending, static_cast<unsigned long long>(static_cast<long long>(s_pending)));
-      if (track && r <= a.R && (s_pending == 0 || !any_placeable(a, r, t0, t1))) {
+      // the placeability check runs after round 0's admission and after
+      // any round that placed nothing
+      if (track && r <= a.R &&
+          (s_pending == 0 ||
+           ((r == 1 || s_pending == before) && !any_placeable(a, r, t0, t1)))) {
         finalize_slots(a, g, t0, t1, red);
         __syncthreads();
         global_step(a, a.R + 1, red, run);
