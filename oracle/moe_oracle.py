@@ -71,6 +71,14 @@ independently implemented, by the GPU path):
       H over the batch's visual tokens; H~ = (H - mu) / (sigma + eps);
       w = sigmoid(-delta * H~) for visual tokens, 1 for text tokens.  delta
       and eps are not given by the page: parameters (defaults 1 and 1e-6).
+  R18 SERE similarity calibration (SERE §4.2: expert activations on a small
+      generic calibration set, a per-layer matrix of Frobenius
+      similarities, computed once offline): A_j = E_j(X) [T_cal, H] for a
+      calibration batch X, every token through every expert; S[i][j] =
+      <A_i, A_j>_F / (||A_i||_F ||A_j||_F) (the cosine of the flattened
+      matrices), S[j][j] = 1; an expert whose activations are all zero has
+      similarity 0 with every other expert.  The calibration set is
+      synthetic (x ~ N(0,1)), like every other input here.
   R17 router scores (MACS §3.1: a router network G scores every expert; its
       form is not given): a bias-free linear map z_t = W_g x_t with W_g
       stored [N, H], one row of H weights per expert, in the activation
@@ -94,7 +102,10 @@ CAP_CLAMP = 1 << 62       # capacities are clamped here so they fit int64
 # element decoding
 # --------------------------------------------------------------------------
 def decode(a: np.ndarray, dtype: str) -> np.ndarray:
-    """Exact fp64 values of a stored array (fp32, or bf16 bit patterns)."""
+    """Exact fp64 values of a stored array (fp32, fp64, or bf16 bit
+    patterns)."""
+    if dtype == "f64":
+        return np.asarray(a, dtype=np.float64)
     if dtype == "f32":
         return np.asarray(a, dtype=np.float32).astype(np.float64)
     if dtype == "bf16":
@@ -361,6 +372,36 @@ def dispatch(slot_out: np.ndarray, N: int):
             np.array([t for _, t, _ in rows], dtype=np.int32),
             np.array([s for _, _, s in rows], dtype=np.int32),
             slot_row)
+
+
+# --------------------------------------------------------------------------
+# SERE similarity calibration  [SERE §4.2; R18]
+# --------------------------------------------------------------------------
+def frobenius_similarity(acts: np.ndarray, dtype: str) -> np.ndarray:
+    """S[i][j] = <A_i, A_j>_F / (||A_i||_F ||A_j||_F) for the N matrices
+    A_j = acts[j] (any shape; flattened), in fp64 from the stored values.
+    S[j][j] = 1; a zero matrix has similarity 0 with every other one."""
+    N = acts.shape[0]
+    v = decode(acts, dtype).reshape(N, -1)
+    g = v @ v.T
+    d = np.sqrt(np.diag(g))
+    S = np.zeros((N, N))
+    for i in range(N):
+        for j in range(N):
+            if i == j:
+                S[i, j] = 1.0
+            elif d[i] > 0 and d[j] > 0:
+                S[i, j] = g[i, j] / (d[i] * d[j])
+    return S
+
+
+def calibration_activations(x_cal: np.ndarray, w13: np.ndarray, w2: np.ndarray,
+                            dtype: str) -> np.ndarray:
+    """A_j = E_j(X) for every expert j and every calibration token, fp64,
+    shape [N, T_cal, H]."""
+    x64 = decode(x_cal, dtype)
+    return np.stack([expert_ffn(x64, decode(w13[j], dtype), decode(w2[j], dtype))
+                     for j in range(w13.shape[0])])
 
 
 # --------------------------------------------------------------------------

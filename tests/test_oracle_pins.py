@@ -532,3 +532,54 @@ def test_router_bf16_inputs_and_expert_permutation():
     # the ranking is the lexsort order of the rounded fp32 scores
     order = np.lexsort((np.arange(7)[None, :].repeat(16, 0), -z.astype(np.float64)), axis=1)
     assert (order[:, :3] == ids).all() and (order[:, 3:5] == fb).all()
+
+
+# ---------------------------------------------------------------- similarity
+# SERE §4.2 (reading R18): Frobenius similarity of per-expert matrices.
+def test_similarity_matches_scipy_cosine():
+    from scipy.spatial.distance import cdist
+    rng = np.random.default_rng(4)
+    a = rng.standard_normal((9, 5, 7)).astype(np.float32)
+    S = O.frobenius_similarity(a, "f32")
+    v = a.reshape(9, -1).astype(np.float64)
+    ref = 1.0 - cdist(v, v, metric="cosine")
+    np.testing.assert_allclose(S, ref, atol=1e-12)
+    assert (np.diag(S) == 1.0).all() and (S == S.T).all()
+
+
+def test_similarity_closed_forms():
+    a = np.zeros((5, 2, 3), dtype=np.float32)
+    a[0] = [[1, 2, 0], [0, -1, 3]]
+    a[1] = 4.0 * a[0]                      # scaled: similarity 1
+    a[2] = -a[0]                           # negated: -1
+    a[3, 1, 1] = 5.0                       # overlaps a[0] in one entry (-1)
+    # a[4] stays zero: 0 with everyone, 1 with itself
+    S = O.frobenius_similarity(a, "f32")
+    n0 = math.sqrt(1 + 4 + 1 + 9)
+    assert abs(S[0, 1] - 1.0) < 1e-15 and abs(S[0, 2] + 1.0) < 1e-15
+    assert abs(S[0, 3] - (-5.0) / (n0 * 5.0)) < 1e-15
+    assert (S[4, :4] == 0).all() and (S[:4, 4] == 0).all() and S[4, 4] == 1.0
+    # bf16 storage of the same small values gives the same matrix
+    bits = (a.view(np.uint32) >> 16).astype(np.uint16)
+    assert (O.frobenius_similarity(bits, "bf16") == S).all()
+
+
+def test_calibration_activations_are_the_expert_ffn():
+    rng = np.random.default_rng(6)
+    N, H, I, T = 3, 8, 4, 5
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    w13 = (rng.standard_normal((N, 2 * I, H)) * 0.3).astype(np.float32)
+    w2 = (rng.standard_normal((N, H, I)) * 0.3).astype(np.float32)
+    A = O.calibration_activations(x, w13, w2, "f32")
+    assert A.shape == (N, T, H)
+    # torch's float64 SwiGLU of expert 1 as an independent evaluation
+    xt = torch.from_numpy(x.astype(np.float64))
+    g = torch.nn.functional.linear(xt, torch.from_numpy(w13[1, :I].astype(np.float64)))
+    u = torch.nn.functional.linear(xt, torch.from_numpy(w13[1, I:].astype(np.float64)))
+    y = torch.nn.functional.linear(torch.nn.functional.silu(g) * u,
+                                   torch.from_numpy(w2[1].astype(np.float64)))
+    np.testing.assert_allclose(A[1], y.numpy(), rtol=1e-13, atol=1e-15)
+    # identical experts have similarity 1
+    w13[2], w2[2] = w13[0], w2[0]
+    S = O.frobenius_similarity(O.calibration_activations(x, w13, w2, "f32"), "f64")
+    assert abs(S[0, 2] - 1.0) < 1e-14
