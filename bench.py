@@ -103,6 +103,10 @@ def parse():
     p.add_argument("--router", action="store_true",
                    help="time the router scores fused with top-k on the "
                         "prefill (T=8192) and decode (T=128) batches and exit")
+    p.add_argument("--similarity", action="store_true",
+                   help="time the SERE similarity calibration of one layer "
+                        "(256 calibration tokens through all 128 experts, then "
+                        "the Frobenius similarity) and exit")
     p.add_argument("--separate-routing", action="store_true",
                    help="route with the four separate calls instead of the "
                         "single fused launch")
@@ -336,6 +340,75 @@ def run_router(args):
                       "decode_t128": res["decode_t128"]}), flush=True)
 
 
+def run_similarity(args):
+    """SERE similarity calibration (SERE §4.2) for one layer of the qwen3
+    shape (N=128, H=2048, I=768, bf16): a calibration batch of 256
+    synthetic tokens goes through every expert (the grouped FFN with k = N,
+    32768 rows), then the Frobenius similarity of the 128 activation
+    matrices [256 x 2048] is formed.  Three copies of the activations
+    rotate between similarity calls so the 128 MB are not served from the
+    Infinity Cache; the similarity step is HBM-bound."""
+    import torch
+    from mixture_experts_layer_macs_amd import binding as B
+    from mixture_experts_layer_macs_amd import configs, synth
+    from mixture_experts_layer_macs_amd.staging import elem_tensor
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = configs.QWEN3_DECODE.with_(T=256)
+    T, H, N, I = wl.T, wl.H, wl.N, wl.I
+    x = elem_tensor(synth.activations(wl, args.seed), "bf16", dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    w13 = torch.empty((N, 2 * I, H), dtype=torch.bfloat16, device=dev).normal_(0.0, 0.02, generator=gen)
+    w2 = torch.empty((N, H, I), dtype=torch.bfloat16, device=dev).normal_(0.0, 0.02, generator=gen)
+    offsets = torch.arange(0, (N + 1) * T, T, dtype=torch.int32, device=dev)
+    row_token = torch.arange(T, dtype=torch.int32, device=dev).repeat(N)
+    h = torch.empty((T * N, I), dtype=torch.bfloat16, device=dev)
+    outs = [torch.empty((T * N, H), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    D = T * H
+    ws = B.new_workspace(B.moe_similarity_workspace_size(N, D, torch.bfloat16), dev)
+    sim = torch.empty((N, N), dtype=torch.float32, device=dev)
+
+    def ffn(i):
+        B.moe_ffn_gate_up(x, row_token, offsets, w13, N, h)
+        B.moe_ffn_down(h, offsets, w2, T, N, outs[i % 3])
+
+    def simc(i):
+        B.moe_expert_similarity(outs[i % 3].view(N, D), ws, sim)
+    for i in range(3):
+        ffn(i)
+    torch.cuda.synchronize()
+
+    def timed(fn, n):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        hold_gpu(0.02)
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+    us_sim = timed(simc, args.steps)
+    us_ffn = timed(ffn, max(5, args.steps // 5))
+    nbytes = N * D * 2 + N * N * 4
+    gbs = nbytes / (us_sim * 1e-6) / 1e9
+    print(json.dumps({"metric": "SERE similarity calibration: Frobenius similarity of the experts' calibration activations",
+                      "value": round(us_sim, 2), "unit": "us per layer (similarity step)",
+                      "higher_is_better": False, "n_gpus": 1, "dtype": "bf16",
+                      "data": "synthetic (seeded calibration tokens, random-init experts)",
+                      "config": {"workload": "similarity_n128_t256_h2048", "N": N, "T_cal": T,
+                                 "H": H, "I": I},
+                      "ffn_all_experts_us": round(us_ffn, 1),
+                      "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                   "bytes_per_launch": nbytes}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -350,6 +423,9 @@ def main():
         return
     if args.router:
         run_router(args)
+        return
+    if args.similarity:
+        run_similarity(args)
         return
     import torch
     if args.copy_probe_mib:

@@ -120,6 +120,34 @@ int moe_router_topk(const void* x, const void* w_gate, int T, int N, int H,
                     size_t workspace_bytes, void* stream);
 
 /*
+ * moe_expert_similarity -- the SERE similarity calibration (multi-image QA
+ * write-up §4.2: expert activations on a small generic calibration set give,
+ * once and offline, the per-layer matrix of Frobenius similarities that
+ * moe_sere_reroute takes as `sim`).
+ *
+ *   sim[i][j] = <A_i, A_j>_F / (||A_i||_F ||A_j||_F),   sim[j][j] = 1,
+ *
+ * where A_j is row j of acts, i.e. the D values of expert j's matrix
+ * flattened; a matrix of zeros has similarity 0 with every other one.  The
+ * out_rows of an FFN pass that sends every calibration token to every
+ * expert (expert_offsets = 0, T, 2T, ...; row_token = 0..T-1 for each
+ * expert; k = N) are exactly acts [N, T*H].
+ *
+ * acts   [N, D]  dtype MOE_BF16 (bf16 MFMA; D a multiple of 64 and acts at
+ *                most 2^31 bytes) or MOE_F32 (exact products summed in
+ *                fp64; meant for small inputs).  N <= 128, else MOE_EUNSUP.
+ * sim    f32[N, N]  out.
+ * Workspace of moe_similarity_workspace_size(N, D, dtype) bytes (scratch
+ * only; no initialisation).  The Gram matrix is accumulated in fp32 over
+ * runs of at most 4096 products (bf16), then in fp64 in a fixed order:
+ * deterministic.  Three launches on `stream`.
+ */
+size_t moe_similarity_workspace_size(int N, long long D, int dtype);
+int moe_expert_similarity(const void* acts, int N, long long D, int dtype,
+                          float* sim, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
  * moe_sere_reroute -- SERE similarity-guided re-routing (multi-image QA
  * write-up §4.1-§4.3), for decode batches.
  *

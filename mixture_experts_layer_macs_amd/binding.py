@@ -39,6 +39,8 @@ _F = ctypes.c_float
 _SIGS = {
     "moe_route": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P]),
     "moe_router_workspace_size": (_SZ, [_I, _I, _I, _I]),
+    "moe_similarity_workspace_size": (_SZ, [_I, ctypes.c_longlong, _I]),
+    "moe_expert_similarity": (_I, [_P, _I, ctypes.c_longlong, _I, _P, _P, _SZ, _P]),
     "moe_router_topk": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P,
                              _P, _SZ, _P]),
     "moe_sere_reroute": (_I, [_P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P]),
@@ -166,6 +168,26 @@ def moe_router_topk(x, w_gate, k, R, workspace, logits=None, topk_ids=None,
         _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
     _check(rc, "moe_router_topk")
     return logits, topk_ids, topk_gates, fallback_ids
+
+
+def moe_similarity_workspace_size(N, D, dtype) -> int:
+    return int(_lib.moe_similarity_workspace_size(N, D, _elem(dtype)))
+
+
+def moe_expert_similarity(acts, workspace, sim=None):
+    """Frobenius similarity of the N rows of acts [N, ...] (each row one
+    expert's flattened calibration activations); returns f32 [N, N]."""
+    N = acts.shape[0]
+    D = acts.numel() // N
+    if not acts.is_contiguous():
+        raise ValueError("acts must be contiguous")
+    sim = _empty((N, N), torch.float32, acts) if sim is None else sim
+    rc = _lib.moe_expert_similarity(
+        _dev(acts, acts.dtype, "acts"), N, D, _elem(acts.dtype),
+        _dev(sim, torch.float32, "sim", (N, N)),
+        _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
+    _check(rc, "moe_expert_similarity")
+    return sim
 
 
 def moe_sere_reroute(topk_ids, N, kprime, rho, sim, prot, slot_expert=None,

@@ -20,7 +20,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_macs.so")
 SOURCES = ["route.hip", "sere.hip", "capacity.hip", "dispatch.hip",
            "routing_fused.hip", "ffn.hip", "combine.hip", "entropy.hip",
-           "router.hip"]
+           "router.hip", "similarity.hip"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 

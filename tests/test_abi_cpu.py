@@ -157,3 +157,24 @@ def test_router_host_checks_and_workspace(lib):
     assert call(nbytes=16) == -1                  # workspace too small
     assert call(x=None) == -1
     assert call(T=0, x=None, ws=None) == 0        # T = 0: nothing to do
+
+
+def test_similarity_host_checks(lib):
+    P, I_, SZ, LL = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_longlong
+    f = lib.moe_similarity_workspace_size
+    f.restype = SZ
+    f.argtypes = [I_, LL, I_]
+    assert f(128, 256 * 2048, 1) >= 128 * 128 * 8
+    assert f(128, 100, 1) == 0            # bf16 needs D % 64 == 0
+    assert f(200, 64, 1) == 0             # N <= 128
+    assert f(8, 100, 0) > 0               # fp32: any D
+    lib.moe_expert_similarity.argtypes = [P, I_, LL, I_, P, P, SZ, P]
+    fake = P(0x1000)
+    call = lib.moe_expert_similarity
+    assert call(fake, 0, 64, 1, fake, fake, 1 << 20, None) == -1
+    assert call(fake, 8, 0, 1, fake, fake, 1 << 20, None) == -1
+    assert call(fake, 8, 100, 1, fake, fake, 1 << 20, None) == -2
+    assert call(fake, 200, 64, 1, fake, fake, 1 << 20, None) == -2
+    assert call(fake, 8, 64, 7, fake, fake, 1 << 20, None) == -2
+    assert call(None, 8, 64, 1, fake, fake, 1 << 20, None) == -1
+    assert call(fake, 8, 64, 1, fake, fake, 8, None) == -1    # workspace short

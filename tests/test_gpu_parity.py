@@ -427,3 +427,94 @@ def test_router_topk_parity(name, T, H, N, k, R, dtype, seed):
     if R:
         assert torch.equal(fb2, fb)
     say(f"max score err / bound {np.max(err / (bound + 1e-30)):.2e}")
+
+
+# ---------------------------------------------------------------- similarity
+# SERE §4.2 calibration (reading R18).  Kernel parity on given matrices:
+# the Gram entries are fp32 sums of at most 4096 exact bf16 products, then
+# fp64 sums, so |dG_ij| <= 4098 * 2^-24 * sum_k |a_ik a_jk| (fp32 partials
+# included); S = G_ij / sqrt(G_ii G_jj) inherits that relative error from
+# each factor, plus the final fp32 rounding.  Twice the bound is allowed.
+def _sim_bound(v):
+    a = np.abs(v)
+    e = 4098 * 2.0 ** -24 * (a @ a.T)
+    g = v @ v.T
+    d = np.sqrt(np.diag(g))
+    dn = np.outer(d, d)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = e / np.where(dn > 0, dn, 1.0)
+        ed = np.diag(e) / np.where(np.diag(g) > 0, np.diag(g), 1.0)
+    return 2.0 * (rel + np.abs(g / np.where(dn > 0, dn, 1.0)) * 0.5 *
+                  (ed[:, None] + ed[None, :])) + 2.0 ** -23
+
+
+SIM_CASES = [
+    ("n128_qwen_cal", 128, 256 * 2048, "bf16", 0),
+    ("n8_mixtral", 8, 64 * 4096, "bf16", 1),
+    ("n60_ragged", 60, 64 * 999, "bf16", 2),
+    ("n100_long", 100, 64 * 9001, "bf16", 3),
+    ("n33_short", 33, 64 * 3, "bf16", 4),
+    ("f32_n8", 8, 300, "f32", 5),
+    ("f32_n128", 128, 1000, "f32", 6),
+]
+
+
+@pytest.mark.parametrize("name,N,D,dtype,seed", SIM_CASES, ids=[c[0] for c in SIM_CASES])
+def test_expert_similarity_parity(name, N, D, dtype, seed):
+    import torch
+    from mixture_experts_layer_macs_amd import binding as B
+    from mixture_experts_layer_macs_amd.staging import elem_tensor
+    say(f"expert similarity {name}: N={N} D={D} {dtype}")
+    rng = np.random.default_rng(seed)
+    v = rng.standard_normal((N, D)).astype(np.float32)
+    # special rows: a scaled copy, a negated copy, a zero row, and a row
+    # correlated with row 0
+    v[1] = 0.5 * v[0]
+    v[2] = -v[0]
+    v[3] = 0.0
+    if N > 5:
+        v[5] = 0.6 * v[0] + 0.8 * v[4]
+    stored = synth.f32_to_bf16_bits(v) if dtype == "bf16" else v
+    ref = O.frobenius_similarity(stored, dtype)
+    vd = elem_tensor(stored, dtype, "cuda")
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    ws = B.new_workspace(B.moe_similarity_workspace_size(N, D, tdt), "cuda")
+    s1 = B.moe_expert_similarity(vd, ws).cpu().numpy().astype(np.float64)
+    s2 = B.moe_expert_similarity(vd, ws).cpu().numpy().astype(np.float64)
+    assert (s1 == s2).all()                       # deterministic
+    bound = _sim_bound(O.decode(stored, dtype))
+    err = np.abs(s1 - ref)
+    assert (err <= bound).all(), f"max err/bound {np.max(err / bound):.3f}"
+    assert (np.diag(s1) == 1.0).all()
+    assert (s1[3, np.arange(N) != 3] == 0.0).all()   # the zero matrix
+    say(f"max |dS| {err.max():.2e}")
+
+
+def test_calibration_pipeline_end_to_end():
+    """Calibration activations from the GPU's own FFN (every token through
+    every expert: k = N) fed to the similarity kernel, against the oracle's
+    fp64 activations.  The GPU rounds h and each output row to bf16
+    (relative 2^-9 per element), so the similarities agree to about 1e-3;
+    5e-3 absolute is allowed."""
+    import torch
+    from mixture_experts_layer_macs_amd import binding as B
+    from mixture_experts_layer_macs_amd.staging import elem_tensor
+    wl = configs.MM_PREFILL.with_(T=64, H=256, N=16, k=4, I=128)
+    T, H, N, I = wl.T, wl.H, wl.N, wl.I
+    say(f"calibration pipeline T={T} H={H} N={N} I={I}")
+    x = synth.activations(wl, 7)
+    w13, w2 = synth.expert_weights(wl, 7)
+    w13[3], w2[3] = w13[1], w2[1]                 # two identical experts
+    ref = O.frobenius_similarity(O.calibration_activations(x, w13, w2, "bf16"), "f64")
+    xd, w13d, w2d = (elem_tensor(a, "bf16", "cuda") for a in (x, w13, w2))
+    offsets = torch.arange(0, (N + 1) * T, T, dtype=torch.int32, device="cuda")
+    row_token = torch.arange(T, dtype=torch.int32, device="cuda").repeat(N)
+    h = torch.empty((T * N, I), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((T * N, H), dtype=torch.bfloat16, device="cuda")
+    B.moe_ffn_gate_up(xd, row_token, offsets, w13d, N, h)
+    B.moe_ffn_down(h, offsets, w2d, T, N, out)
+    ws = B.new_workspace(B.moe_similarity_workspace_size(N, T * H, torch.bfloat16), "cuda")
+    s = B.moe_expert_similarity(out.view(N, T * H), ws).cpu().numpy().astype(np.float64)
+    assert np.abs(s - ref).max() <= 5e-3, np.abs(s - ref).max()
+    assert s[1, 3] == 1.0 or abs(s[1, 3] - 1.0) < 1e-6   # identical experts
+    say(f"max |dS| {np.abs(s - ref).max():.2e}")
