@@ -565,29 +565,54 @@ __device__ void cap_rounds_dec(const Args& a, int g, int r, unsigned char* smem)
     }
     return;
   }
-  // this block's prefix over the earlier blocks of round r-1's proposals
-  for (int e = tid; e < N; e += nthr) bv[e] = 0;
-  __syncthreads();
+  // this block's prefix over the earlier blocks of round r-1's proposals.
+  // With N a multiple of 4, V = N / 4 threads cover a block's row with
+  // 16-byte loads and P = nthr / V such groups split the earlier blocks, so
+  // a thread issues all of its (at most 16) loads at once; otherwise one
+  // thread per expert.  The partial sums meet in LDS in a fixed order.
   {
     const int32_t* pp = a.part + static_cast<size_t>((r - 1) & 1) * GN;
-    const int n = g * N;
-    for (int i0 = tid; i0 < n; i0 += nthr * 8) {
-      int32_t v[8];
+    int64_t* red64 = reinterpret_cast<int64_t*>(run);  // free until the offers
+    if ((N & 3) == 0 && N / 4 <= nthr) {
+      const int V = N / 4, P = nthr / V;
+      const int v = tid % V, part = tid / V;
+      int64_t acc[4] = {0, 0, 0, 0};
+      if (part < P) {
+        for (int b0 = part; b0 < g; b0 += 16 * P) {
+          int4 x[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * nthr;
-        v[u] = i < n ? pp[i] : 0;
-      }
+          for (int u = 0; u < 16; ++u) {
+            const int b = b0 + u * P;
+            x[u] = b < g ? *reinterpret_cast<const int4*>(pp + static_cast<size_t>(b) * N + 4 * v)
+                         : make_int4(0, 0, 0, 0);
+          }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * nthr;
-        if (i < n && v[u])
-          atomicAdd(reinterpret_cast<unsigned long long*>(&bv[i % N]),
-                    static_cast<unsigned long long>(v[u]));
+          for (int u = 0; u < 16; ++u) {
+            acc[0] += x[u].x;
+            acc[1] += x[u].y;
+            acc[2] += x[u].z;
+            acc[3] += x[u].w;
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) red64[part * N + 4 * v + c] = acc[c];
       }
+      __syncthreads();
+      for (int e = tid; e < N; e += nthr) {
+        int64_t t = red64[e];
+        for (int q = 1; q < P; ++q) t += red64[q * N + e];
+        bv[e] = t;
+      }
+      __syncthreads();
+    } else {
+      for (int e = tid; e < N; e += nthr) {
+        int64_t t = 0;
+        for (int b = 0; b < g; ++b) t += pp[static_cast<size_t>(b) * N + e];
+        bv[e] = t;
+      }
+      __syncthreads();
     }
   }
-  __syncthreads();
   apply(a, r - 1, t0, t1, amax, &s_pending, bv, dv,
         last ? nullptr : a.adm + static_cast<size_t>((r - 1) % 3) * N);
   __syncthreads();
