@@ -574,7 +574,7 @@ __device__ void cap_rounds_dec(const Args& a, int g, int r, unsigned char* smem)
     const int32_t* pp = a.part + static_cast<size_t>((r - 1) & 1) * GN;
     int64_t* red64 = reinterpret_cast<int64_t*>(run);  // free until the offers
     if ((N & 3) == 0 && N / 4 <= nthr) {
-      const int V = N / 4, P = nthr / V;
+      const int V = N / 4, P = max(1, min(nthr / V, g));  // no more groups than blocks
       const int v = tid % V, part = tid / V;
       int64_t acc[4] = {0, 0, 0, 0};
       if (part < P) {

@@ -113,7 +113,7 @@ inline size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 inline Layout layout(int T, int N, int k) {
   Layout L{};
   const long items = static_cast<long>(T) * k;
-  if (items <= 8192) {
+  if (items <= 4096) {
     L.G = 1;
     L.TB = T > 0 ? T : 1;
     L.threads = 1024;
