@@ -268,7 +268,11 @@ __device__ void finalize_slots(const Args& a, int g, int t0, int t1,
 
 // Global step after round r's proposals (r <= R) or after the last apply
 // (r == R + 1).  Run by exactly one workgroup.
-__device__ void global_step(const Args& a, int r, int64_t* red, int32_t* lds) {
+// adm: the largest admitted running weight of round r-1 per expert -- the
+// global atomicMax target a.adm with several workgroups (cleared here after
+// use), or the single workgroup's own LDS maxima (cleared by its next apply).
+__device__ void global_step(const Args& a, int r, int64_t* red, int32_t* lds,
+                            unsigned long long* adm) {
   const int tid = threadIdx.x, nthr = blockDim.x, N = a.N, G = a.G;
   __shared__ double s_rv;
   if (r == 0) {
@@ -295,7 +299,7 @@ __device__ void global_step(const Args& a, int r, int64_t* red, int32_t* lds) {
       a.cap_q[e] = c;
       a.drem[e] = c;
       a.active[e] = (a.act_bits[e >> 5] >> (e & 31)) & 1u;
-      a.adm[e] = 0ull;  // a decentralised call may leave one round's maxima
+      if (G > 1) a.adm[e] = 0ull;  // a decentralised call may leave one round's maxima
     }
     __syncthreads();
     if (tid < 32) a.act_bits[tid] = 0u;
@@ -305,8 +309,8 @@ __device__ void global_step(const Args& a, int r, int64_t* red, int32_t* lds) {
     }
   } else {
     for (int e = tid; e < N; e += nthr) {
-      const int64_t m = static_cast<int64_t>(a.adm[e]);
-      a.adm[e] = 0ull;
+      const int64_t m = static_cast<int64_t>(adm[e]);
+      if (G > 1) adm[e] = 0ull;
       const int64_t d = a.drem[e] - m;
       a.drem[e] = d;
       if (r > a.R) a.load_q[e] = a.capv[e] - d;
@@ -340,7 +344,8 @@ __device__ void global_step(const Args& a, int r, int64_t* red, int32_t* lds) {
 // -- c in A, in the group of one of its overflowed slots, not held, and at
 // least the token's weight of capacity left -- no later round admits
 // anything, and the slots can be finalised at once.
-__device__ bool any_placeable(const Args& a, int r, int t0, int t1) {
+__device__ bool any_placeable(const Args& a, int r, int t0, int t1,
+                              const unsigned long long* adm) {
   __shared__ int s_any;
   const int tid = threadIdx.x, nthr = blockDim.x, k = a.k;
   if (tid == 0) s_any = 0;
@@ -362,7 +367,7 @@ __device__ bool any_placeable(const Args& a, int r, int t0, int t1) {
       grp |= (ss[s] & ST_MASK) == ST_OVER && e / a.group == gc;
     }
     if (grp && !held && a.active[c] &&
-        a.drem[c] - static_cast<int64_t>(a.adm[c]) >= a.wq[t])
+        a.drem[c] - static_cast<int64_t>(adm[c]) >= a.wq[t])
       s_any = 1;
   }
   __syncthreads();
@@ -415,7 +420,7 @@ __device__ void cap_rounds(const Args& a, int g, int r_first, int r_last,
     if (ph == PH_FINISH) {
       finalize_slots(a, g, t0, t1, red);
       if (!last_block(a)) return;
-      global_step(a, a.R + 1, red, run);
+      global_step(a, a.R + 1, red, run, a.adm);
       if (threadIdx.x == 0) *a.phase = PH_DONE;
       return;
     }
@@ -424,7 +429,7 @@ __device__ void cap_rounds(const Args& a, int g, int r_first, int r_last,
     if (r >= 1) {
       const int before = s_pending;
       apply(a, r - 1, t0, t1, amax, (track || multi) ? &s_pending : nullptr,
-            a.base + static_cast<size_t>(g) * a.N, a.drem, a.adm);
+            a.base + static_cast<size_t>(g) * a.N, a.drem, multi ? a.adm : nullptr);
       __syncthreads();
       if (multi && threadIdx.x == 0 && s_pending != 0)
         atomicAdd(a.pending, static_cast<unsigned long long>(static_cast<long long>(s_pending)));
@@ -432,10 +437,10 @@ __device__ void cap_rounds(const Args& a, int g, int r_first, int r_last,
       // any round that placed nothing
       if (track && r <= a.R &&
           (s_pending == 0 ||
-           ((r == 1 || s_pending == before) && !any_placeable(a, r, t0, t1)))) {
+           ((r == 1 || s_pending == before) && !any_placeable(a, r, t0, t1, amax)))) {
         finalize_slots(a, g, t0, t1, red);
         __syncthreads();
-        global_step(a, a.R + 1, red, run);
+        global_step(a, a.R + 1, red, run, amax);
         __syncthreads();
         return;
       }
@@ -451,7 +456,7 @@ __device__ void cap_rounds(const Args& a, int g, int r_first, int r_last,
     } else {
       __syncthreads();
     }
-    global_step(a, r, red, run);
+    global_step(a, r, red, run, multi ? a.adm : amax);
     __syncthreads();
   }
 }
