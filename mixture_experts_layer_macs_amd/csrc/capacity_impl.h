@@ -181,7 +181,8 @@ __device__ void propose_round(const Args& a, int r, int g, int t0, int t1,
 }
 
 // Admit or refuse the proposals of round r against base (this block's
-// exclusive prefix of round r's proposal weight over the earlier blocks) and
+// exclusive prefix of round r's proposal weight over the earlier blocks;
+// null for a single workgroup, where it is zero) and
 // drem (capacity left before round r).  amax (LDS) ends with this block's
 // largest admitted running weight per expert, also folded into adm[] with
 // atomicMax unless adm is null.
@@ -198,7 +199,7 @@ __device__ void apply(const Args& a, int r, int t0, int t1,
   if (r == 0) {
     for (int i = t0 * k + tid; i < t1 * k; i += nthr) {
       const int e = a.cur[i];
-      const int64_t v = base[e] + a.incl_slot[i];
+      const int64_t v = (base ? base[e] : 0) + a.incl_slot[i];
       if (v <= drem[e]) {
         atomicMax(&amax[e], static_cast<unsigned long long>(v));
       } else {
@@ -211,7 +212,7 @@ __device__ void apply(const Args& a, int r, int t0, int t1,
       const int s = a.offer_s[t];
       if (s < 0) continue;
       const int c = a.offer_c[t];
-      const int64_t v = base[c] + a.incl_tok[t];
+      const int64_t v = (base ? base[c] : 0) + a.incl_tok[t];
       if (v <= drem[c]) {
         const size_t i = static_cast<size_t>(t) * k + s;
         a.st[i] = (a.st[i] & ST_SERE) | ST_PLACED;
@@ -321,7 +322,9 @@ __device__ void global_step(const Args& a, int r, int64_t* red, int32_t* lds,
   if (G > 1 && r >= 1 && r <= a.R && tid == 0 && atomicAdd(a.pending, 0ull) == 0ull)
     *a.phase = PH_FINISH;
   if (r <= a.R) {
-    column_scan<int64_t>(a.part, a.base, nullptr, G, N, lds, a.lds_scan);
+    // one workgroup: no earlier block, every prefix base is zero (apply is
+    // passed no base array)
+    if (G > 1) column_scan<int64_t>(a.part, a.base, nullptr, G, N, lds, a.lds_scan);
   } else {
     int64_t nd = 0, nm = 0;
     for (int g = tid; g < G; g += nthr) {
@@ -429,7 +432,8 @@ __device__ void cap_rounds(const Args& a, int g, int r_first, int r_last,
     if (r >= 1) {
       const int before = s_pending;
       apply(a, r - 1, t0, t1, amax, (track || multi) ? &s_pending : nullptr,
-            a.base + static_cast<size_t>(g) * a.N, a.drem, multi ? a.adm : nullptr);
+            multi ? a.base + static_cast<size_t>(g) * a.N : nullptr, a.drem,
+            multi ? a.adm : nullptr);
       __syncthreads();
       if (multi && threadIdx.x == 0 && s_pending != 0)
         atomicAdd(a.pending, static_cast<unsigned long long>(static_cast<long long>(s_pending)));
