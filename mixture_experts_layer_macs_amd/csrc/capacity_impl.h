@@ -354,7 +354,9 @@ __device__ bool any_placeable(const Args& a, int r, int t0, int t1,
   if (tid == 0) s_any = 0;
   __syncthreads();
   // one (token, round) pair per step: the pairs are independent, so their
-  // loads overlap
+  // loads overlap; with one group of all N experts (the one-GPU case) the
+  // group test, an integer division per slot otherwise, drops out
+  const bool one_group = a.group >= a.N;
   const int nr = a.R - r + 1;
   const int npairs = (t1 - t0) * nr;
   for (int p = tid; p < npairs; p += nthr) {
@@ -362,12 +364,12 @@ __device__ bool any_placeable(const Args& a, int r, int t0, int t1,
     const int32_t* cs = a.cur + static_cast<size_t>(t) * k;
     const uint8_t* ss = a.st + static_cast<size_t>(t) * k;
     const int c = a.fallback[static_cast<size_t>(t) * a.R + (rr - 1)];
-    const int gc = c / a.group;
+    const int gc = one_group ? 0 : c / a.group;
     bool held = false, grp = false;
     for (int s = 0; s < k; ++s) {
       const int e = cs[s];
       held |= e == c;
-      grp |= (ss[s] & ST_MASK) == ST_OVER && e / a.group == gc;
+      grp |= (ss[s] & ST_MASK) == ST_OVER && (one_group || e / a.group == gc);
     }
     if (grp && !held && a.active[c] &&
         a.drem[c] - static_cast<int64_t>(adm[c]) >= a.wq[t])
