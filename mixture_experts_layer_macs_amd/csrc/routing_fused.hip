@@ -231,6 +231,26 @@ __global__ __launch_bounds__(FT) void routing_kernel(Args f, cap::Args ca,
   constexpr int TPB = FT / GT;
   const int grp = threadIdx.x / GT;
   const int t = blockIdx.x * TPB + grp;
+  // The tail's SERE step scans similarity and protection rows that are cold
+  // in HBM.  The first threads of the grid read them once now, 16 bytes
+  // each, so that the memory-side cache holds them by the time the tail
+  // asks; the loads complete under the route step (the hand-off waits for
+  // every outstanding load anyway).
+  int4 pf = make_int4(0, 0, 0, 0);
+  bool pf_on = false;
+  if (f.kprime > 0 && ((reinterpret_cast<uintptr_t>(f.sim) |
+                         reinterpret_cast<uintptr_t>(f.prot)) & 15) == 0) {
+    const size_t sc = static_cast<size_t>(f.N) * f.N / 4;   // 16-byte chunks of sim
+    const size_t pc = static_cast<size_t>(f.N) * f.N / 16;  // and of prot
+    const size_t i = static_cast<size_t>(blockIdx.x) * FT + threadIdx.x;
+    if (i < sc) {
+      pf = reinterpret_cast<const int4*>(f.sim)[i];
+      pf_on = true;
+    } else if (i < sc + pc) {
+      pf = reinterpret_cast<const int4*>(f.prot)[i - sc];
+      pf_on = true;
+    }
+  }
   rt::route_token<GT>(f.logits + static_cast<size_t>(t) * f.N, f.N, f.k, f.R, t, t < f.T,
                       smem + grp * rt::token_lds_bytes(f.N, GT), f.topk_ids,
                       f.topk_gates, f.fallback_ids);
@@ -240,6 +260,8 @@ __global__ __launch_bounds__(FT) void routing_kernel(Args f, cap::Args ca,
   // once per workgroup, not once per wave: every wave first waits for its
   // own stores, the barrier joins them, and one thread fences and counts.
   wait_stores();
+  // never true (T >= 0): only keeps the warming loads from being dropped
+  if (pf_on && f.T < 0 && (pf.x | pf.y | pf.z | pf.w) == 0) s_last = 0;
   __syncthreads();
   if (threadIdx.x == 0) {
     __threadfence();
