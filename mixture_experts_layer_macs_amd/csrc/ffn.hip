@@ -620,6 +620,118 @@ void gemm_dual_kernel(Args a) {
   }
 }
 
+// Small-batch decode: with a handful of active experts, tiles of 128 weight
+// rows give only a few hundred workgroups, and each streams its panel at the
+// rate of one CU.  This kernel streams panels of 16 weight rows instead, for
+// token tiles of 16 rows (the 16 x 16 x 32 MFMA): eight times the
+// workgroups for the same bytes, each over the whole reduction, several per
+// CU with a shallow ring.  The 4 waves split each 128-wide K slice: wave w
+// runs the MFMA of K sub-step w into its own accumulator and loads rows
+// [4 w, 4 w + 4) of both operands, and the four partial accumulators are
+// added in LDS in wave order before the epilogue.
+//
+// Gate-up panel row p is gate column 2 * (p / 4) + p % 4 of the panel when
+// p % 4 < 2, else the up row of column 2 * (p / 4) + p % 4 - 2, so each
+// lane's four accumulator rows (panel rows 4 * (lane / 16) + i) hold two
+// gate rows and their up rows.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+template <int MODE, int S>
+__global__ __launch_bounds__(4 * MOE_WAVE) void gemm_skinny_kernel(Args a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int BM = 16, BN = 16, BK = 128;
+  constexpr int SLICE_A = BM * BK * 2, SLICE_B = BN * BK * 2;  // 4 KB each
+  constexpr int STAGE = SLICE_A + SLICE_B;
+  static_assert(S >= 2 && S * STAGE >= 4 * MOE_WAVE * 4 * 4, "LDS for the partials");
+  int j, m0, nt, Mj, row0;
+  if (!find_tile_s<BM>(a, reinterpret_cast<int*>(smem), j, m0, nt, Mj, row0)) return;
+
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / MOE_WAVE);
+  const int K = a.K;
+  const uint32_t row_bytes = static_cast<uint32_t>(K) * 2;
+  const int tile_rows = min(BM, Mj - m0);
+  const i32x4 rsrc_a =
+      MODE == GATEUP ? buffer_rsrc(a.a, static_cast<uint32_t>(a.a_rows) * row_bytes)
+                     : buffer_rsrc(a.a + static_cast<size_t>(row0 + m0) * K,
+                                   static_cast<uint32_t>(tile_rows) * row_bytes);
+  const i32x4 rsrc_b = buffer_rsrc(a.w + static_cast<size_t>(j) * a.w_stride,
+                                   static_cast<uint32_t>(a.w_stride) * 2);
+  // wave w fills rows [4 w, 4 w + 4) of both operands (one load each: 4
+  // rows of 256 bytes); the lane filling LDS slot s of row r fetches chunk
+  // s ^ r
+  const int row = wave * 4 + lane / 16, ch = (lane % 16) ^ row;
+  uint32_t va, vb;
+  if (MODE == GATEUP)
+    va = row < tile_rows
+             ? static_cast<uint32_t>(a.row_token[row0 + m0 + row]) * row_bytes + ch * 16
+             : OOB_OFF;
+  else
+    va = static_cast<uint32_t>(row) * row_bytes + ch * 16;  // past the tile: outside
+  {
+    uint32_t wrow;
+    if (MODE == GATEUP) {
+      const int c = nt * 8 + 2 * (row / 4) + row % 2;
+      wrow = row % 4 < 2 ? c : a.I + c;
+    } else {
+      wrow = nt * BN + row;
+    }
+    vb = wrow * row_bytes + ch * 16;
+  }
+  const uint32_t lds_base = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char*)(smem))));
+  const int nk = K / BK;
+  auto issue = [&](int s) {
+    const uint32_t k0 = static_cast<uint32_t>(min(s, nk - 1) * BK * 2);
+    const uint32_t st = lds_base + (s % S) * STAGE + wave * 1024;
+    lds_dma16(rsrc_a, va, k0, st);
+    lds_dma16(rsrc_b, vb, k0, st + SLICE_A);
+  };
+  typedef __attribute__((address_space(3))) const bf16x8 lds_frag;
+  typedef __attribute__((address_space(3))) const unsigned char lds_byte;
+  lds_byte* lds0 = (lds_byte*)(smem);
+  const int frow = lane % 16;
+  const int sw = ((wave * 4 + lane / 16) ^ frow) << 4;  // K sub-step = wave
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s0 = 0; s0 + 1 < S; ++s0) issue(s0);
+  for (int s0 = 0; s0 < nk; ++s0) {
+    wait_vmcnt<(S - 2) * 2>();
+    wg_barrier();
+    issue(s0 + S - 1);
+    lds_byte* st = lds0 + (s0 % S) * STAGE;
+    const bf16x8 fa = *(lds_frag*)(st + frow * (BK * 2) + sw);
+    const bf16x8 fb = *(lds_frag*)(st + SLICE_A + frow * (BK * 2) + sw);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, fa, acc, 0, 0, 0);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);  // [wave][lane][4]
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[(wave * MOE_WAVE + lane) * 4 + r] = acc[r];
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float v = red[lane * 4 + r];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) v += red[(w * MOE_WAVE + lane) * 4 + r];
+    acc[r] = v;
+  }
+  // lane holds token row lane % 16 and panel rows 4 * (lane / 16) + r
+  const bool live = m0 + frow < Mj;
+  const size_t orow = static_cast<size_t>(row0 + m0 + frow) * a.NC;
+  const int g4 = lane / 16;
+  if constexpr (MODE == GATEUP) {
+    const uint32_t pk = pack_bf16x2(silu(acc[0]) * acc[2], silu(acc[1]) * acc[3]);
+    if (live) *reinterpret_cast<uint32_t*>(&a.out[orow + nt * 8 + 2 * g4]) = pk;
+  } else {
+    uint2 pk;
+    pk.x = pack_bf16x2(acc[0], acc[1]);
+    pk.y = pack_bf16x2(acc[2], acc[3]);
+    if (live) *reinterpret_cast<uint2*>(&a.out[orow + nt * BN + 4 * g4]) = pk;
+  }
+}
+
 // ------------------------------------------------------------- fp32 path
 // Plain fp32 FMA kernels (small fp32 layers); one thread per output value.
 __device__ __forceinline__ int expert_of_row(const int32_t* off, int N, int row) {
@@ -679,7 +791,9 @@ static int launch_gemm_dma(const Args& a, int rows_cap, hipStream_t s) {
       return MOE_EHIP;
     attr_set = true;
   }
-  const int mt_ub = (rows_cap + BM - 1) / BM + a.N;
+  // tiles <= sum over active experts of (rows / BM + 1), and at most
+  // min(N, rows) experts are active
+  const int mt_ub = (rows_cap + BM - 1) / BM + std::min(a.N, rows_cap);
   long grid = static_cast<long>(mt_ub) * a.n_tiles;
   grid = (grid + 7) / 8 * 8;
   hipLaunchKernelGGL((gemm_dma_kernel<MODE, BM, BN, BK, WM, WN, S, WPE, SB>), dim3(grid),
@@ -703,11 +817,30 @@ static int launch_gemm_dual(Args a, int rows_cap, hipStream_t s) {
   }
   a.dual_limit = WPE * cu_count();
   constexpr int BMIN = BMA < BMB ? BMA : BMB;
-  const int mt_ub = (rows_cap + BMIN - 1) / BMIN + a.N;
+  const int mt_ub = (rows_cap + BMIN - 1) / BMIN + std::min(a.N, rows_cap);
   long grid = static_cast<long>(mt_ub) * a.n_tiles;
   grid = (grid + 7) / 8 * 8;
   hipLaunchKernelGGL((gemm_dual_kernel<MODE, BN, BK, BMA, SA, BMB, SB, WPE>), dim3(grid),
                      dim3(4 * MOE_WAVE), lds, s, a);
+  return MOE_OK;
+}
+
+// Small-batch decode: panels of 16 weight rows (see gemm_skinny_kernel).
+#ifndef MOE_SKINNY_S
+#define MOE_SKINNY_S 3
+#endif
+constexpr int SKINNY_S = MOE_SKINNY_S;
+template <int MODE>
+static int launch_gemm_skinny(Args a, int rows_cap, hipStream_t s) {
+  constexpr int BM = 16, BN = 16, BK = 128;
+  constexpr size_t lds = static_cast<size_t>(SKINNY_S) * (BM + BN) * BK * 2;
+  static_assert(lds <= 65536, "default LDS limit");
+  a.n_tiles = MODE == GATEUP ? a.I / (BN / 2) : a.NC / BN;
+  const int mt_ub = (rows_cap + BM - 1) / BM + std::min(a.N, rows_cap);
+  long grid = static_cast<long>(mt_ub) * a.n_tiles;
+  grid = (grid + 7) / 8 * 8;
+  hipLaunchKernelGGL((gemm_skinny_kernel<MODE, SKINNY_S>), dim3(grid), dim3(4 * MOE_WAVE), lds,
+                     s, a);
   return MOE_OK;
 }
 
@@ -820,6 +953,19 @@ static bool decode_tiles(int T, int N, int k) {
 }
 
 
+// The smallest batches (a few dispatch rows) stream 16-row weight panels:
+// gate-up up to 32 dispatch rows, down up to 16 (measured on the 2048 x 768
+// expert shape at 8, 16 and 32 rows).
+#ifndef MOE_SKINNY_ROWS_GU
+#define MOE_SKINNY_ROWS_GU 32
+#endif
+#ifndef MOE_SKINNY_ROWS_DN
+#define MOE_SKINNY_ROWS_DN 16
+#endif
+static bool skinny_tiles(int T, int k, int mode) {
+  return static_cast<long>(T) * k <= (mode == GATEUP ? MOE_SKINNY_ROWS_GU : MOE_SKINNY_ROWS_DN);
+}
+
 // Decode weight-tile height: 256 rows unless that gives fewer tiles than
 // two per CU (the number of experts with rows is at most min(N, T*k)).
 static bool narrow_decode_tiles(int T, int N, int k, int cols_per_256) {
@@ -884,7 +1030,9 @@ extern "C" int moe_ffn_gate_up(const void* x, const int32_t* row_token,
   if (decode_tiles(T, N, k)) {
     int st;
     g.n_tiles = I / 64;
-    if (H >= 4096) {
+    if (skinny_tiles(T, k, GATEUP)) {
+      st = launch_gemm_skinny<GATEUP>(g, rows_cap, s);
+    } else if (H >= 4096) {
       constexpr DecCfg c = DEC_GU_WIDE;
       st = launch_gemm_dma<GATEUP, c.bm, 128, c.bk, 1, 4, c.s, dec_wpe(c, 128)>(g, rows_cap, s);
     } else {
@@ -937,7 +1085,9 @@ extern "C" int moe_ffn_down(const void* h, const int32_t* expert_offsets,
   if (decode_tiles(T, N, k)) {
     int st;
     const bool narrow = narrow_decode_tiles(T, N, k, H / 256);
-    if (I >= 4096) {
+    if (skinny_tiles(T, k, DOWN)) {
+      st = launch_gemm_skinny<DOWN>(d, rows_cap, s);
+    } else if (I >= 4096) {
       constexpr DecCfg c = DEC_DN_WIDE;
       const bool nar = narrow || !DN_256_WIDE;
       d.n_tiles = nar ? H / 128 : H / 256;

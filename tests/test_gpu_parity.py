@@ -51,6 +51,17 @@ FULL_Y_CASES = [
     ("qwen3_decode_b128_s1", configs.QWEN3_DECODE, 1),
     ("sweep_layer_macs_b64", configs.SWEEP_LAYER.with_(T=64, kprime=2), 0),
     ("sweep_layer_b1", configs.SWEEP_LAYER.with_(T=1, kprime=1), 0),
+    # a few dispatch rows: the 16-row weight panel kernels (gate-up up to 32
+    # rows, down up to 16), on both sides of the thresholds
+    ("sweep_layer_b2", configs.SWEEP_LAYER.with_(T=2, kprime=0), 1),
+    ("sweep_layer_b4", configs.SWEEP_LAYER.with_(T=4, kprime=0), 2),
+    ("mid_bf16_skinny_t3", _mid_bf16(T=3, kprime=0), 8),
+    ("mid_bf16_skinny_t4_h768", _mid_bf16(T=4, H=768, I=384, gamma=0.7), 9),
+    ("mid_bf16_t5", _mid_bf16(T=5), 10),
+    ("mid_bf16_t9", _mid_bf16(T=9), 12),
+    # one expert with more than 16 rows: several 16-row token tiles
+    ("mid_bf16_skinny_k1_t30", _mid_bf16(T=30, k=1, R=2, skew_expert0=10.0,
+                                                gamma=math.inf), 11),
 ]
 
 
