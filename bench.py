@@ -46,9 +46,9 @@ GEMM_SOURCES = ("mixture_experts_layer_macs_amd/csrc/ffn.hip",
                 "mixture_experts_layer_macs_amd/csrc/dma.h")
 HBM_COUNTERS = {
     "qwen3_decode_b128": dict(
-        kernel="gate_up_swiglu", fetch_kib=130579.7, write_kib=1536.0,
+        kernel="gate_up_swiglu", fetch_kib=130591.3, write_kib=1536.0,
         fetch_scale=2.0, write_scale=1.0,
-        sources_sha256="92a56e7fff2b6ef319738c83715a52a7ceb8b42553c33faf98a10367c72422b6"),
+        sources_sha256="f1fd8b7617762a8c7ebfebb380783f1b28f490fcc6073b541065acb7dc7ccd5d"),
 }
 
 
