@@ -1099,12 +1099,7 @@ extern "C" int moe_ffn_down(const void* h, const int32_t* expert_offsets,
       }
     } else {
       constexpr DecCfg c = DEC_DN;
-      // up to 1024 dispatch rows the 128-column tiles (twice the tiles, and
-      // 40 KB of LDS instead of 72 KB, so four workgroups per CU) measured
-      // faster on the 2048 x 768 expert shape, with and without SERE (e.g.
-      // 128 tokens, top-8: 28.5 -> 26.8 us with SERE, 60.0 -> 56.1 without);
-      // at 2048 rows the 256-column tiles were as fast or faster
-      const bool nar = narrow || static_cast<long>(T) * k <= 1024 || !DN_256;
+      const bool nar = narrow || !DN_256;
       d.n_tiles = nar ? H / 128 : H / 256;
       if constexpr (DN_256) {
         st = nar ? launch_gemm_dma<DOWN, c.bm, 128, c.bk, 1, 4, c.s, dec_wpe(c, 128)>(d, rows_cap, s)
