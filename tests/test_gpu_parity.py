@@ -59,6 +59,9 @@ FULL_Y_CASES = [
     ("mid_bf16_skinny_t4_h768", _mid_bf16(T=4, H=768, I=384, gamma=0.7), 9),
     ("mid_bf16_t5", _mid_bf16(T=5), 10),
     ("mid_bf16_t9", _mid_bf16(T=9), 12),
+    # long reductions in the 16-row panel kernels (32 K slices)
+    ("mid_bf16_skinny_h4096", _mid_bf16(T=3, H=4096, I=512, k=2), 13),
+    ("mid_bf16_skinny_i4096", _mid_bf16(T=2, H=512, I=4096), 14),
     # one expert with more than 16 rows: several 16-row token tiles
     ("mid_bf16_skinny_k1_t30", _mid_bf16(T=30, k=1, R=2, skew_expert0=10.0,
                                                 gamma=math.inf), 11),
