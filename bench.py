@@ -44,6 +44,8 @@ METRIC = ("MoE-layer tokens/s (prefill) + decode-step µs at B=128; "
 GEMM_SOURCES = ("mixture_experts_layer_macs_amd/csrc/ffn.hip",
                 "mixture_experts_layer_macs_amd/csrc/common.h",
                 "mixture_experts_layer_macs_amd/csrc/dma.h")
+DIFF_REPS = 5  # timed-region pairs per in-step kernel duration
+
 HBM_COUNTERS = {
     "qwen3_decode_b128": dict(
         kernel="gate_up_swiglu", fetch_kib=130591.3, write_kib=1536.0,
@@ -483,21 +485,27 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
+    graph_cache = {}
+
     def timed(skip=(), graph=False):
         """Mean ms per step over `steps` steps, HIP events at the two ends of
         the region only.  Eager: the stream is held by a spin kernel while
         the host queues the steps, so they then run back to back.  Graph: the
-        step is captured once per weight copy and replayed."""
+        step is captured once per weight copy (and kept for later regions
+        with the same kernels left out) and replayed."""
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         if graph:
-            graphs = []
-            cap_stream = torch.cuda.Stream()
-            for c in range(len(w13s)):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=cap_stream):
-                    step(c, skip)
-                graphs.append(g)
+            if skip not in graph_cache:
+                graphs = []
+                cap_stream = torch.cuda.Stream()
+                for c in range(len(w13s)):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=cap_stream):
+                        step(c, skip)
+                    graphs.append(g)
+                graph_cache[skip] = graphs
+            graphs = graph_cache[skip]
             for i in range(args.warmup):
                 graphs[i % len(graphs)].replay()
             torch.cuda.synchronize()
@@ -524,13 +532,20 @@ def main():
     graph_ms = None if args.no_graph else timed(graph=True)
 
     # In-step duration of each expert GEMM: the step time minus the time of
-    # the same step with that kernel left out (same timing mode).  An event
+    # the same step with that kernel left out (same timing mode), as the
+    # median over DIFF_REPS alternating pairs of timed regions, since one
+    # difference of two step times carries the noise of both.  An event
     # pair around a single kernel would add the dispatch gap after the first
     # event to the interval.
     use_graph = not args.no_graph
-    full_ms = graph_ms if use_graph else ms
-    gu_ms = full_ms - timed(("gate_up",), use_graph)
-    dn_ms = full_ms - timed(("down",), use_graph)
+
+    def in_step_ms(name):
+        diffs = [timed((), use_graph) - timed((name,), use_graph)
+                 for _ in range(DIFF_REPS)]
+        return float(np.median(diffs))
+
+    gu_ms = in_step_ms("gate_up")
+    dn_ms = in_step_ms("down")
 
     off = lay.disp["expert_offsets"].cpu().numpy()
     counts = np.diff(off)
