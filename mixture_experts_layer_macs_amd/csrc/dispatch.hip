@@ -4,16 +4,20 @@
 // permuted copy of the activations is ever written.
 //
 // Same block decomposition as the capacity step: each workgroup ranks its
-// own slots per expert (ordered per-key prefix with unit weights), the last
-// workgroup to finish turns the per-block counts into expert offsets and
-// per-block bases, and a second launch scatters the row maps.  A batch that
+// own slots per expert (ordered per-key prefix with unit weights) and
+// writes its per-expert counts; in a second launch every workgroup sums the
+// counts into the expert offsets and its own bases and scatters the row
+// maps.  Beyond 128 workgroups the last workgroup of the first launch (an
+// atomic ticket) computes offsets and bases for all instead.  A batch that
 // fits one workgroup does everything in a single launch.
 #include "dispatch_impl.h"
 
 namespace moe {
 namespace disp {
 
-// phase 0: count + (last block) offsets; phase 1: scatter; single block: both
+// phase 0: count (+ offsets and bases by the last block beyond 128 blocks);
+// phase 1: scatter (+ its own offsets and bases up to 128 blocks); single
+// block: all of it
 __global__ __launch_bounds__(1024) void dispatch_kernel(Args a, int phase_first,
                                                         int phase_last) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -23,8 +27,13 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(Args a, int phase_first,
   __shared__ int s_last;
   const int g = blockIdx.x;
   const int t0 = g * a.TB, t1 = min(a.T, t0 + a.TB);
+  if (phase_first == 1 && a.G <= DEC_MAX_G) {  // after a count-only launch
+    scatter_dec(a, g, smem);
+    return;
+  }
   if (phase_first == 0) {
     count_block(a, g, t0, t1, run);
+    if (a.G > 1 && a.G <= DEC_MAX_G) return;  // the next launch does the rest
     if (a.G > 1) {  // one agent-scope fence per workgroup, not per wave
       wait_stores();
       __syncthreads();
@@ -40,7 +49,8 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(Args a, int phase_first,
     scan_offsets(a, tot, run);
     __syncthreads();
   }
-  if (phase_last == 1) scatter_block(a, g, t0, t1);
+  if (phase_last == 1)
+    scatter_block(a, t0, t1, a.offsets, a.base + static_cast<size_t>(g) * a.N);
 }
 
 }  // namespace disp
