@@ -121,6 +121,9 @@ ROUTING_CASES = [
                                           group=1024, gamma=1.0), 7),
     ("k1_many_tokens", configs.TINY_F32.with_(T=9000, N=8, k=1, R=3, gamma=0.9,
                                               skew_expert0=3.0), 8),
+    # 133 token blocks: capacity rounds and dispatch past 128 blocks take
+    # the last-workgroup (ticket) path
+    ("prefill_133_blocks", configs.MM_PREFILL.with_(T=17000, gamma=0.8), 9),
 ]
 
 
