@@ -48,9 +48,9 @@ DIFF_REPS = 5  # timed-region pairs per in-step kernel duration
 
 HBM_COUNTERS = {
     "qwen3_decode_b128": dict(
-        kernel="gate_up_swiglu", fetch_kib=130590.2051, write_kib=1536.0,
+        kernel="gate_up_swiglu", fetch_kib=130590.2632, write_kib=1536.0039,
         fetch_scale=2.0, write_scale=1.0,
-        sources_sha256="f1fd8b7617762a8c7ebfebb380783f1b28f490fcc6073b541065acb7dc7ccd5d"),
+        sources_sha256="7da2eaf79500ebbe2665d23c74dce9aaed4e1d56a9ad5e6cb8bc1dced7e4be4e"),
 }
 
 

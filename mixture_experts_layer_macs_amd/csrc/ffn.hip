@@ -954,10 +954,10 @@ static bool decode_tiles(int T, int N, int k) {
 
 
 // The smallest batches (a few dispatch rows) stream 16-row weight panels:
-// gate-up up to 32 dispatch rows, down up to 16 (measured on the 2048 x 768
-// expert shape at 8, 16 and 32 rows).
+// gate-up up to 64 dispatch rows, down up to 16 (measured on the 2048 x 768
+// expert shape at 8, 16, 32, 48, 64 and 128 rows, with and without SERE).
 #ifndef MOE_SKINNY_ROWS_GU
-#define MOE_SKINNY_ROWS_GU 32
+#define MOE_SKINNY_ROWS_GU 64
 #endif
 #ifndef MOE_SKINNY_ROWS_DN
 #define MOE_SKINNY_ROWS_DN 16

@@ -51,7 +51,7 @@ FULL_Y_CASES = [
     ("qwen3_decode_b128_s1", configs.QWEN3_DECODE, 1),
     ("sweep_layer_macs_b64", configs.SWEEP_LAYER.with_(T=64, kprime=2), 0),
     ("sweep_layer_b1", configs.SWEEP_LAYER.with_(T=1, kprime=1), 0),
-    # a few dispatch rows: the 16-row weight panel kernels (gate-up up to 32
+    # a few dispatch rows: the 16-row weight panel kernels (gate-up up to 64
     # rows, down up to 16), on both sides of the thresholds
     ("sweep_layer_b2", configs.SWEEP_LAYER.with_(T=2, kprime=0), 1),
     ("sweep_layer_b4", configs.SWEEP_LAYER.with_(T=4, kprime=0), 2),
@@ -59,6 +59,7 @@ FULL_Y_CASES = [
     ("mid_bf16_skinny_t4_h768", _mid_bf16(T=4, H=768, I=384, gamma=0.7), 9),
     ("mid_bf16_t5", _mid_bf16(T=5), 10),
     ("mid_bf16_t9", _mid_bf16(T=9), 12),
+    ("mid_bf16_t17", _mid_bf16(T=17), 15),
     # long reductions in the 16-row panel kernels (32 K slices)
     ("mid_bf16_skinny_h4096", _mid_bf16(T=3, H=4096, I=512, k=2), 13),
     ("mid_bf16_skinny_i4096", _mid_bf16(T=2, H=512, I=4096), 14),
