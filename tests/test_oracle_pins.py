@@ -61,8 +61,10 @@ def test_hand_layer_case(case):
                          ids=lambda c: c["name"])
 def test_hand_capacity_case(case):
     slot_in = np.array(case["slot_in"], dtype=np.int32)
+    # router ranks: the post-SERE slots unless the case moved some
+    topk = np.array(case.get("topk", case["slot_in"]), dtype=np.int32)
     out, flags, load, _ = O.capacity_assign(
-        slot_in, slot_in, np.array(case["fallback"], dtype=np.int32),
+        topk, slot_in, np.array(case["fallback"], dtype=np.int32),
         case["w_q"], case["cap_q"], case["N"], case["R"], case["group"])
     np.testing.assert_array_equal(out, case["expect"]["slot_out"])
     np.testing.assert_array_equal(flags, case["expect"]["flags"])
@@ -257,23 +259,27 @@ def _check_invariants(topk, gates, fb, slot_in, wq, cap, out, flags, load,
 @settings(max_examples=80, deadline=None)
 @given(seed=st.integers(0, 100_000), gamma=st.sampled_from([0.3, 0.7, 1.0, 1.5, math.inf]),
        R=st.integers(0, 3), group=st.sampled_from([2, 3, 6]),
-       frac=st.sampled_from([0.0, 0.5, 1.0]))
-def test_capacity_invariants(seed, gamma, R, group, frac):
+       frac=st.sampled_from([0.0, 0.5, 1.0]), sere=st.booleans())
+def test_capacity_invariants(seed, gamma, R, group, frac, sere):
     rng = np.random.default_rng(seed)
     T, N, k = 24, 6, 2
     topk, gates, fb, vis, ew = _cap_instance(rng, T, N, k, R, frac)
+    slot_in = topk
+    if sere:        # capacity after SERE (R3): K'=1, a low threshold
+        sim, prot = _sere_instance(rng, T, N, k)[1:3]
+        slot_in = O.sere_reroute(topk, 1, 0.3, sim, prot)[0]
     wq = O.token_weights_q(vis, ew)
     m = rng.integers(-1, 2, size=N)
     _, _, _, cap = O.capacities(wq, vis, T, N, k, gamma, 1.0, m)
-    out, flags, load, _ = O.capacity_assign(topk, topk, fb, wq, cap, N, R,
+    out, flags, load, _ = O.capacity_assign(topk, slot_in, fb, wq, cap, N, R,
                                             group)
-    _check_invariants(topk, gates, fb, topk, wq, cap, out, flags, load,
+    _check_invariants(topk, gates, fb, slot_in, wq, cap, out, flags, load,
                       N, k, R, group)
     if cap is not None:
         # every expert with a proposer keeps at least its first one (C >= 1)
-        for j in set(topk.ravel().tolist()):
+        for j in set(slot_in.ravel().tolist()):
             assert load[j] > 0 or all(
-                wq[t] == 0 for t, s in np.argwhere(topk == j))
+                wq[t] == 0 for t, s in np.argwhere(slot_in == j))
 
 
 def test_floor_keeps_union_at_decode():
