@@ -18,6 +18,12 @@ inline int launch_status() {
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Index of the current device, or -1 if there is none below 64.
+inline int current_device() {
+  int dev = 0;
+  return hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 ? dev : -1;
+}
+
 // Compute units of the current device (cached per device; 256 if unknown).
 inline int cu_count() {
   static int cus[64] = {0};

@@ -20,6 +20,7 @@
 // L2.  The grid is an upper bound sized on the host (no device read-back);
 // surplus workgroups exit after reading the expert offsets.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -783,13 +784,15 @@ static int launch_gemm_dma(const Args& a, int rows_cap, hipStream_t s) {
   constexpr size_t ring = (static_cast<size_t>(S) * BM + static_cast<size_t>(SB) * BN) * BK * 2;
   constexpr size_t epi = MODE == DOWN ? static_cast<size_t>(BM) * (BN * 2 + 16) : 0;
   constexpr size_t lds = ring > epi ? ring : epi;
-  static bool attr_set = false;
-  if (!attr_set) {
+  // the LDS limit is a per-device function attribute: set once per device
+  static std::atomic<bool> attr_set[64];
+  const int dev = current_device();
+  if (dev < 0 || !attr_set[dev].load(std::memory_order_acquire)) {
     if (hipFuncSetAttribute(
             reinterpret_cast<const void*>(gemm_dma_kernel<MODE, BM, BN, BK, WM, WN, S, WPE, SB>),
             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)) != hipSuccess)
       return MOE_EHIP;
-    attr_set = true;
+    if (dev >= 0) attr_set[dev].store(true, std::memory_order_release);
   }
   // tiles <= sum over active experts of (rows / BM + 1), and at most
   // min(N, rows) experts are active
@@ -806,14 +809,15 @@ static int launch_gemm_dual(Args a, int rows_cap, hipStream_t s) {
   constexpr size_t la = static_cast<size_t>(SA) * (BMA + BN) * BK * 2;
   constexpr size_t lb = static_cast<size_t>(SB) * (BMB + BN) * BK * 2;
   constexpr size_t lds = la > lb ? la : lb;
-  static bool attr_set = false;
+  static std::atomic<bool> attr_set[64];
   const void* fn =
       reinterpret_cast<const void*>(gemm_dual_kernel<MODE, BN, BK, BMA, SA, BMB, SB, WPE>);
-  if (!attr_set) {
+  const int dev = current_device();
+  if (dev < 0 || !attr_set[dev].load(std::memory_order_acquire)) {
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(lds)) != hipSuccess)
       return MOE_EHIP;
-    attr_set = true;
+    if (dev >= 0) attr_set[dev].store(true, std::memory_order_release);
   }
   a.dual_limit = WPE * cu_count();
   constexpr int BMIN = BMA < BMB ? BMA : BMB;
@@ -1135,3 +1139,4 @@ extern "C" int moe_expert_ffn(const void* x, const int32_t* row_token,
   return moe_ffn_down(workspace, expert_offsets, w2, T, N, k, H, I, dtype,
                       out_rows, stream);
 }
+

@@ -66,6 +66,12 @@ FULL_Y_CASES = [
     # one expert with more than 16 rows: several 16-row token tiles
     ("mid_bf16_skinny_k1_t30", _mid_bf16(T=30, k=1, R=2, skew_expert0=10.0,
                                                 gamma=math.inf), 11),
+    # the 48-layer sweep's layer at batches 1 and 128, half the tokens
+    # visual, without SERE and with K'=2 (MACS on in all four)
+    ("sweep_b1_vis05_off", configs.SWEEP_LAYER.with_(T=1, kprime=0), 0),
+    ("sweep_b1_vis05_k2", configs.SWEEP_LAYER.with_(T=1, kprime=2), 0),
+    ("sweep_b128_vis05_off", configs.SWEEP_LAYER.with_(T=128, kprime=0), 0),
+    ("sweep_b128_vis05_k2", configs.SWEEP_LAYER.with_(T=128, kprime=2), 0),
 ]
 
 
@@ -139,6 +145,81 @@ def test_routing_parity(name, wl, seed, fused):
     rt = O.layer_routing(inp)
     g = run_gpu_layer(inp, tokens_out=False, fused=fused)
     assert_routing_equal(g, rt, inp)
+
+
+SWEEP_POINTS = [(T, frac, kp) for T in (1, 8, 32, 64, 128, 256)
+                for frac in (0.1, 0.5, 0.9) for kp in (0, 1, 2)]
+
+
+@pytest.mark.parametrize("T,frac,kp", SWEEP_POINTS,
+                         ids=[f"b{T}_vis{f}_k{kp}" for T, f, kp in SWEEP_POINTS])
+def test_sweep_point_routing_every_layer(T, frac, kp):
+    """Every point of the 48-layer decode sweep (batch x visual fraction x
+    SERE setting, MACS gamma 1.25, R 8), every layer with its own logits,
+    similarity and protection matrices, routed as the sweep routes it (the
+    fused launch) and compared bit for bit with the oracle: ids, post-SERE
+    slots, final slots, flags, loads, capacities and dispatch maps, so the
+    union sizes the sweep reports are the oracle's too."""
+    wl = configs.SWEEP_LAYER.with_(T=T, visual=f"frac:{frac}", kprime=kp)
+    unions = np.zeros(3)
+    for layer in range(wl.layers):
+        inp = synth.make_inputs(wl, 0, layer=layer, weights=False)
+        rt = O.layer_routing(inp)
+        g = run_gpu_layer(inp, tokens_out=False)
+        assert_routing_equal(g, rt, inp)
+        unions += (rt["union_baseline"], rt["union_sere"], rt["union_final"])
+    u = unions / wl.layers
+    say(f"sweep point b{T} vis{frac} K'={kp}: {wl.layers} layers bit-exact, "
+        f"mean unions {u[0]:.2f} / {u[1]:.2f} / {u[2]:.2f}")
+
+
+def _hand_inputs(c):
+    N = c["N"]
+    return dict(
+        T=c["T"], H=256, N=N, k=c["k"], I=128, dtype="bf16", R=c["R"],
+        group=c["group"], gamma=math.inf if c["gamma"] == "inf" else float(c["gamma"]),
+        lam=float(c["lam"]), kprime=c["kprime"], rho=float(c["rho"]),
+        logits=np.array(c["logits"], dtype=np.float32),
+        is_visual=np.array(c["is_visual"], dtype=np.uint8),
+        entropy_w=np.array(c["entropy_w"], dtype=np.float32),
+        modality=np.array(c["modality"], dtype=np.int8),
+        sim=np.array(c.get("sim", np.eye(N)), dtype=np.float32),
+        prot=np.array(c.get("prot", np.zeros((N, N))), dtype=np.uint8))
+
+
+def _hand_cases():
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden",
+                           "hand_cases.json")) as f:
+        return json.load(f)["layer_cases"]
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+@pytest.mark.parametrize("case", _hand_cases(), ids=lambda c: c["name"])
+def test_hand_cases_on_gpu(case, fused):
+    """The hand-worked routing cases (values derived by hand from the pages
+    and the readings) reproduced by the HIP path directly."""
+    inp = _hand_inputs(case)
+    say(f"hand case {case['name']} fused={fused}")
+    g = run_gpu_layer(inp, tokens_out=False, fused=fused)
+    M = int(g["expert_offsets"][-1])
+    got = dict(g, row_token=g["row_token"][:M], row_slot=g["row_slot"][:M],
+               slot_expert=g["slot_expert"])
+    for key, want in case["expect"].items():
+        if key in ("gate_closed_form", "w_q"):
+            continue
+        if key == "r_v":
+            assert g["r_v"] == want, key
+        elif key == "cap_q" and case["gamma"] == "inf":
+            continue
+        elif key.startswith("union_"):
+            src = {"union_baseline": g["topk_ids"], "union_sere": g["slot_sere"],
+                   "union_final": g["slot_expert"]}[key]
+            assert len(set(src[src >= 0].ravel().tolist())) == want, key
+        else:
+            np.testing.assert_array_equal(np.asarray(got[key]), np.array(want),
+                                          err_msg=key)
 
 
 FUSED_CASES = [
