@@ -23,6 +23,9 @@
  * Conventions shared by every entry point
  *   - Every array argument is a DEVICE pointer owned by the caller; the
  *     library never allocates, frees or keeps pointers after returning.
+ *     The only state it keeps is per device and set on first use: the
+ *     compute-unit count, whether a GEMM kernel's LDS limit has been set,
+ *     and the device address of moe_expert_ffn_noalloc's fixed buffer.
  *   - Arrays are dense and row-major; "[T,k]" means T rows of k elements.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
  *     void*; NULL = the default stream).  No entry point synchronises with
@@ -32,7 +35,9 @@
  *     error nothing is enqueued and the call returns:
  *        MOE_EINVAL  a required pointer is NULL or a size is out of range,
  *        MOE_EUNSUP  unsupported element type,
- *        MOE_EHIP    the HIP runtime reported a launch error.
+ *        MOE_EHIP    the HIP runtime reported a launch error,
+ *        MOE_ESCRATCH  the no-allocation variant's fixed buffer is too
+ *                    small for the call.
  *   - T == 0 is valid and enqueues nothing.
  *   - Limits: 1 <= N <= 1024 experts, 1 <= k <= N, 0 <= R <= N - k,
  *     T <= 2^20 tokens.
@@ -60,7 +65,8 @@
 extern "C" {
 #endif
 
-enum { MOE_OK = 0, MOE_EINVAL = -1, MOE_EUNSUP = -2, MOE_EHIP = -3 };
+enum { MOE_OK = 0, MOE_EINVAL = -1, MOE_EUNSUP = -2, MOE_EHIP = -3,
+       MOE_ESCRATCH = -4 };
 
 /* element type of x, expert weights, intermediates, out_rows and y */
 enum { MOE_F32 = 0, MOE_BF16 = 1 };
@@ -342,6 +348,30 @@ int moe_ffn_gate_up(const void* x, const int32_t* row_token,
 int moe_ffn_down(const void* h, const int32_t* expert_offsets, const void* w2,
                  int T, int N, int k, int H, int I, int dtype, void* out_rows,
                  void* stream);
+
+/*
+ * moe_expert_ffn_noalloc -- moe_expert_ffn for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): same arguments, same kernels and the
+ * same results bit for bit, minus the workspace.  h is kept in a fixed
+ * device-resident buffer of MOE_FFN_NOALLOC_MAX_BYTES that the library
+ * holds on every GPU it runs on until the process ends; the call itself
+ * allocates and frees nothing.
+ * Limit: moe_ffn_workspace_size(T, N, k, H, I, dtype) must not exceed
+ * MOE_FFN_NOALLOC_MAX_BYTES (32 MiB: every decode batch of the shapes
+ * above, e.g. T*k*I*2 bytes of bf16 h up to 16 Mi elements), else the call
+ * returns MOE_ESCRATCH and enqueues nothing.
+ * Every call on one GPU uses that GPU's one buffer: calls that may overlap
+ * on one GPU (several streams, or several host threads) race and must be
+ * serialised by the caller.  Nothing in the buffer needs to start at zero.
+ * Errors: as moe_expert_ffn, plus MOE_ESCRATCH, and MOE_EHIP when the
+ * runtime cannot report the buffer's device address.
+ */
+#define MOE_FFN_NOALLOC_MAX_BYTES (32u << 20)
+int moe_expert_ffn_noalloc(const void* x, const int32_t* row_token,
+                           const int32_t* expert_offsets, const void* w13,
+                           const void* w2, int T, int N, int k, int H, int I,
+                           int dtype, void* out_rows, void* stream);
 
 /*
  * moe_combine -- gate-weighted combine (MACS §3.1 Eq. 1):

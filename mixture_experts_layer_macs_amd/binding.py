@@ -21,14 +21,16 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_macs.so")
 
-MOE_OK, MOE_EINVAL, MOE_EUNSUP, MOE_EHIP = 0, -1, -2, -3
+MOE_OK, MOE_EINVAL, MOE_EUNSUP, MOE_EHIP, MOE_ESCRATCH = 0, -1, -2, -3, -4
+FFN_NOALLOC_MAX_BYTES = 32 << 20
 MOE_F32, MOE_BF16 = 0, 1
 FLAG_SERE, FLAG_MACS, FLAG_DROP = 1, 2, 4
 WEIGHT_ONE = 65536
 
 _ERR = {MOE_EINVAL: "MOE_EINVAL (bad argument)",
         MOE_EUNSUP: "MOE_EUNSUP (unsupported type or shape)",
-        MOE_EHIP: "MOE_EHIP (HIP launch error)"}
+        MOE_EHIP: "MOE_EHIP (HIP launch error)",
+        MOE_ESCRATCH: "MOE_ESCRATCH (larger than the fixed no-allocation buffer)"}
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -58,6 +60,8 @@ _SIGS = {
     "moe_ffn_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "moe_expert_ffn": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P,
                             _P, _SZ, _P]),
+    "moe_expert_ffn_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                                    _P, _P]),
     "moe_ffn_gate_up": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
     "moe_ffn_down": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
     "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P]),
@@ -347,6 +351,27 @@ def moe_expert_ffn(x, row_token, expert_offsets, w13, w2, k, workspace,
         T, N, k, H, I, dt, _dev(out_rows, x.dtype, "out_rows", (T * k, H)),
         _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
     _check(rc, "moe_expert_ffn")
+    return out_rows
+
+
+def moe_expert_ffn_noalloc(x, row_token, expert_offsets, w13, w2, k,
+                           out_rows=None):
+    """moe_expert_ffn with h in the library's fixed device buffer (no
+    workspace; at most FFN_NOALLOC_MAX_BYTES of h)."""
+    T, H = x.shape
+    N, I2, H2 = w13.shape
+    I = I2 // 2
+    if H2 != H or tuple(w2.shape) != (N, H, I):
+        raise ValueError("expert weight shapes do not match x")
+    if out_rows is None:
+        out_rows = _empty((T * k, H), x.dtype, x)
+    rc = _lib.moe_expert_ffn_noalloc(
+        _dev(x, x.dtype, "x"), _dev(row_token, torch.int32, "row_token", (T * k,)),
+        _dev(expert_offsets, torch.int32, "expert_offsets", (N + 1,)),
+        _dev(w13, x.dtype, "w13"), _dev(w2, x.dtype, "w2"),
+        T, N, k, H, I, _elem(x.dtype),
+        _dev(out_rows, x.dtype, "out_rows", (T * k, H)), _stream())
+    _check(rc, "moe_expert_ffn_noalloc")
     return out_rows
 
 

@@ -21,6 +21,7 @@
 // surplus workgroups exit after reading the expert offsets.
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -1140,3 +1141,46 @@ extern "C" int moe_expert_ffn(const void* x, const int32_t* row_token,
                       out_rows, stream);
 }
 
+// ------------------------------------------------------- no allocation
+// h of moe_expert_ffn_noalloc lives in this file-scope device array: each
+// GPU the library runs on holds its own copy until the process ends.  Host
+// code never passes the array's name to a kernel (on the host it is only a
+// stand-in symbol); it asks the runtime once per device for the array's
+// device address and passes that, as moe_expert_ffn passes its workspace.
+static __device__ __align__(256) unsigned char scratch[MOE_FFN_NOALLOC_MAX_BYTES];
+
+// Device address of `scratch` on the current device, looked up on the first
+// call made with that device current; nullptr if the lookup fails.
+static void* scratch_on_current_device() {
+  static std::atomic<void*> addr[64];
+  static std::mutex lookup;
+  const int dev = current_device();
+  if (dev < 0) return nullptr;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> g(lookup);
+  p = addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+  addr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
+extern "C" int moe_expert_ffn_noalloc(const void* x, const int32_t* row_token,
+                                      const int32_t* expert_offsets, const void* w13,
+                                      const void* w2, int T, int N, int k, int H, int I,
+                                      int dtype, void* out_rows, void* stream) {
+  const int st = check_ffn_shape(T, N, k, H, I, dtype);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (moe_ffn_workspace_size(T, N, k, H, I, dtype) > MOE_FFN_NOALLOC_MAX_BYTES)
+    return MOE_ESCRATCH;
+  void* h = scratch_on_current_device();
+  if (!h) return MOE_EHIP;
+  // h needs no clearing: the gate-up GEMM writes every row the down GEMM reads
+  const int r = moe_ffn_gate_up(x, row_token, expert_offsets, w13, T, N, k, H,
+                                I, dtype, h, stream);
+  if (r != MOE_OK) return r;
+  return moe_ffn_down(h, expert_offsets, w2, T, N, k, H, I, dtype, out_rows,
+                      stream);
+}

@@ -178,3 +178,32 @@ def test_similarity_host_checks(lib):
     assert call(fake, 8, 64, 7, fake, fake, 1 << 20, None) == -2
     assert call(None, 8, 64, 1, fake, fake, 1 << 20, None) == -1
     assert call(fake, 8, 64, 1, fake, fake, 8, None) == -1    # workspace short
+
+
+def test_noalloc_ffn_host_checks(lib):
+    P = ctypes.c_void_p
+    fake = P(0x1000)   # never dereferenced: every call below fails its checks
+    f = lib.moe_expert_ffn_noalloc
+    f.argtypes = [P] * 5 + [ctypes.c_int] * 6 + [P, P]
+    ws = lib.moe_ffn_workspace_size
+    ws.restype = ctypes.c_size_t
+    limit = 32 << 20
+    # 8192 tokens of the 2048 x 768 shape need 96 MiB of bf16 h: refused
+    assert ws(8192, 128, 8, 2048, 768, 1) > limit
+    assert f(fake, fake, fake, fake, fake, 8192, 128, 8, 2048, 768, 1, fake,
+             None) == -4
+    # the largest batch that fits (2730 tokens: 33 546 240 bytes of h) is
+    # accepted by the size check (not called here: it would launch); one
+    # token more is refused
+    T_max = limit // (8 * 768 * 2)
+    assert ws(T_max, 128, 8, 2048, 768, 1) <= limit
+    assert ws(T_max + 1, 128, 8, 2048, 768, 1) > limit
+    assert f(fake, fake, fake, fake, fake, T_max + 1, 128, 8, 2048, 768, 1,
+             fake, None) == -4
+    # the usual shape and argument checks come first
+    assert f(fake, fake, fake, fake, fake, 4, 8, 2, 200, 768, 1, fake,
+             None) == -2
+    assert f(fake, fake, fake, fake, fake, 4, 8, 9, 2048, 768, 1, fake,
+             None) == -1
+    assert f(None, None, None, None, None, 0, 8, 2, 2048, 768, 1, None,
+             None) == 0                                    # T = 0: nothing
