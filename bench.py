@@ -9,10 +9,18 @@ pass of the whole path over one batch; inputs are resident in HBM before the
 timed region.  Two copies of the expert weights alternate between steps so
 the weight stream is not served from the 256 MB Infinity Cache.
 
-Prints one JSON line: whole-layer tokens/s (value), ms per step, the
-roofline of the dominant kernel (HBM-bound gate-up GEMM for decode,
-MFMA-bound for prefill) timed with HIP events on the launch stream, and the
-CPU oracle timed on a bounded sample of the same workload.
+Prints one JSON line: whole-layer tokens/s (value) and µs per decode step,
+the roofline of the dominant kernel (the HBM-bound gate-up GEMM), the
+whole step's HBM fraction from the per-token byte model, per-kernel
+fractions, p10/p50/p90 of the graph-replayed step, the largest
+entropy-weighted expert load (the straggler that sets an expert-parallel
+layer's latency), and the CPU oracle timed on a bounded sample of the same
+workload.  The same line carries the prefill half of the metric
+("prefill": the 8192-token multimodal prefill with MACS, tokens/s and the
+MFMA fractions of both expert GEMMs), the tiny fp32 layer and the
+Mixtral-shaped decode and prefill layers (also with re-routing off, R = 0:
+capacity plus drop only), each timed in its own regions.  --only times the
+named workload alone.
 """
 from __future__ import annotations
 
@@ -109,6 +117,11 @@ def parse():
                    help="time the SERE similarity calibration of one layer "
                         "(256 calibration tokens through all 128 experts, then "
                         "the Frobenius similarity) and exit")
+    p.add_argument("--only", action="store_true",
+                   help="time the named workload alone (by default the "
+                        "decode headline also times the 8192-token multimodal "
+                        "prefill, the tiny fp32 layer and the Mixtral-shaped "
+                        "layers)")
     p.add_argument("--separate-routing", action="store_true",
                    help="route with the four separate calls instead of the "
                         "single fused launch")
@@ -121,9 +134,13 @@ def cpu_baseline(inp, budget_s):
     from oracle import moe_oracle as O
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        cores = 1
+        blas = 1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except Exception:
+        affinity = os.cpu_count() or 1
     t0 = time.perf_counter()
     n = 0
     t_route = t_ffn = 0.0
@@ -140,11 +157,17 @@ def cpu_baseline(inp, budget_s):
             break
     el = time.perf_counter() - t0
     return dict(value=round(n * inp["T"] / el, 3), unit="tokens/s",
-                cores=int(cores), kind="oracle",
+                cores=int(blas), kind="oracle",
+                cores_detail=dict(routing_threads=1, ffn_blas_threads=int(blas),
+                                  os_cpu_count=os.cpu_count(),
+                                  affinity=int(affinity)),
+                routing_s_per_step=round(t_route / n, 4),
+                ffn_s_per_step=round(t_ffn / n, 4),
                 sample=(f"{n} full layer step(s) of the same workload "
                         f"(T={inp['T']}): routing {t_route / n:.3f} s/step "
                         f"single-threaded Python, FFN+combine "
-                        f"{t_ffn / n:.3f} s/step fp64 numpy"))
+                        f"{t_ffn / n:.3f} s/step fp64 numpy on "
+                        f"{int(blas)} BLAS threads"))
 
 
 
@@ -411,6 +434,216 @@ def run_similarity(args):
                                    "bytes_per_launch": nbytes}}), flush=True)
 
 
+def _q(xs, q):
+    return float(np.percentile(np.asarray(xs), q))
+
+
+def measure(wl, args, with_cpu=False):
+    """Time one workload: a step is one pass of route -> SERE -> capacity ->
+    dispatch -> gate-up -> down -> combine over one batch, inputs resident
+    in HBM.  Returns a dict of step times, in-step kernel times, routing
+    statistics and roofline figures."""
+    import torch
+    from mixture_experts_layer_macs_amd import binding as B
+    from mixture_experts_layer_macs_amd import synth
+    from mixture_experts_layer_macs_amd.staging import to_device, torch_elem_dtype
+
+    dev = torch.device("cuda:0")
+    print(f"[bench] {wl.name}: generating inputs", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(wl, args.seed)
+    d = to_device(inp, dev)
+    w13s = [d["w13"]] + [d["w13"].clone() for _ in range(args.copies - 1)]
+    w2s = [d["w2"]] + [d["w2"].clone() for _ in range(args.copies - 1)]
+    T, H, N, k, I, R = wl.T, wl.H, wl.N, wl.k, wl.I, wl.R
+    lay = B.Layer(T, H, N, k, I, R, torch_elem_dtype(wl.dtype), dev)
+    h = torch.empty((T * k, I), dtype=torch_elem_dtype(wl.dtype), device=dev)
+    decode = wl.kprime > 0 or T * k <= 32 * N
+    fused = lay.can_fuse and not args.separate_routing
+    steps = args.steps if decode else max(5, args.steps // 2)
+
+    def gate_up(i):
+        B.moe_ffn_gate_up(d["x"], lay.disp["row_token"],
+                          lay.disp["expert_offsets"], w13s[i % len(w13s)], k, h)
+
+    def down(i):
+        B.moe_ffn_down(h, lay.disp["expert_offsets"], w2s[i % len(w2s)], T, k,
+                       lay.out_rows)
+
+    def step(i, skip=()):
+        lay.routing(d["logits"], d["is_visual"], d["entropy_w"], d["modality"],
+                    d["sim"], d["prot"], wl.kprime, wl.rho, wl.gamma, wl.lam,
+                    wl.group, fused=fused)
+        if "gate_up" not in skip:
+            gate_up(i)
+        if "down" not in skip:
+            down(i)
+        B.moe_combine(lay.out_rows, lay.disp["slot_row"], lay.topk_gates, lay.y)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    graph_cache = {}
+
+    def graphs_for(skip):
+        if skip not in graph_cache:
+            gs = []
+            cap_stream = torch.cuda.Stream()
+            for c in range(len(w13s)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap_stream):
+                    step(c, skip)
+                gs.append(g)
+            graph_cache[skip] = gs
+        return graph_cache[skip]
+
+    def timed(skip=(), graph=False, per_step=False):
+        """Mean ms per step over `steps` steps with HIP events at the two ends
+        of the region (and, with per_step, one event between replays).
+        Eager: a spin kernel holds the stream while the host queues the
+        steps, so they then run back to back.  Graph: the step is captured
+        once per weight copy and replayed."""
+        ev = [torch.cuda.Event(enable_timing=True)
+              for _ in range(steps + 1 if per_step else 2)]
+        if graph:
+            gs = graphs_for(skip)
+            for i in range(args.warmup):
+                gs[i % len(gs)].replay()
+            torch.cuda.synchronize()
+            ev[0].record()
+            for i in range(steps):
+                gs[i % len(gs)].replay()
+                if per_step:
+                    ev[i + 1].record()
+            ev[-1].record()
+        else:
+            torch.cuda.synchronize()
+            hold_gpu(steps * 1e-4 + 2e-3)
+            ev[0].record()
+            for i in range(steps):
+                step(i, skip)
+            ev[-1].record()
+        torch.cuda.synchronize()
+        if per_step:
+            return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+        return ev[0].elapsed_time(ev[-1]) / steps
+
+    print(f"[bench] {wl.name}: timed steps", file=sys.stderr, flush=True)
+    t_wall = time.perf_counter()
+    eager_ms = timed()
+    t_wall = time.perf_counter() - t_wall
+    per_step = None if args.no_graph else timed(graph=True, per_step=True)
+    graph_ms = None if per_step is None else float(np.mean(per_step))
+    use_graph = not args.no_graph
+
+    # In-step duration of each expert GEMM: the step time minus the time of
+    # the same step with that kernel left out (same timing mode), the median
+    # over DIFF_REPS alternating pairs of timed regions.  An event pair around
+    # one launch would add the dispatch gap after the first event.
+    def in_step_ms(name):
+        return float(np.median([timed((), use_graph) - timed((name,), use_graph)
+                                for _ in range(DIFF_REPS)]))
+    gu_ms = in_step_ms("gate_up")
+    dn_ms = in_step_ms("down")
+
+    off = lay.disp["expert_offsets"].cpu().numpy()
+    counts = np.diff(off)
+    M = int(off[-1])
+    U = int((counts > 0).sum())
+    el = 2 if wl.dtype == "bf16" else 4
+    stats = lay.cap["stats"].cpu().numpy()
+    load_q = lay.cap["load_q"].cpu().numpy().astype(np.float64) / 65536.0
+    topk = lay.topk_ids.cpu().numpy()
+    slot_sere = (lay.slot_sere if wl.kprime else lay.topk_ids).cpu().numpy()
+    best_ms = eager_ms if graph_ms is None else min(eager_ms, graph_ms)
+    out = dict(
+        workload=wl.name, T=T, H=H, N=N, k=k, I=I, dtype=wl.dtype,
+        step_us=round(best_ms * 1e3, 2),
+        tokens_per_s=round(T / (best_ms * 1e-3), 1),
+        eager_us=round(eager_ms * 1e3, 2),
+        graph_us=None if graph_ms is None else round(graph_ms * 1e3, 2),
+        mode="eager" if graph_ms is None or eager_ms <= graph_ms else "hip-graph",
+        steps=steps,
+        routing="fused" if fused else "separate",
+        union_baseline=int(len(np.unique(topk))),
+        union_sere=int(len(np.unique(slot_sere))),
+        union_final=U, kept_rows=M,
+        dropped=int(stats[2]), macs_rerouted=int(stats[3]),
+        # Eq. 2 straggler proxy: the largest entropy-weighted expert load
+        max_load_tokens=round(float(load_q.max()), 4),
+        mean_active_load_tokens=round(float(load_q[load_q > 0].mean()), 4)
+        if (load_q > 0).any() else 0.0,
+        kernels_us={"gate_up_swiglu": round(gu_ms * 1e3, 2),
+                    "down": round(dn_ms * 1e3, 2),
+                    "routing_combine_and_gaps": round((best_ms - gu_ms - dn_ms) * 1e3, 2)},
+        wall_s=round(t_wall, 3),
+    )
+    if per_step is not None:
+        out["graph_step_us_p10_p50_p90"] = [round(_q(per_step, q) * 1e3, 2)
+                                           for q in (10, 50, 90)]
+    if decode:
+        # algorithmic bytes: every active expert's weights once, x once per
+        # token, h written by gate-up and read by down, out rows
+        gu_bytes = U * 2 * I * H * el + T * H * el + M * I * el
+        dn_bytes = U * H * I * el + M * I * el + M * H * el
+        step_bytes = (U * 3 * H * I * el + 2 * T * H * el + T * N * 4
+                      + (N * N * 5 if wl.kprime else 0))
+        gbs = lambda b, ms: b / (ms * 1e-3) / 1e9
+        out["roofline"] = dict(
+            bound="hbm", achieved=round(gbs(gu_bytes, gu_ms), 1),
+            peak=HBM_PEAK_GBS, unit="GB/s",
+            frac=round(gbs(gu_bytes, gu_ms) / HBM_PEAK_GBS, 4),
+            traffic=counted_traffic(wl.name), kernel="gate_up_swiglu",
+            kernel_us=round(gu_ms * 1e3, 2), bytes_per_launch=int(gu_bytes))
+        out["kernels_roofline"] = {
+            "gate_up_swiglu": dict(GBps=round(gbs(gu_bytes, gu_ms), 1),
+                                   frac=round(gbs(gu_bytes, gu_ms) / HBM_PEAK_GBS, 4),
+                                   bytes=int(gu_bytes)),
+            "down": dict(GBps=round(gbs(dn_bytes, dn_ms), 1),
+                         frac=round(gbs(dn_bytes, dn_ms) / HBM_PEAK_GBS, 4),
+                         bytes=int(dn_bytes))}
+        out["step_roofline"] = dict(
+            bound="hbm", bytes_per_step=int(step_bytes),
+            achieved=round(gbs(step_bytes, best_ms), 1), peak=HBM_PEAK_GBS,
+            unit="GB/s", frac=round(gbs(step_bytes, best_ms) / HBM_PEAK_GBS, 4),
+            bytes_model="union_final*3*H*I*el + 2*T*H*el + T*N*4 (+ N*N*5 with SERE)")
+    else:
+        peak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_VALU_PEAK_TFLOPS
+        bound = "mfma" if wl.dtype == "bf16" else "alu"
+        gu_fl, dn_fl = 4.0 * M * H * I, 2.0 * M * H * I
+        tf = lambda f, ms: f / (ms * 1e-3) / 1e12
+        out["roofline"] = dict(
+            bound=bound, achieved=round(tf(gu_fl, gu_ms), 2), peak=peak,
+            unit="TFLOP/s", frac=round(tf(gu_fl, gu_ms) / peak, 4),
+            traffic=counted_traffic(wl.name), kernel="gate_up_swiglu",
+            kernel_us=round(gu_ms * 1e3, 2), flops_per_launch=gu_fl)
+        out["kernels_roofline"] = {
+            "gate_up_swiglu": dict(TFLOPs=round(tf(gu_fl, gu_ms), 2),
+                                   frac=round(tf(gu_fl, gu_ms) / peak, 4),
+                                   flops=gu_fl),
+            "down": dict(TFLOPs=round(tf(dn_fl, dn_ms), 2),
+                         frac=round(tf(dn_fl, dn_ms) / peak, 4), flops=dn_fl)}
+        out["step_roofline"] = dict(
+            bound=bound, flops_per_step=gu_fl + dn_fl,
+            achieved=round(tf(gu_fl + dn_fl, best_ms), 2), peak=peak,
+            unit="TFLOP/s", frac=round(tf(gu_fl + dn_fl, best_ms) / peak, 4))
+    if with_cpu and not args.no_cpu_baseline:
+        print(f"[bench] {wl.name}: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    del graph_cache, w13s, w2s, d, lay, h
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def _brief(m):
+    keys = ("step_us", "tokens_per_s", "graph_step_us_p10_p50_p90", "kernels_us",
+            "kernels_roofline", "step_roofline", "union_baseline", "union_sere",
+            "union_final", "kept_rows", "dropped", "macs_rerouted",
+            "max_load_tokens", "mean_active_load_tokens", "mode", "routing")
+    return {"workload": m["workload"], **{k: m[k] for k in keys if k in m}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -442,178 +675,61 @@ def main():
     from mixture_experts_layer_macs_amd import build as _build
     if not os.path.exists(_build.LIB):
         _build.build()
-    from mixture_experts_layer_macs_amd import binding as B
-    from mixture_experts_layer_macs_amd import configs, synth
-    from mixture_experts_layer_macs_amd.staging import (elem_tensor, to_device,
-                                                        torch_elem_dtype)
+    from mixture_experts_layer_macs_amd import configs
+    torch.cuda.set_device(0)
 
     wl = configs.WORKLOADS[args.workload]
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    print(f"[bench] generating inputs for {wl.name}", file=sys.stderr, flush=True)
-    inp = synth.make_inputs(wl, args.seed)
-    d = to_device(inp, dev)
-    w13s = [d["w13"]] + [d["w13"].clone() for _ in range(args.copies - 1)]
-    w2s = [d["w2"]] + [d["w2"].clone() for _ in range(args.copies - 1)]
-    T, H, N, k, I, R = wl.T, wl.H, wl.N, wl.k, wl.I, wl.R
-    lay = B.Layer(T, H, N, k, I, R, torch_elem_dtype(wl.dtype), dev)
-    h = torch.empty((T * k, I), dtype=torch_elem_dtype(wl.dtype), device=dev)
-    decode = wl.kprime > 0 or T * k <= 32 * N
-
-    fused = lay.can_fuse and not args.separate_routing
-
-    def gate_up(i):
-        B.moe_ffn_gate_up(d["x"], lay.disp["row_token"],
-                          lay.disp["expert_offsets"], w13s[i % len(w13s)], k, h)
-
-    def down(i):
-        B.moe_ffn_down(h, lay.disp["expert_offsets"], w2s[i % len(w2s)], T, k,
-                       lay.out_rows)
-
-    def step(i, skip=()):
-        lay.routing(d["logits"], d["is_visual"], d["entropy_w"], d["modality"],
-                    d["sim"], d["prot"], wl.kprime, wl.rho, wl.gamma, wl.lam,
-                    wl.group, fused=fused)
-        if "gate_up" not in skip:
-            gate_up(i)
-        if "down" not in skip:
-            down(i)
-        B.moe_combine(lay.out_rows, lay.disp["slot_row"], lay.topk_gates, lay.y)
-
-    print("[bench] warmup", file=sys.stderr, flush=True)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    graph_cache = {}
-
-    def timed(skip=(), graph=False):
-        """Mean ms per step over `steps` steps, HIP events at the two ends of
-        the region only.  Eager: the stream is held by a spin kernel while
-        the host queues the steps, so they then run back to back.  Graph: the
-        step is captured once per weight copy (and kept for later regions
-        with the same kernels left out) and replayed."""
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        if graph:
-            if skip not in graph_cache:
-                graphs = []
-                cap_stream = torch.cuda.Stream()
-                for c in range(len(w13s)):
-                    g = torch.cuda.CUDAGraph()
-                    with torch.cuda.graph(g, stream=cap_stream):
-                        step(c, skip)
-                    graphs.append(g)
-                graph_cache[skip] = graphs
-            graphs = graph_cache[skip]
-            for i in range(args.warmup):
-                graphs[i % len(graphs)].replay()
-            torch.cuda.synchronize()
-            e0.record()
-            for i in range(args.steps):
-                graphs[i % len(graphs)].replay()
-            e1.record()
-        else:
-            torch.cuda.synchronize()
-            hold_gpu(args.steps * 1e-4 + 2e-3)
-            e0.record()
-            for i in range(args.steps):
-                step(i, skip)
-            e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps
-
-    print("[bench] timed steps", file=sys.stderr, flush=True)
-    t_wall = time.perf_counter()
-    ms = timed()
-    t_wall = time.perf_counter() - t_wall
-    # second timed region: the same step replayed from HIP graphs (no host
-    # launch overhead between kernels)
-    graph_ms = None if args.no_graph else timed(graph=True)
-
-    # In-step duration of each expert GEMM: the step time minus the time of
-    # the same step with that kernel left out (same timing mode), as the
-    # median over DIFF_REPS alternating pairs of timed regions, since one
-    # difference of two step times carries the noise of both.  An event
-    # pair around a single kernel would add the dispatch gap after the first
-    # event to the interval.
-    use_graph = not args.no_graph
-
-    def in_step_ms(name):
-        diffs = [timed((), use_graph) - timed((name,), use_graph)
-                 for _ in range(DIFF_REPS)]
-        return float(np.median(diffs))
-
-    gu_ms = in_step_ms("gate_up")
-    dn_ms = in_step_ms("down")
-
-    off = lay.disp["expert_offsets"].cpu().numpy()
-    counts = np.diff(off)
-    M = int(off[-1])
-    U = int((counts > 0).sum())
-    el = 2 if wl.dtype == "bf16" else 4
-    stats = lay.cap["stats"].cpu().numpy()
-    topk = lay.topk_ids.cpu().numpy()
-    slot_sere = (lay.slot_sere if wl.kprime else lay.topk_ids).cpu().numpy()
-
-    if decode:
-        # gate-up kernel: every active expert's W13 once, its x rows, its h rows
-        gu_bytes = U * 2 * I * H * el + M * H * el + M * I * el
-        achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
-        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
-                    unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
-                    traffic=counted_traffic(wl.name), kernel="gate_up_swiglu",
-                    kernel_ms=round(gu_ms, 4), bytes_per_launch=int(gu_bytes))
-    else:
-        gu_flops = 2.0 * M * H * 2 * I
-        achieved = gu_flops / (gu_ms * 1e-3) / 1e12
-        peak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_VALU_PEAK_TFLOPS
-        roof = dict(bound="mfma" if wl.dtype == "bf16" else "alu",
-                    achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
-                    frac=round(achieved / peak, 4),
-                    traffic=counted_traffic(wl.name),
-                    kernel="gate_up_swiglu", kernel_ms=round(gu_ms, 4),
-                    flops_per_launch=gu_flops)
-
-    best_ms = ms if graph_ms is None else min(ms, graph_ms)
+    head = measure(wl, args, with_cpu=True)
     res = {
         "metric": METRIC,
-        "value": round(T / (best_ms * 1e-3), 1),
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": head["steps"],
         "warmup": args.warmup,
-        "ms_per_step": round(best_ms, 5),
-        "step_us": round(best_ms * 1e3, 2),
-        "eager_ms_per_step": round(ms, 5),
-        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
+        "ms_per_step": round(head["step_us"] * 1e-3, 5),
+        "step_us": head["step_us"],
+        "eager_ms_per_step": round(head["eager_us"] * 1e-3, 5),
+        "graph_ms_per_step": (None if head["graph_us"] is None
+                              else round(head["graph_us"] * 1e-3, 5)),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic (seeded; random-init weights of the stated shape)",
         "config": {
-            "workload": wl.name, "T": T, "H": H, "N": N, "k": k, "I": I,
-            "kprime": wl.kprime, "rho": wl.rho,
-            "gamma": "inf" if math.isinf(wl.gamma) else wl.gamma, "R": R,
-            "union_baseline": int(len(np.unique(topk))),
-            "union_sere": int(len(np.unique(slot_sere))),
-            "union_final": U, "kept_rows": M,
-            "dropped": int(stats[2]), "macs_rerouted": int(stats[3]),
-            "weight_copies": args.copies,
-            "routing": "fused" if fused else "separate",
-            "mode": "eager" if graph_ms is None or ms <= graph_ms else "hip-graph",
+            "workload": wl.name, "T": wl.T, "H": wl.H, "N": wl.N, "k": wl.k,
+            "I": wl.I, "kprime": wl.kprime, "rho": wl.rho,
+            "gamma": "inf" if math.isinf(wl.gamma) else wl.gamma, "R": wl.R,
+            "union_baseline": head["union_baseline"],
+            "union_sere": head["union_sere"], "union_final": head["union_final"],
+            "kept_rows": head["kept_rows"], "dropped": head["dropped"],
+            "macs_rerouted": head["macs_rerouted"],
+            "weight_copies": args.copies, "routing": head["routing"],
+            "mode": head["mode"],
         },
-        "roofline": roof,
-        "kernels_ms": {"gate_up_swiglu": round(gu_ms, 4),
-                       "down": round(dn_ms, 4)},
-        "wall_s": round(t_wall, 3),
+        "roofline": head["roofline"],
+        "step_roofline": head["step_roofline"],
+        "kernels_roofline": head["kernels_roofline"],
+        "kernels_ms": {k: round(v * 1e-3, 4) for k, v in head["kernels_us"].items()},
+        "graph_step_us_p10_p50_p90": head.get("graph_step_us_p10_p50_p90"),
+        "max_load_tokens": head["max_load_tokens"],
+        "mean_active_load_tokens": head["mean_active_load_tokens"],
+        "wall_s": head["wall_s"],
+        "cpu_baseline": head.get("cpu_baseline"),
     }
-    if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
-    else:
-        res["cpu_baseline"] = None
+    if args.workload == "qwen3_decode_b128" and not args.only:
+        # the prefill half of the metric and the other workloads, each its
+        # own timed regions after the headline ones
+        others = [("prefill", configs.MM_PREFILL),
+                  ("tiny_f32", configs.TINY_F32),
+                  ("mixtral_decode_t64", configs.MIXTRAL_DECODE),
+                  ("mixtral_prefill_t4096", configs.MIXTRAL_PREFILL),
+                  ("mixtral_prefill_t4096_drop_only",
+                   configs.MIXTRAL_PREFILL.with_(name="mixtral_prefill_t4096_r0",
+                                                 R=0))]
+        for key, owl in others:
+            res[key] = _brief(measure(owl, args))
     print(json.dumps(res), flush=True)
 
 

@@ -166,10 +166,11 @@ __device__ __forceinline__ void gemm_body(const Args& a, unsigned char* smem, in
   constexpr int STAGE = A_BYTES + B_BYTES;
   // Ring layout.  Symmetric (SB == S): stage s holds slice A then slice B.
   // Asymmetric: S stages of A, then SB stages of B, so the weights can be
-  // requested further ahead than the token rows.
+  // requested further ahead than the token rows (or, with 3 and 2, the
+  // token rows further ahead).
   constexpr bool ASYM = SB != S;
-  static_assert(!ASYM || (S == 2 && SB == 3) || (S == 3 && SB == 2),
-                "asymmetric ring: 2 and 3 stages");
+  static_assert(!ASYM || (S == 2 && SB >= 3) || (S == 3 && SB == 2),
+                "asymmetric ring: 2 A stages and 3 or more B stages, or 3 and 2");
   constexpr int A_STRIDE = ASYM ? A_BYTES : STAGE;
   constexpr int B_BASE = ASYM ? S * A_BYTES : A_BYTES;
   constexpr int B_STRIDE = ASYM ? B_BYTES : STAGE;
@@ -352,13 +353,13 @@ __device__ __forceinline__ void gemm_body(const Args& a, unsigned char* smem, in
                                                                    0, 0, 0);
         }
       };
-      if constexpr (ASYM && SB == 3) {
-        // A(0), B(0), B(1) ahead; iteration kt requests A(kt+1) then
-        // B(kt+2), so A(kt) has landed once at most the last group's B
+      if constexpr (ASYM && SB >= 3) {
+        // A(0), B(0) .. B(SB-2) ahead; iteration kt requests A(kt+1) then
+        // B(kt+SB-1), so A(kt) has landed once at most the last group's B
         // loads are outstanding, and B(kt), requested before it, too
         issue_a(0);
-        issue_b(0);
-        issue_b(1);
+#pragma unroll
+        for (int t = 0; t + 1 < SB; ++t) issue_b(t);
       } else if constexpr (ASYM) {  // the same with A and B exchanged
         issue_b(0);
         issue_a(0);
@@ -368,11 +369,11 @@ __device__ __forceinline__ void gemm_body(const Args& a, unsigned char* smem, in
         for (int t = 0; t + 1 < S; ++t) issue(t);
       }
       for (int kt = 0; kt < nk; ++kt) {
-        if constexpr (ASYM && SB == 3) {
+        if constexpr (ASYM && SB >= 3) {
           wait_vmcnt<QB>();
           wg_barrier();
           issue_a(kt + 1);
-          issue_b(kt + 2);
+          issue_b(kt + SB - 1);
         } else if constexpr (ASYM) {
           wait_vmcnt<QA>();
           wg_barrier();
@@ -570,11 +571,13 @@ void gemm_dma_kernel(Args a) {
 }
 
 // Decode gate-up with the tile height chosen on the device: tiles of BMA
-// token rows (S_A stages) when they number at most a.dual_limit, i.e. when
-// every tile gets a workgroup slot at once, else tiles of BMB rows (S_B
-// stages).  Every workgroup reads the same offsets, so all take the same
-// branch; the grid covers the larger tile count.
-template <int MODE, int BN, int BK, int BMA, int SA, int BMB, int SB, int WPE>
+// token rows (SA token-row stages, SAB weight stages) when they number at
+// most a.dual_limit, i.e. when every tile gets a workgroup slot at once,
+// else tiles of BMB rows (SB and SBB stages).  Every workgroup reads the
+// same offsets, so all take the same branch; the grid covers the larger
+// tile count.
+template <int MODE, int BN, int BK, int BMA, int SA, int SAB, int BMB, int SB, int SBB,
+          int WPE>
 __global__ __launch_bounds__(4 * MOE_WAVE)
 __attribute__((amdgpu_waves_per_eu(1, WPE)))
 void gemm_dual_kernel(Args a) {
@@ -604,21 +607,37 @@ void gemm_dual_kernel(Args a) {
     // leaves LDS for more ring stages: more weight bytes in flight for the
     // same weight stream.  (Deepening only the small tiles of a launch that
     // also has large ones made the large ones finish later.)
-    constexpr int RING = SA * (BMA + BN) * BK * 2;  // the LDS of the launch
-    constexpr int S32 = RING / ((32 + BN) * BK * 2), S64 = RING / ((64 + BN) * BK * 2);
-    if constexpr (BMA > 64 && S32 > SA && S64 >= SA) {
-      if (most_rows <= 32) {
-        gemm_tile<MODE, 32, BN, BK, 1, 4, (S32 < 8 ? S32 : 8)>(a, smem, cum);
-        return;
+    constexpr int RING = (SA * BMA + SAB * BN) * BK * 2;  // the LDS of the launch
+    if constexpr (SA == SAB) {
+      constexpr int S32 = RING / ((32 + BN) * BK * 2), S64 = RING / ((64 + BN) * BK * 2);
+      if constexpr (BMA > 64 && S32 > SA && S64 >= SA) {
+        if (most_rows <= 32) {
+          gemm_tile<MODE, 32, BN, BK, 1, 4, (S32 < 8 ? S32 : 8)>(a, smem, cum);
+          return;
+        }
+        if (most_rows <= 64) {
+          gemm_tile<MODE, 64, BN, BK, 1, 4, (S64 < 8 ? S64 : 8)>(a, smem, cum);
+          return;
+        }
       }
-      if (most_rows <= 64) {
-        gemm_tile<MODE, 64, BN, BK, 1, 4, (S64 < 8 ? S64 : 8)>(a, smem, cum);
-        return;
+    } else {
+      // the same with 2 token-row stages and the rest of the ring as weights
+      constexpr int B32 = (RING - 2 * 32 * BK * 2) / (BN * BK * 2);
+      constexpr int B64 = (RING - 2 * 64 * BK * 2) / (BN * BK * 2);
+      if constexpr (BMA > 64 && B64 > SAB) {
+        if (most_rows <= 32) {
+          gemm_tile<MODE, 32, BN, BK, 1, 4, 2, (B32 < 8 ? B32 : 8)>(a, smem, cum);
+          return;
+        }
+        if (most_rows <= 64) {
+          gemm_tile<MODE, 64, BN, BK, 1, 4, 2, (B64 < 8 ? B64 : 8)>(a, smem, cum);
+          return;
+        }
       }
     }
-    gemm_tile<MODE, BMA, BN, BK, 1, 4, SA>(a, smem, cum);
+    gemm_tile<MODE, BMA, BN, BK, 1, 4, SA, SAB>(a, smem, cum);
   } else {
-    gemm_tile<MODE, BMB, BN, BK, 1, 4, SB>(a, smem, cum);
+    gemm_tile<MODE, BMB, BN, BK, 1, 4, SB, SBB>(a, smem, cum);
   }
 }
 
@@ -805,14 +824,15 @@ static int launch_gemm_dma(const Args& a, int rows_cap, hipStream_t s) {
   return MOE_OK;
 }
 
-template <int MODE, int BN, int BK, int BMA, int SA, int BMB, int SB, int WPE>
+template <int MODE, int BN, int BK, int BMA, int SA, int SAB, int BMB, int SB, int SBB,
+          int WPE>
 static int launch_gemm_dual(Args a, int rows_cap, hipStream_t s) {
-  constexpr size_t la = static_cast<size_t>(SA) * (BMA + BN) * BK * 2;
-  constexpr size_t lb = static_cast<size_t>(SB) * (BMB + BN) * BK * 2;
+  constexpr size_t la = (static_cast<size_t>(SA) * BMA + static_cast<size_t>(SAB) * BN) * BK * 2;
+  constexpr size_t lb = (static_cast<size_t>(SB) * BMB + static_cast<size_t>(SBB) * BN) * BK * 2;
   constexpr size_t lds = la > lb ? la : lb;
   static std::atomic<bool> attr_set[64];
   const void* fn =
-      reinterpret_cast<const void*>(gemm_dual_kernel<MODE, BN, BK, BMA, SA, BMB, SB, WPE>);
+      reinterpret_cast<const void*>(gemm_dual_kernel<MODE, BN, BK, BMA, SA, SAB, BMB, SB, SBB, WPE>);
   const int dev = current_device();
   if (dev < 0 || !attr_set[dev].load(std::memory_order_acquire)) {
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -825,7 +845,7 @@ static int launch_gemm_dual(Args a, int rows_cap, hipStream_t s) {
   const int mt_ub = (rows_cap + BMIN - 1) / BMIN + std::min(a.N, rows_cap);
   long grid = static_cast<long>(mt_ub) * a.n_tiles;
   grid = (grid + 7) / 8 * 8;
-  hipLaunchKernelGGL((gemm_dual_kernel<MODE, BN, BK, BMA, SA, BMB, SB, WPE>), dim3(grid),
+  hipLaunchKernelGGL((gemm_dual_kernel<MODE, BN, BK, BMA, SA, SAB, BMB, SB, SBB, WPE>), dim3(grid),
                      dim3(4 * MOE_WAVE), lds, s, a);
   return MOE_OK;
 }
@@ -899,7 +919,8 @@ using namespace moe::ffn;
 //            then 128-row ones; 32 token rows; K slices of 64 with 2 stages,
 //            or of 128 with 3 stages for reductions of 4096 or more.
 //   K slices of 32 (64-byte row segments) stream worse than 64 or 128.
-// Decode tile configurations {token rows, K slice, ring stages}; the _WIDE
+// Decode tile configurations {token rows, K slice, token-row stages,
+// weight stages (0: as many as token-row stages)}; the _WIDE
 // ones serve reductions of 4096 or more.  Gate-up below that picks on the
 // device between DEC_GU (one tile per expert and weight panel, when those
 // tiles fit the workgroup slots at once) and DEC_GU_MANY (32-row tiles and
@@ -920,14 +941,15 @@ using namespace moe::ffn;
 #define MOE_DEC_DN_WIDE 32, 128, 3
 #endif
 struct DecCfg {
-  int bm, bk, s;
+  int bm, bk, s, sb0;
+  constexpr int sb() const { return sb0 ? sb0 : s; }
 };
 constexpr DecCfg DEC_GU = {MOE_DEC_GU}, DEC_GU_MANY = {MOE_DEC_GU_MANY},
                  DEC_GU_WIDE = {MOE_DEC_GU_WIDE},
                  DEC_DN = {MOE_DEC_DN}, DEC_DN_WIDE = {MOE_DEC_DN_WIDE};
 // LDS of a decode workgroup with bn weight rows: the ring (the tile-count
 // table shares it)
-constexpr int dec_lds(DecCfg c, int bn) { return c.s * (c.bm + bn) * c.bk * 2; }
+constexpr int dec_lds(DecCfg c, int bn) { return (c.s * c.bm + c.sb() * bn) * c.bk * 2; }
 // workgroups per CU that the LDS allows (160 KB per CU), at most 4
 constexpr int dec_wpe(DecCfg c, int bn) {
   return (160 * 1024) / dec_lds(c, bn) < 4 ? (160 * 1024) / dec_lds(c, bn) : 4;
@@ -973,7 +995,11 @@ static bool skinny_tiles(int T, int k, int mode) {
 
 // Decode weight-tile height: 256 rows unless that gives fewer tiles than
 // two per CU (the number of experts with rows is at most min(N, T*k)).
+#ifndef MOE_DEC_DN_NARROW
+#define MOE_DEC_DN_NARROW 0
+#endif
 static bool narrow_decode_tiles(int T, int N, int k, int cols_per_256) {
+  if (MOE_DEC_DN_NARROW) return true;
   const long experts = std::min(static_cast<long>(N), static_cast<long>(T) * k);
   return experts * cols_per_256 < 2L * cu_count();
 }
@@ -1039,14 +1065,14 @@ extern "C" int moe_ffn_gate_up(const void* x, const int32_t* row_token,
       st = launch_gemm_skinny<GATEUP>(g, rows_cap, s);
     } else if (H >= 4096) {
       constexpr DecCfg c = DEC_GU_WIDE;
-      st = launch_gemm_dma<GATEUP, c.bm, 128, c.bk, 1, 4, c.s, dec_wpe(c, 128)>(g, rows_cap, s);
+      st = launch_gemm_dma<GATEUP, c.bm, 128, c.bk, 1, 4, c.s, dec_wpe(c, 128), c.sb()>(g, rows_cap, s);
     } else {
       // one wave of DEC_GU tiles when they fit the workgroup slots (few
       // active experts, e.g. after SERE), else the DEC_GU_MANY tiles
       constexpr DecCfg c = DEC_GU, m = DEC_GU_MANY;
       static_assert(c.bk == m.bk, "one K slice for both tile heights");
       constexpr int wpe = dec_wpe(c, 128) < dec_wpe(m, 128) ? dec_wpe(c, 128) : dec_wpe(m, 128);
-      st = launch_gemm_dual<GATEUP, 128, c.bk, c.bm, c.s, m.bm, m.s, wpe>(g, rows_cap, s);
+      st = launch_gemm_dual<GATEUP, 128, c.bk, c.bm, c.s, c.sb(), m.bm, m.s, m.sb(), wpe>(g, rows_cap, s);
     }
     if (st != MOE_OK) return MOE_EHIP;
   } else {
@@ -1097,20 +1123,20 @@ extern "C" int moe_ffn_down(const void* h, const int32_t* expert_offsets,
       const bool nar = narrow || !DN_256_WIDE;
       d.n_tiles = nar ? H / 128 : H / 256;
       if constexpr (DN_256_WIDE) {
-        st = nar ? launch_gemm_dma<DOWN, c.bm, 128, c.bk, 1, 4, c.s, dec_wpe(c, 128)>(d, rows_cap, s)
-                 : launch_gemm_dma<DOWN, c.bm, 256, c.bk, 1, 4, c.s, dec_wpe(c, 256)>(d, rows_cap, s);
+        st = nar ? launch_gemm_dma<DOWN, c.bm, 128, c.bk, 1, 4, c.s, dec_wpe(c, 128), c.sb()>(d, rows_cap, s)
+                 : launch_gemm_dma<DOWN, c.bm, 256, c.bk, 1, 4, c.s, dec_wpe(c, 256), c.sb()>(d, rows_cap, s);
       } else {
-        st = launch_gemm_dma<DOWN, c.bm, 128, c.bk, 1, 4, c.s, dec_wpe(c, 128)>(d, rows_cap, s);
+        st = launch_gemm_dma<DOWN, c.bm, 128, c.bk, 1, 4, c.s, dec_wpe(c, 128), c.sb()>(d, rows_cap, s);
       }
     } else {
       constexpr DecCfg c = DEC_DN;
       const bool nar = narrow || !DN_256;
       d.n_tiles = nar ? H / 128 : H / 256;
       if constexpr (DN_256) {
-        st = nar ? launch_gemm_dma<DOWN, c.bm, 128, c.bk, 1, 4, c.s, dec_wpe(c, 128)>(d, rows_cap, s)
-                 : launch_gemm_dma<DOWN, c.bm, 256, c.bk, 1, 4, c.s, dec_wpe(c, 256)>(d, rows_cap, s);
+        st = nar ? launch_gemm_dma<DOWN, c.bm, 128, c.bk, 1, 4, c.s, dec_wpe(c, 128), c.sb()>(d, rows_cap, s)
+                 : launch_gemm_dma<DOWN, c.bm, 256, c.bk, 1, 4, c.s, dec_wpe(c, 256), c.sb()>(d, rows_cap, s);
       } else {
-        st = launch_gemm_dma<DOWN, c.bm, 128, c.bk, 1, 4, c.s, dec_wpe(c, 128)>(d, rows_cap, s);
+        st = launch_gemm_dma<DOWN, c.bm, 128, c.bk, 1, 4, c.s, dec_wpe(c, 128), c.sb()>(d, rows_cap, s);
       }
     }
     if (st != MOE_OK) return MOE_EHIP;
