@@ -21,10 +21,12 @@
 // live in LDS too), and writes the results out once, coalesced.  Shapes
 // whose tail does not fit in LDS are not supported here (the separate entry
 // points cover them).
+#include <atomic>
 #include <cmath>
 
 #include "capacity_impl.h"
 #include "dispatch_impl.h"
+#include "dtail_impl.h"
 #include "route_impl.h"
 #include "sere_impl.h"
 
@@ -222,11 +224,12 @@ __device__ void tail(const Args& f, const cap::Args& cg, const disp::Args& dg,
   }
 }
 
-template <int GT>
+// DT: the batch-wide steps run as dtail::run (decode batches within its
+// limits), else as tail() above.
+template <int GT, bool DT>
 __global__ __launch_bounds__(FT) void routing_kernel(Args f, cap::Args ca,
-                                                       disp::Args da) {
+                                                       disp::Args da, dtail::Args dta) {
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ sr::SereLds sl;
   __shared__ int s_last;
   constexpr int TPB = FT / GT;
   const int grp = threadIdx.x / GT;
@@ -272,7 +275,12 @@ __global__ __launch_bounds__(FT) void routing_kernel(Args f, cap::Args ca,
   __syncthreads();
   if (!s_last) return;
 
-  tail(f, ca, da, smem, sl);
+  if constexpr (DT) {
+    dtail::run(dta, smem);
+  } else {
+    __shared__ sr::SereLds sl;
+    tail(f, ca, da, smem, sl);
+  }
 }
 
 // Dynamic LDS of the kernel: the larger of the routing groups and the tail.
@@ -325,6 +333,8 @@ extern "C" int moe_routing_fused(
     return MOE_EINVAL;
   if (kprime > 0 && (!sim || !prot || !slot_sere)) return MOE_EINVAL;
   if (workspace_bytes < fused::WS_BYTES) return MOE_EINVAL;
+  hipStream_t s = as_stream(stream);
+
   char* ws = static_cast<char*>(workspace);
 
   fused::Args f{};
@@ -389,21 +399,63 @@ extern "C" int moe_routing_fused(
   const int GT = MOE_FUSED_GT ? MOE_FUSED_GT
                               : (T <= cu_count() ? fused::FT : (N <= 128 ? 64 : 256));
   const int TPB = fused::FT / GT;
-  const size_t lds = fused::kernel_lds(f.tl, N, GT);
-  const void* fn = GT == 64  ? reinterpret_cast<const void*>(fused::routing_kernel<64>)
-                   : GT == 256 ? reinterpret_cast<const void*>(fused::routing_kernel<256>)
-                               : reinterpret_cast<const void*>(fused::routing_kernel<fused::FT>);
-  if (lds > 65536 &&
-      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          static_cast<int>(lds)) != hipSuccess)
-    return MOE_EHIP;
-  hipStream_t s = as_stream(stream);
   const dim3 grid((T + TPB - 1) / TPB), block(fused::FT);
-  if (GT == 64)
-    hipLaunchKernelGGL(fused::routing_kernel<64>, grid, block, lds, s, f, ca, da);
-  else if (GT == 256)
-    hipLaunchKernelGGL(fused::routing_kernel<256>, grid, block, lds, s, f, ca, da);
-  else
-    hipLaunchKernelGGL(fused::routing_kernel<fused::FT>, grid, block, lds, s, f, ca, da);
-  return launch_status();
+
+  // Decode batches within the compact tail's limits run it as the last
+  // workgroup's steps.
+  static_assert(fused::FT == dtail::NT, "the compact tail runs in one routing workgroup");
+  const bool dt = dtail::supported(T, N, k, R);
+  dtail::Args d{};
+  if (dt) {
+    d.topk = topk_ids;
+    d.fb = fallback_ids;
+    d.vis = is_visual;
+    d.ew = entropy_w;
+    d.mod = modality;
+    d.sim = sim;
+    d.prot = prot;
+    d.T = T;
+    d.N = N;
+    d.k = k;
+    d.R = R;
+    d.kprime = kprime;
+    d.group = group;
+    d.nbits = nb;
+    d.rho = rho;
+    d.gamma = gamma;
+    d.lam = lam;
+    d.cap_on = !std::isinf(gamma);
+    d.sim_lds = kprime > 0 && N <= dtail::SIM_LDS_N;
+    d.slot_sere = slot_sere;
+    d.slot_expert = slot_expert;
+    d.flags = flags;
+    d.load_q = load_q;
+    d.cap_q = cap_q;
+    d.stats = stats;
+    d.r_v = r_v;
+    d.offsets = expert_offsets;
+    d.row_token = row_token;
+    d.row_slot = row_slot;
+    d.slot_row = slot_row;
+  }
+  const size_t route_lds = static_cast<size_t>(TPB) * rt::token_lds_bytes(N, GT);
+  const size_t lds = dt ? std::max(route_lds, dtail::dyn_lds(N, d.sim_lds))
+                        : fused::kernel_lds(f.tl, N, GT);
+  auto launch = [&](auto kern) -> int {
+    const void* fn = reinterpret_cast<const void*>(kern);
+    if (lds > 65536 &&
+        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(lds)) != hipSuccess)
+      return static_cast<int>(MOE_EHIP);
+    hipLaunchKernelGGL(kern, grid, block, lds, s, f, ca, da, d);
+    return launch_status();
+  };
+  if (dt) {
+    if (GT == 64) return launch(fused::routing_kernel<64, true>);
+    if (GT == 256) return launch(fused::routing_kernel<256, true>);
+    return launch(fused::routing_kernel<fused::FT, true>);
+  }
+  if (GT == 64) return launch(fused::routing_kernel<64, false>);
+  if (GT == 256) return launch(fused::routing_kernel<256, false>);
+  return launch(fused::routing_kernel<fused::FT, false>);
 }
