@@ -178,29 +178,55 @@ __device__ __forceinline__ void ordered_prefix(int n, int N, int nbits, uint32_t
     if (key[c] >= 0) incl[c] += myrun[key[c]];
 }
 
-// The batch-wide steps, run by one workgroup of NT threads once every
-// token's ranks are visible in a.topk and a.fb.  dyn: dynamic LDS of at
-// least dyn_lds(N, a.sim_lds) bytes ([N*N f32 sim][N*N u8 prot]).
-__device__ __forceinline__ void run(const Args& a, unsigned char* dyn) {
-  __shared__ int16_t s_e[MAX_SLOTS];      // router experts, then final experts
-  __shared__ int16_t s_cur[MAX_SLOTS];    // post-SERE experts, then placed ones
-  __shared__ uint8_t s_st[MAX_SLOTS];
-  __shared__ int16_t s_fb[MAX_FB];
-  __shared__ int32_t s_wq[MAX_T];
-  __shared__ uint8_t s_inp[MAX_N], s_sec[MAX_N], s_active[MAX_N];
-  __shared__ int16_t s_target[MAX_N];
-  __shared__ uint32_t s_run[NW * MAX_N];   // round 0
-  __shared__ uint32_t s_drun[NW * MAX_N];  // dispatch
-  __shared__ uint32_t s_tot[MAX_N];
-  __shared__ int32_t s_cap[MAX_N];        // capacity, clamped to 2^30
-  __shared__ uint32_t s_load0[MAX_N];
-  __shared__ uint32_t s_U[(MAX_R + 1) * MAX_N];
-  __shared__ uint32_t s_tab[2 * 4 * MAX_N];
-  __shared__ unsigned long long s_load_off[MAX_N];
-  __shared__ int32_t s_off[MAX_N + 1];
-  __shared__ unsigned long long s_sum[4];  // W, W_vis, dropped, re-routed
-  __shared__ uint8_t s_pend[8];            // token waves with a pending overflow, by round parity
+// LDS of the compact tail (every instantiation of run() shares one block).
+struct Lds {
+  int16_t s_e[MAX_SLOTS];      // router experts, then final experts
+  int16_t s_cur[MAX_SLOTS];    // post-SERE experts, then placed ones
+  uint8_t s_st[MAX_SLOTS];
+  int16_t s_fb[MAX_FB];
+  int32_t s_wq[MAX_T];
+  uint8_t s_inp[MAX_N], s_sec[MAX_N], s_active[MAX_N];
+  int16_t s_target[MAX_N];
+  uint32_t s_run[NW * MAX_N];   // round 0
+  uint32_t s_drun[NW * MAX_N];  // dispatch
+  uint32_t s_tot[MAX_N];
+  int32_t s_cap[MAX_N];        // capacity, clamped to 2^30
+  uint32_t s_load0[MAX_N];
+  uint32_t s_U[(MAX_R + 1) * MAX_N];
+  uint32_t s_tab[2 * 4 * MAX_N];
+  unsigned long long s_load_off[MAX_N];
+  int32_t s_off[MAX_N + 1];
+  unsigned long long s_sum[4];  // W, W_vis, dropped, re-routed
+  uint8_t s_pend[8];            // token waves with a pending overflow, by round parity
+};
 
+// The batch-wide steps, run by one workgroup of NT threads once every
+// token's ranks are visible in a.topk and a.fb; k <= MK and R <= MR (the
+// per-token loops of the fallback rounds are unrolled to these bounds).
+// dyn: dynamic LDS of at least dyn_lds(N, a.sim_lds) bytes
+// ([N*N f32 sim][N*N u8 prot]).
+template <int MK, int MR>
+__device__ __forceinline__ void run(const Args& a, unsigned char* dyn, Lds& L) {
+  auto& s_e = L.s_e;
+  auto& s_cur = L.s_cur;
+  auto& s_st = L.s_st;
+  auto& s_fb = L.s_fb;
+  auto& s_wq = L.s_wq;
+  auto& s_inp = L.s_inp;
+  auto& s_sec = L.s_sec;
+  auto& s_active = L.s_active;
+  auto& s_target = L.s_target;
+  auto& s_run = L.s_run;
+  auto& s_drun = L.s_drun;
+  auto& s_tot = L.s_tot;
+  auto& s_cap = L.s_cap;
+  auto& s_load0 = L.s_load0;
+  auto& s_U = L.s_U;
+  auto& s_tab = L.s_tab;
+  auto& s_load_off = L.s_load_off;
+  auto& s_off = L.s_off;
+  auto& s_sum = L.s_sum;
+  auto& s_pend = L.s_pend;
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / MOE_WAVE);
   const int T = a.T, N = a.N, k = a.k, R = a.R, Tk = T * k, TR = T * R;
@@ -446,10 +472,10 @@ __device__ __forceinline__ void run(const Args& a, unsigned char* dyn) {
 
     // ---- fallback rounds: thread t owns token t
     const bool tok = tid < T;
-    int cur[MAX_K];
+    int cur[MK];
     uint32_t over = 0u, placed = 0u;
 #pragma unroll
-    for (int s = 0; s < MAX_K; ++s) {
+    for (int s = 0; s < MK; ++s) {
       cur[s] = -1;
       if (tok && s < k) {
         cur[s] = s_cur[tid * k + s];
@@ -458,9 +484,9 @@ __device__ __forceinline__ void run(const Args& a, unsigned char* dyn) {
     }
     const bool one_group = a.group >= N;
     const int tw = (T + MOE_WAVE - 1) / MOE_WAVE;  // waves holding tokens
-    int fbr[MAX_R];
+    int fbr[MR];
 #pragma unroll
-    for (int q = 0; q < MAX_R; ++q) fbr[q] = tok && q < R ? s_fb[tid * R + q] : 0;
+    for (int q = 0; q < MR; ++q) fbr[q] = tok && q < R ? s_fb[tid * R + q] : 0;
     // A (experts with a round-0 proposer) as four 64-bit words, the same in
     // every lane
     uint64_t am[4];
@@ -476,11 +502,11 @@ __device__ __forceinline__ void run(const Args& a, unsigned char* dyn) {
     uint32_t cand = 0u;
     if (tok && over) {
 #pragma unroll
-      for (int q = 0; q < MAX_R; ++q) {
+      for (int q = 0; q < MR; ++q) {
         const int c = fbr[q];
         bool held = false;
 #pragma unroll
-        for (int s = 0; s < MAX_K; ++s) held |= !((over >> s) & 1u) && cur[s] == c;
+        for (int s = 0; s < MK; ++s) held |= !((over >> s) & 1u) && cur[s] == c;
         const uint64_t aw = c < 64 ? am[0] : c < 128 ? am[1] : c < 192 ? am[2] : am[3];
         if (q < R && ((aw >> (c & 63)) & 1u) && !held) cand |= 1u << q;
       }
@@ -495,12 +521,12 @@ __device__ __forceinline__ void run(const Args& a, unsigned char* dyn) {
       if (tok && over && ((cand >> (r - 1)) & 1u)) {
         const int s0 = __builtin_ctz(over);
 #pragma unroll
-        for (int q = 0; q < MAX_R; ++q)
+        for (int q = 0; q < MR; ++q)
           if (q == r - 1) c = fbr[q];
         bool held = false;
         int e0 = 0;  // the offered slot's expert (register array, static indices)
 #pragma unroll
-        for (int s = 0; s < MAX_K; ++s) {
+        for (int s = 0; s < MK; ++s) {
           held |= cur[s] == c;
           if (s == s0) e0 = cur[s];
         }
@@ -526,29 +552,29 @@ __device__ __forceinline__ void run(const Args& a, unsigned char* dyn) {
       if (offer) {
         // every read of the round at once: the other token waves' totals,
         // the capacity, round 0's load and the earlier rounds' admissions
-        uint32_t x[3], u[MAX_R];
+        uint32_t x[3], u[MR];
 #pragma unroll
         for (int v = 0; v < 3; ++v) x[v] = tab[v * MAX_N + c];
         const int32_t cap = s_cap[c], l0 = static_cast<int32_t>(s_load0[c]);
 #pragma unroll
-        for (int q = 1; q < MAX_R; ++q) u[q] = s_U[q * MAX_N + c];
+        for (int q = 1; q < MR; ++q) u[q] = s_U[q * MAX_N + c];
         uint32_t base = 0;
 #pragma unroll
         for (int v = 0; v < 3; ++v)
           if (v < wave && v < tw && (x[v] & ~VAL_MASK) == tag) base += x[v] & VAL_MASK;
         int32_t rem = cap - l0;
 #pragma unroll
-        for (int q = 1; q < MAX_R; ++q)
+        for (int q = 1; q < MR; ++q)
           if (q < r) rem -= static_cast<int32_t>(u[q]);
         if (static_cast<int32_t>(base + local) <= rem) {
           const int s0 = __builtin_ctz(over);
 #pragma unroll
-          for (int s = 0; s < MAX_K; ++s)
+          for (int s = 0; s < MK; ++s)
             if (s == s0) cur[s] = c;
           over &= ~(1u << s0);
           placed |= 1u << s0;
 #pragma unroll
-          for (int q = 0; q < MAX_R; ++q)
+          for (int q = 0; q < MR; ++q)
             if (fbr[q] == c) cand &= ~(1u << q);  // now held
           atomicAdd(&s_U[r * MAX_N + c], static_cast<uint32_t>(wq));
         }
@@ -556,7 +582,7 @@ __device__ __forceinline__ void run(const Args& a, unsigned char* dyn) {
     }
     if (tok) {
 #pragma unroll
-      for (int s = 0; s < MAX_K; ++s)
+      for (int s = 0; s < MK; ++s)
         if (s < k) {
           const int i = tid * k + s;
           s_cur[i] = static_cast<int16_t>(cur[s]);

@@ -276,7 +276,11 @@ __global__ __launch_bounds__(FT) void routing_kernel(Args f, cap::Args ca,
   if (!s_last) return;
 
   if constexpr (DT) {
-    dtail::run(dta, smem);
+    __shared__ dtail::Lds dl;
+    if (dta.k <= 8 && dta.R <= 8)
+      dtail::run<8, 8>(dta, smem, dl);
+    else
+      dtail::run<dtail::MAX_K, dtail::MAX_R>(dta, smem, dl);
   } else {
     __shared__ sr::SereLds sl;
     tail(f, ca, da, smem, sl);
