@@ -754,48 +754,108 @@ __global__ __launch_bounds__(4 * MOE_WAVE) void gemm_skinny_kernel(Args a) {
 }
 
 // ------------------------------------------------------------- fp32 path
-// Plain fp32 FMA kernels (small fp32 layers); one thread per output value.
-__device__ __forceinline__ int expert_of_row(const int32_t* off, int N, int row) {
-  int lo = 0, hi = N - 1;  // last expert with off[e] <= row
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) / 2;
-    if (off[mid] <= row) lo = mid; else hi = mid - 1;
+// Small fp32 layers: one workgroup of 256 threads per (expert, 16-row tile,
+// 32-column tile), K in chunks of 64 staged through LDS; each thread owns a
+// 1 x 2 block of outputs (gate-up: of both the gate and the up columns).
+// Small tiles spread a tiny layer over many CUs.  fp32 accumulation in
+// ascending K order.
+constexpr int F32_BM = 16, F32_BN = 32, F32_BK = 64;
+
+template <int MODE>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(Args a, const float* __restrict__ x,
+                                                       const float* __restrict__ w,
+                                                       float* __restrict__ out) {
+  __shared__ int cum[1024 + 2];
+  __shared__ float sa[F32_BM][F32_BK + 1];
+  __shared__ float sb[MODE == GATEUP ? 2 : 1][F32_BN][F32_BK + 1];
+  int j, m0, nt, Mj, row0;
+  const bool live = find_tile<F32_BM>(a, cum, j, m0, nt, Mj, row0);
+  if (!live) return;
+  const int tid = threadIdx.x;
+  const int K = a.K, I = a.I;
+  const int tr = tid / 16, tc = tid % 16;  // row tr; columns 2 tc, 2 tc + 1
+  const int rows = min(F32_BM, Mj - m0);
+  const float* wbase = w + static_cast<size_t>(j) * a.w_stride;
+  constexpr int NB = MODE == GATEUP ? 2 : 1;
+  float acc[NB][2] = {};
+  // the row tile (gathered by token for gate-up) and the weight rows of one
+  // K chunk go through registers: chunk k0 + BK is requested before chunk k0
+  // is multiplied, so its memory latency overlaps the FMAs
+  constexpr int UA = F32_BM * F32_BK / 256, UB = NB * F32_BN * F32_BK / 256;
+  float va[UA], vb[UB];
+  size_t asrc[UA];
+#pragma unroll
+  for (int u = 0; u < UA; ++u) {
+    const int r = (tid + u * 256) / F32_BK;
+    asrc[u] = r >= rows ? ~size_t(0)
+              : MODE == GATEUP ? static_cast<size_t>(a.row_token[row0 + m0 + r]) * K
+                               : static_cast<size_t>(row0 + m0 + r) * K;
   }
-  return lo;
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < UA; ++u) {
+      const int c = (tid + u * 256) % F32_BK;
+      va[u] = asrc[u] != ~size_t(0) && k0 + c < K ? x[asrc[u] + k0 + c] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const int i = tid + u * 256;
+      const int b = i / (F32_BN * F32_BK), r = (i / F32_BK) % F32_BN, c = i % F32_BK;
+      const int col = nt * F32_BN + r;  // h column (gate-up) or output column (down)
+      const size_t wrow = MODE == GATEUP ? static_cast<size_t>(b * I + col) : col;
+      vb[u] = col < a.NC && k0 + c < K ? wbase[wrow * K + k0 + c] : 0.f;
+    }
+  };
+  fetch(0);
+  for (int k0 = 0; k0 < K; k0 += F32_BK) {
+#pragma unroll
+    for (int u = 0; u < UA; ++u) {
+      const int i = tid + u * 256;
+      sa[i / F32_BK][i % F32_BK] = va[u];
+    }
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const int i = tid + u * 256;
+      sb[i / (F32_BN * F32_BK)][(i / F32_BK) % F32_BN][i % F32_BK] = vb[u];
+    }
+    __syncthreads();
+    if (k0 + F32_BK < K) fetch(k0 + F32_BK);
+#pragma unroll 8
+    for (int kk = 0; kk < F32_BK; ++kk) {
+      const float x0 = sa[tr][kk];
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) acc[b][q] = fmaf(x0, sb[b][2 * tc + q][kk], acc[b][q]);
+    }
+    __syncthreads();
+  }
+  if (tr < rows) {
+    float* orow = out + static_cast<size_t>(row0 + m0 + tr) * a.NC;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int col = nt * F32_BN + 2 * tc + q;
+      if (col >= a.NC) continue;
+      if constexpr (MODE == GATEUP) {
+        const float g = acc[0][q], u = acc[1][q];
+        orow[col] = (g / (1.f + expf(-g))) * u;
+      } else {
+        orow[col] = acc[0][q];
+      }
+    }
+  }
 }
 
-__global__ __launch_bounds__(256) void gateup_f32(
-    const float* __restrict__ x, const int32_t* __restrict__ row_token,
-    const int32_t* __restrict__ off, const float* __restrict__ w13, int N,
-    int H, int I, int rows_cap, float* __restrict__ h) {
-  const long gid = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int row = static_cast<int>(gid / I), c = static_cast<int>(gid % I);
-  if (row >= rows_cap || row >= off[N]) return;
-  const int j = expert_of_row(off, N, row);
-  const float* xr = x + static_cast<size_t>(row_token[row]) * H;
-  const float* w1 = w13 + (static_cast<size_t>(j) * 2 * I + c) * H;
-  const float* w3 = w1 + static_cast<size_t>(I) * H;
-  float g = 0.f, u = 0.f;
-  for (int kk = 0; kk < H; ++kk) {
-    g = fmaf(xr[kk], w1[kk], g);
-    u = fmaf(xr[kk], w3[kk], u);
-  }
-  h[static_cast<size_t>(row) * I + c] = (g / (1.f + expf(-g))) * u;
-}
-
-__global__ __launch_bounds__(256) void down_f32(
-    const float* __restrict__ h, const int32_t* __restrict__ off,
-    const float* __restrict__ w2, int N, int H, int I, int rows_cap,
-    float* __restrict__ out) {
-  const long gid = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int row = static_cast<int>(gid / H), c = static_cast<int>(gid % H);
-  if (row >= rows_cap || row >= off[N]) return;
-  const int j = expert_of_row(off, N, row);
-  const float* hr = h + static_cast<size_t>(row) * I;
-  const float* wr = w2 + (static_cast<size_t>(j) * H + c) * I;
-  float acc = 0.f;
-  for (int kk = 0; kk < I; ++kk) acc = fmaf(hr[kk], wr[kk], acc);
-  out[static_cast<size_t>(row) * H + c] = acc;
+template <int MODE>
+static int launch_gemm_f32(Args a, const float* x, const float* w, float* out, int rows_cap,
+                           hipStream_t s) {
+  if (a.N > 1024) return MOE_EUNSUP;
+  a.n_tiles = (a.NC + F32_BN - 1) / F32_BN;
+  const int mt_ub = (rows_cap + F32_BM - 1) / F32_BM + std::min(a.N, rows_cap);
+  long grid = static_cast<long>(mt_ub) * a.n_tiles;
+  grid = (grid + 7) / 8 * 8;
+  hipLaunchKernelGGL(gemm_f32_kernel<MODE>, dim3(grid), dim3(256), 0, s, a, x, w, out);
+  return launch_status();
 }
 
 // ------------------------------------------------------------------ host
@@ -1039,12 +1099,17 @@ extern "C" int moe_ffn_gate_up(const void* x, const int32_t* row_token,
   hipStream_t s = as_stream(stream);
   const int rows_cap = T * k;
   if (dtype == MOE_F32) {
-    const long n1 = static_cast<long>(rows_cap) * I;
-    hipLaunchKernelGGL(gateup_f32, dim3((n1 + 255) / 256), dim3(256), 0, s,
-                       static_cast<const float*>(x), row_token, expert_offsets,
-                       static_cast<const float*>(w13), N, H, I, rows_cap,
-                       static_cast<float*>(h));
-    return launch_status();
+    Args g{};
+    g.row_token = row_token;
+    g.offsets = expert_offsets;
+    g.N = N;
+    g.K = H;
+    g.NC = I;
+    g.I = I;
+    g.w_stride = 2L * I * H;
+    return launch_gemm_f32<GATEUP>(g, static_cast<const float*>(x),
+                                   static_cast<const float*>(w13), static_cast<float*>(h),
+                                   rows_cap, s);
   }
   Args g{};
   g.a = static_cast<const uint16_t*>(x);
@@ -1094,12 +1159,16 @@ extern "C" int moe_ffn_down(const void* h, const int32_t* expert_offsets,
   hipStream_t s = as_stream(stream);
   const int rows_cap = T * k;
   if (dtype == MOE_F32) {
-    const long n2 = static_cast<long>(rows_cap) * H;
-    hipLaunchKernelGGL(down_f32, dim3((n2 + 255) / 256), dim3(256), 0, s,
-                       static_cast<const float*>(h), expert_offsets,
-                       static_cast<const float*>(w2), N, H, I, rows_cap,
-                       static_cast<float*>(out_rows));
-    return launch_status();
+    Args d{};
+    d.offsets = expert_offsets;
+    d.N = N;
+    d.K = I;
+    d.NC = H;
+    d.I = I;
+    d.w_stride = static_cast<long>(H) * I;
+    return launch_gemm_f32<DOWN>(d, static_cast<const float*>(h),
+                                 static_cast<const float*>(w2), static_cast<float*>(out_rows),
+                                 rows_cap, s);
   }
   Args d{};
   d.a = static_cast<const uint16_t*>(h);
