@@ -56,9 +56,9 @@ DIFF_REPS = 5  # timed-region pairs per in-step kernel duration
 
 HBM_COUNTERS = {
     "qwen3_decode_b128": dict(
-        kernel="gate_up_swiglu", fetch_kib=130590.2632, write_kib=1536.0039,
+        kernel="gate_up_swiglu", fetch_kib=130576.674, write_kib=1536.0,
         fetch_scale=2.0, write_scale=1.0,
-        sources_sha256="7da2eaf79500ebbe2665d23c74dce9aaed4e1d56a9ad5e6cb8bc1dced7e4be4e"),
+        sources_sha256="1b3922dc86448d537f3c6717116a56f0d830d7a3c6845e3aebb9d2a5cdcee9df"),
 }
 
 
