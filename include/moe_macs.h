@@ -229,6 +229,10 @@ int moe_capacity_assign(const int32_t* topk_ids, const int32_t* slot_in,
 /*
  * moe_dispatch -- permutation of the kept slots into expert-major rows,
  * ordered by (token, slot) inside each expert; feeds the grouped FFN.
+ * This is the hand-off of the multi-image QA write-up §4.2 (online
+ * execution): the re-routed slots go straight to the fused expert FFN, the
+ * grouping done by a counting scan rather than a sort; dropped slots
+ * (MACS §1, Fig. 1) take no row.
  *
  * slot_expert     i32[T,k]   final experts, -1 = dropped.
  * expert_offsets  i32[N+1]   out: rows of expert j are

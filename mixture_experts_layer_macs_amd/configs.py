@@ -27,7 +27,7 @@ INF = math.inf
 # b_j = -ZIPF_BETA * 1.1 * ln(rank_j).  Chosen once by bisection so that the
 # mean top-8 batch union of a 128-token, 128-expert batch over seeds 0-9 is
 # about 90 experts (the Qwen3-30B-A3B union at batch 128 reported in the
-# multi-image QA write-up, §2.2).  oracle/calibrate_zipf.py reproduces it.
+# multi-image QA write-up, §2.2).  tests/calibrate_zipf.py reproduces it.
 ZIPF_BETA = 0.7735
 
 

@@ -4,7 +4,7 @@ Finds beta such that the mean top-8 batch union over a 128-token,
 128-expert batch, averaged over seeds 0-9, is 90 experts (the batch-128
 union the multi-image QA write-up reports for Qwen3-30B-A3B in §2.2).
 The union is computed with the oracle's router.  Run:
-    python -m oracle.calibrate_zipf
+    python -m tests.calibrate_zipf
 and copy the printed value into configs.ZIPF_BETA.
 """
 import numpy as np

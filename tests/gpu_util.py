@@ -2,11 +2,12 @@
 seeded inputs and compare with the CPU oracle.
 
 Tolerances on the layer output y (values of the oracle in fp64):
-  bf16: |dy| <= 1e-2 + 2e-2 |y|  (the stated bar), and, because y of the
-        Qwen-shaped layer is itself ~1e-2, also the normwise bound
-        |dy| <= 1e-2 * max|y| + 2e-2 |y|.  The GPU rounds h and the expert
-        output rows to bf16 (relative 2^-9 each) and y once more, so its
-        error is a few 2^-9 of the row scale.
+  bf16: element by element, |dy| <= min(1e-2, 1e-2 max|y|) + 2e-2 |y|:
+        the stated bar 1e-2 + 2e-2 |y|, with the absolute floor cut to 1%
+        of the largest output when y is small (y of the Qwen-shaped layer
+        is itself ~1e-2).  The GPU rounds h and the expert output rows to
+        bf16 (relative 2^-9 each) and y once more, so its error is a few
+        2^-9 of the row scale.
   fp32: |dy| <= 1e-5 + 1e-5 |y|.
 Gates (fp32 on the GPU, fp64 in the oracle): |dg| <= 1e-7 + 1e-5 |g|.
 """
