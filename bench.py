@@ -122,6 +122,9 @@ def parse():
                         "decode headline also times the 8192-token multimodal "
                         "prefill, the tiny fp32 layer and the Mixtral-shaped "
                         "layers)")
+    p.add_argument("--weights", choices=("panels", "rows"), default="panels",
+                   help="bf16 expert weights in the panel layout written once "
+                        "by moe_pack_weights (default), or in the row layout")
     p.add_argument("--separate-routing", action="store_true",
                    help="route with the four separate calls instead of the "
                         "single fused launch")
@@ -195,6 +198,12 @@ def run_sweep(args):
         0.0, 0.02, generator=gen) for _ in range(L)]
     w2 = [torch.empty((N, H, I), dtype=torch.bfloat16, device=dev).normal_(
         0.0, 0.02, generator=gen) for _ in range(L)]
+    panels = args.weights == "panels"
+    if panels:  # packed once per layer, as at model load
+        for l in range(L):
+            w13[l], w2[l] = B.moe_pack_weights(w13[l], w2[l])
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     rows = []
     for T in (1, 8, 32, 64, 128, 256):
         x = elem_tensor(synth.activations(base.with_(T=T), args.seed), "bf16", dev)
@@ -213,9 +222,10 @@ def run_sweep(args):
                                 d["modality"], d["sim"], d["prot"], kp, wl.rho,
                                 wl.gamma, wl.lam, wl.group)
                     B.moe_ffn_gate_up(x, lay.disp["row_token"],
-                                      lay.disp["expert_offsets"], w13[l], k, h)
+                                      lay.disp["expert_offsets"], w13[l], k, h,
+                                      panels=panels)
                     B.moe_ffn_down(h, lay.disp["expert_offsets"], w2[l], T, k,
-                                   lay.out_rows)
+                                   lay.out_rows, panels=panels)
                     B.moe_combine(lay.out_rows, lay.disp["slot_row"],
                                   lay.topk_gates, lay.y)
 
@@ -259,6 +269,7 @@ def run_sweep(args):
                                 "moved and us per 48-layer step",
                       "unit": "us", "higher_is_better": False, "n_gpus": 1,
                       "layers": L, "dtype": "bf16",
+                      "weights": "panels" if panels else "rows",
                       "data": "synthetic (seeded; random-init weights)",
                       "config": {"workload": "sweep_layer x 48", "H": H, "N": N,
                                  "k": k, "I": I, "gamma": base.gamma,
@@ -454,6 +465,15 @@ def measure(wl, args, with_cpu=False):
     d = to_device(inp, dev)
     w13s = [d["w13"]] + [d["w13"].clone() for _ in range(args.copies - 1)]
     w2s = [d["w2"]] + [d["w2"].clone() for _ in range(args.copies - 1)]
+    # weights packed once, as at model load; the step reads only the packs
+    panels = wl.dtype == "bf16" and args.weights == "panels"
+    if panels:
+        packed = [B.moe_pack_weights(a, b) for a, b in zip(w13s, w2s)]
+        w13s, w2s = [p[0] for p in packed], [p[1] for p in packed]
+        del packed
+        d["w13"] = d["w2"] = None
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     T, H, N, k, I, R = wl.T, wl.H, wl.N, wl.k, wl.I, wl.R
     lay = B.Layer(T, H, N, k, I, R, torch_elem_dtype(wl.dtype), dev)
     h = torch.empty((T * k, I), dtype=torch_elem_dtype(wl.dtype), device=dev)
@@ -463,11 +483,12 @@ def measure(wl, args, with_cpu=False):
 
     def gate_up(i):
         B.moe_ffn_gate_up(d["x"], lay.disp["row_token"],
-                          lay.disp["expert_offsets"], w13s[i % len(w13s)], k, h)
+                          lay.disp["expert_offsets"], w13s[i % len(w13s)], k, h,
+                          panels=panels)
 
     def down(i):
         B.moe_ffn_down(h, lay.disp["expert_offsets"], w2s[i % len(w2s)], T, k,
-                       lay.out_rows)
+                       lay.out_rows, panels=panels)
 
     def step(i, skip=()):
         lay.routing(d["logits"], d["is_visual"], d["entropy_w"], d["modality"],
@@ -565,6 +586,7 @@ def measure(wl, args, with_cpu=False):
         mode="eager" if graph_ms is None or eager_ms <= graph_ms else "hip-graph",
         steps=steps,
         routing="fused" if fused else "separate",
+        weights="panels" if panels else "rows",
         union_baseline=int(len(np.unique(topk))),
         union_sere=int(len(np.unique(slot_sere))),
         union_final=U, kept_rows=M,

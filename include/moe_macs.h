@@ -68,8 +68,10 @@ extern "C" {
 enum { MOE_OK = 0, MOE_EINVAL = -1, MOE_EUNSUP = -2, MOE_EHIP = -3,
        MOE_ESCRATCH = -4 };
 
-/* element type of x, expert weights, intermediates, out_rows and y */
-enum { MOE_F32 = 0, MOE_BF16 = 1 };
+/* element type of x, expert weights, intermediates, out_rows and y;
+ * MOE_BF16_PANELS (expert FFN calls only) is bf16 with the expert weights in
+ * the panel layout written by moe_pack_weights */
+enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_BF16_PANELS = 2 };
 
 /* flags[t,s] bits written by moe_sere_reroute / moe_capacity_assign */
 enum { MOE_FLAG_SERE = 1, MOE_FLAG_MACS = 2, MOE_FLAG_DROP = 4 };
@@ -329,9 +331,12 @@ int moe_routing_fused(const float* logits, const uint8_t* is_visual,
  *                            contiguous.
  * out_rows        [T*k,H]    out: un-gated expert outputs, first M rows.
  * dtype           MOE_F32 (fp32 FMA) or MOE_BF16 (bf16 MFMA with fp32
- *                 accumulation; h and out_rows are rounded to bf16).
+ *                 accumulation; h and out_rows are rounded to bf16), or
+ *                 MOE_BF16_PANELS: MOE_BF16 arithmetic, with w13 and w2 as
+ *                 moe_pack_weights wrote them; the results equal those of
+ *                 MOE_BF16 on the unpacked weights bit for bit.
  * The workspace holds h ([T*k, I] of dtype).
- * Shapes: MOE_BF16 needs H % 256 == 0, I % 128 == 0, x of at most 2 GiB
+ * Shapes: the bf16 formats need H % 256 == 0, I % 128 == 0, x of at most 2 GiB
  * (T*H*2 <= 2^31 bytes) and one expert's w13 under 4 GiB (I*H*4 < 2^32
  * bytes); MOE_F32 needs H % 4 == 0 and I % 4 == 0; otherwise MOE_EUNSUP.
  *
@@ -352,6 +357,41 @@ int moe_ffn_gate_up(const void* x, const int32_t* row_token,
 int moe_ffn_down(const void* h, const int32_t* expert_offsets, const void* w2,
                  int T, int N, int k, int H, int I, int dtype, void* out_rows,
                  void* stream);
+
+/*
+ * moe_pack_weights -- the expert weights in the panel layout that the
+ * expert FFN streams from HBM in whole 16 KB blocks, each wave's share of a
+ * block loaded straight into its MFMA operand registers (dtype
+ * MOE_BF16_PANELS), written once when the weights are loaded.  The FFN of a
+ * decode step reads every active expert's weights once (MACS §3.1 Eq. 1,
+ * E_j), so its speed is the rate at which those blocks stream.
+ *
+ * Layout, per expert (K = H for w13, I for w2): the rows of the matrix in
+ * tile order -- w13: for each 16 h columns c0 .. c0+15 (c0 = 0, 16, ...)
+ * the 16 gate rows c0 .. c0+15, then the 16 up rows I+c0 .. I+c0+15; w2:
+ * rows 0 .. H-1 -- are cut into panels of 128 rows, and panel P is stored
+ * as K/64 consecutive 16 KB blocks, block b holding elements 64b .. 64b+63
+ * of the panel's rows in the operand order of the 32x32x16 bf16 MFMA: for
+ * each row group G = 0..3 (32 rows) and K step s = 0..3 (16 elements), 64
+ * chunks of 8 elements, chunk l being elements 64b + 16s + 8(l/32) .. +7 of
+ * group row l % 32.  So element (t, kk) of the tile-order matrix (kk % 8 ==
+ * 0 starts a chunk) is at byte
+ *   (P * K/64 + kk/64) * 16384
+ *     + ((G * 4 + (kk % 64)/16) * 64 + ((kk % 16)/8) * 32 + t % 32) * 16,
+ * P = t / 128, G = (t % 128) / 32, from the start of the expert's block,
+ * whose size and position are those of the row layout.
+ *
+ * w13, w2           [N,2I,H], [N,H,I] bf16 in the row layout (device).
+ * w13_panels,       out: the same sizes, packed (device; must not alias
+ * w2_panels         the inputs).  Either pair may be NULL to skip it.
+ * dtype             MOE_BF16 (the element type); MOE_F32 and
+ *                   MOE_BF16_PANELS give MOE_EUNSUP.
+ * Shapes as the bf16 expert FFN (H % 256 == 0, I % 128 == 0); errors:
+ * MOE_EINVAL for bad sizes, a pointer given without its partner, or
+ * aliasing; MOE_EUNSUP for other shapes; MOE_EHIP for launch failures.
+ */
+int moe_pack_weights(const void* w13, const void* w2, int N, int H, int I,
+                     int dtype, void* w13_panels, void* w2_panels, void* stream);
 
 /*
  * moe_expert_ffn_noalloc -- moe_expert_ffn for callers that cannot allocate

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_macs.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUP, MOE_EHIP, MOE_ESCRATCH = 0, -1, -2, -3, -4
 FFN_NOALLOC_MAX_BYTES = 32 << 20
-MOE_F32, MOE_BF16 = 0, 1
+MOE_F32, MOE_BF16, MOE_BF16_PANELS = 0, 1, 2
 FLAG_SERE, FLAG_MACS, FLAG_DROP = 1, 2, 4
 WEIGHT_ONE = 65536
 
@@ -65,6 +65,7 @@ _SIGS = {
     "moe_ffn_gate_up": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
     "moe_ffn_down": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
     "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P]),
+    "moe_pack_weights": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
 }
 
 
@@ -123,6 +124,16 @@ def _elem(dtype: torch.dtype) -> int:
     if dtype == torch.float32:
         return MOE_F32
     raise ValueError(f"unsupported element type {dtype}")
+
+
+def _ffn_format(dtype: torch.dtype, panels: bool) -> int:
+    """Format code of the expert FFN calls: panels selects the packed
+    weights of moe_pack_weights (bf16 only)."""
+    if not panels:
+        return _elem(dtype)
+    if dtype != torch.bfloat16:
+        raise ValueError("packed (panel) weights are bf16 only")
+    return MOE_BF16_PANELS
 
 
 def _empty(shape, dtype, like):
@@ -334,14 +345,43 @@ def moe_routing_fused(logits, is_visual, entropy_w, modality, sim, prot, k, R,
     _check(rc, "moe_routing_fused")
 
 
+def moe_pack_weights(w13=None, w2=None, w13_panels=None, w2_panels=None):
+    """Copies of w13 [N,2I,H] and/or w2 [N,H,I] (bf16) in the panel layout
+    that the expert FFN calls read with panels=True.  The packed tensors keep
+    the shapes of the originals; only the order of their elements differs."""
+    if w13 is None and w2 is None:
+        raise ValueError("nothing to pack")
+    if w13 is not None:
+        N, I2, H = w13.shape
+        I = I2 // 2
+    else:
+        N, H, I = w2.shape
+    if w13 is not None and w2 is not None and tuple(w2.shape) != (N, H, I):
+        raise ValueError("w13 and w2 shapes do not match")
+    ref = w13 if w13 is not None else w2
+    if w13 is not None and w13_panels is None:
+        w13_panels = torch.empty_like(w13)
+    if w2 is not None and w2_panels is None:
+        w2_panels = torch.empty_like(w2)
+    rc = _lib.moe_pack_weights(
+        _opt(w13, torch.bfloat16, "w13", (N, 2 * I, H)),
+        _opt(w2, torch.bfloat16, "w2", (N, H, I)), N, H, I, _elem(ref.dtype),
+        _opt(w13_panels if w13 is not None else None, torch.bfloat16, "w13_panels",
+             (N, 2 * I, H)),
+        _opt(w2_panels if w2 is not None else None, torch.bfloat16, "w2_panels",
+             (N, H, I)), _stream())
+    _check(rc, "moe_pack_weights")
+    return w13_panels, w2_panels
+
+
 def moe_expert_ffn(x, row_token, expert_offsets, w13, w2, k, workspace,
-                   out_rows=None):
+                   out_rows=None, panels=False):
     T, H = x.shape
     N, I2, H2 = w13.shape
     I = I2 // 2
     if H2 != H or tuple(w2.shape) != (N, H, I):
         raise ValueError("expert weight shapes do not match x")
-    dt = _elem(x.dtype)
+    dt = _ffn_format(x.dtype, panels)
     if out_rows is None:
         out_rows = _empty((T * k, H), x.dtype, x)
     rc = _lib.moe_expert_ffn(
@@ -355,7 +395,7 @@ def moe_expert_ffn(x, row_token, expert_offsets, w13, w2, k, workspace,
 
 
 def moe_expert_ffn_noalloc(x, row_token, expert_offsets, w13, w2, k,
-                           out_rows=None):
+                           out_rows=None, panels=False):
     """moe_expert_ffn with h in the library's fixed device buffer (no
     workspace; at most FFN_NOALLOC_MAX_BYTES of h)."""
     T, H = x.shape
@@ -369,31 +409,32 @@ def moe_expert_ffn_noalloc(x, row_token, expert_offsets, w13, w2, k,
         _dev(x, x.dtype, "x"), _dev(row_token, torch.int32, "row_token", (T * k,)),
         _dev(expert_offsets, torch.int32, "expert_offsets", (N + 1,)),
         _dev(w13, x.dtype, "w13"), _dev(w2, x.dtype, "w2"),
-        T, N, k, H, I, _elem(x.dtype),
+        T, N, k, H, I, _ffn_format(x.dtype, panels),
         _dev(out_rows, x.dtype, "out_rows", (T * k, H)), _stream())
     _check(rc, "moe_expert_ffn_noalloc")
     return out_rows
 
 
-def moe_ffn_gate_up(x, row_token, expert_offsets, w13, k, h):
+def moe_ffn_gate_up(x, row_token, expert_offsets, w13, k, h, panels=False):
     T, H = x.shape
     N, I2, _ = w13.shape
     I = I2 // 2
     rc = _lib.moe_ffn_gate_up(
         _dev(x, x.dtype, "x"), _dev(row_token, torch.int32, "row_token", (T * k,)),
         _dev(expert_offsets, torch.int32, "expert_offsets", (N + 1,)),
-        _dev(w13, x.dtype, "w13", (N, 2 * I, H)), T, N, k, H, I, _elem(x.dtype),
+        _dev(w13, x.dtype, "w13", (N, 2 * I, H)), T, N, k, H, I,
+        _ffn_format(x.dtype, panels),
         _dev(h, x.dtype, "h", (T * k, I)), _stream())
     _check(rc, "moe_ffn_gate_up")
     return h
 
 
-def moe_ffn_down(h, expert_offsets, w2, T, k, out_rows):
+def moe_ffn_down(h, expert_offsets, w2, T, k, out_rows, panels=False):
     N, H, I = w2.shape
     rc = _lib.moe_ffn_down(
         _dev(h, h.dtype, "h", (T * k, I)),
         _dev(expert_offsets, torch.int32, "expert_offsets", (N + 1,)),
-        _dev(w2, h.dtype, "w2"), T, N, k, H, I, _elem(h.dtype),
+        _dev(w2, h.dtype, "w2"), T, N, k, H, I, _ffn_format(h.dtype, panels),
         _dev(out_rows, h.dtype, "out_rows", (T * k, H)), _stream())
     _check(rc, "moe_ffn_down")
     return out_rows
@@ -477,11 +518,12 @@ class Layer:
 
     def forward(self, logits, x, w13, w2, is_visual, entropy_w, modality,
                 sim=None, prot=None, kprime=0, rho=0.5, gamma=math.inf,
-                lam=1.0, group=None, fused=None):
+                lam=1.0, group=None, fused=None, panels=False):
+        """panels: w13 and w2 are the packed copies of moe_pack_weights."""
         k = self.k
         self.routing(logits, is_visual, entropy_w, modality, sim, prot, kprime,
                      rho, gamma, lam, group, fused)
         moe_expert_ffn(x, self.disp["row_token"], self.disp["expert_offsets"],
-                       w13, w2, k, self.ws_ffn, self.out_rows)
+                       w13, w2, k, self.ws_ffn, self.out_rows, panels=panels)
         moe_combine(self.out_rows, self.disp["slot_row"], self.topk_gates, self.y)
         return self.y

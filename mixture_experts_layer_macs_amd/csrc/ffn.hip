@@ -23,6 +23,7 @@
 #include <atomic>
 #include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "dma.h"
@@ -47,6 +48,7 @@ struct Args {
   long w_stride;           // weight elements per expert
   int n_tiles;
   int dual_limit;          // gemm_dual_kernel: most tiles of the first height
+  int panels;              // 1: w in the panel layout (moe_pack_weights)
 };
 
 // Two fp32 values to a packed bf16 pair (round to nearest even), one
@@ -63,6 +65,54 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // (about 1 ulp each; the result is rounded to bf16 afterwards).
 __device__ __forceinline__ float silu(float g) {
   return g * __builtin_amdgcn_rcpf(1.f + __expf(-g));
+}
+
+// ------------------------------------------------------------ panel layout
+// moe_pack_weights stores each expert's weight matrix for the MFMA operand
+// order.  Rows, in tile order, form panels of 128; a panel is stored as K/64
+// consecutive blocks of 16 KB (128 rows x 64 K elements), and inside a block
+// the bytes follow the 32 x 32 x 16 MFMA operand: for row group G (32 rows)
+// and K step kk (16 elements), 1 KB holding, for lane l, the 8 elements
+// 8 (l / 32) .. +7 of step kk of row l % 32 of the group.  A wave's operand
+// for one K step is then one contiguous 1 KB load, and one 64-wide K slice
+// of a 128-row panel one contiguous 16 KB block.
+//
+// Tile order of w13: panel P holds h columns 64P .. 64P+63 as four groups of
+// 32 rows, group G = 16 gate rows (columns 64P+16G .. +15) followed by the
+// 16 up rows of the same columns, so that the gate and up value of one h
+// column meet in one lane's accumulators.  Tile order of w2: its rows.
+constexpr uint32_t PANEL_ROWS = 128, PANEL_K = 64, PANEL_BLOCK = PANEL_ROWS * PANEL_K * 2;
+
+// Tile-order row of w13 row wrow (gate rows 0 .. I-1, then the up rows).
+__host__ __device__ __forceinline__ uint32_t w13_tile_row(uint32_t wrow, uint32_t I) {
+  const uint32_t up = wrow >= I, c = up ? wrow - I : wrow;
+  return (c / 64) * PANEL_ROWS + ((c % 64) / 16) * 32 + up * 16 + c % 16;
+}
+
+// Byte offset, from the start of one expert's packed block, of the 16-byte
+// chunk of tile-order row t that starts at element k (k % 8 == 0), K being
+// the reduction length.
+__host__ __device__ __forceinline__ uint32_t panel_off(uint32_t t, uint32_t k, uint32_t K) {
+  const uint32_t blk = (t / PANEL_ROWS) * (K / PANEL_K) + k / PANEL_K;
+  const uint32_t G = (t % PANEL_ROWS) / 32, kk = (k % PANEL_K) / 16, half = (k % 16) / 8;
+  return blk * PANEL_BLOCK + ((G * 4 + kk) * 64 + half * 32 + t % 32) * 16;
+}
+
+// Byte offset, inside one expert's weight block, of the 16-byte chunk at
+// element kelem (a multiple of 8 below the slice width) of weight row wrow
+// in a K slice starting at element 0; weight_k0 adds the slice start.
+template <int MODE>
+__device__ __forceinline__ uint32_t weight_off(const Args& a, uint32_t wrow, uint32_t kelem) {
+  if (!a.panels) return wrow * static_cast<uint32_t>(a.K) * 2 + kelem * 2;
+  const uint32_t t = MODE == GATEUP ? w13_tile_row(wrow, a.I) : wrow;
+  return panel_off(t, kelem, static_cast<uint32_t>(a.K));
+}
+
+// Byte offset of K slice start kelem (a multiple of the slice width, 16 or
+// more), added to every weight_off of that slice: whole blocks, then whole
+// K steps inside the block (each step's 1 KB groups sit 1 KB apart).
+__device__ __forceinline__ uint32_t weight_k0(const Args& a, uint32_t kelem) {
+  return a.panels ? (kelem / PANEL_K) * PANEL_BLOCK + ((kelem % PANEL_K) / 16) * 1024 : kelem * 2;
 }
 
 // Locate the tile of this workgroup.  cum: LDS [N+2], the cumulative tile
@@ -224,7 +274,7 @@ __device__ __forceinline__ void gemm_body(const Args& a, unsigned char* smem, in
     } else {
       wrow = nt * BN + row;
     }
-    vb[q] = wrow * row_bytes + ch * 16;
+    vb[q] = weight_off<MODE>(a, wrow, ch * 8);
   }
   // LDS byte address of the dynamic LDS block (M0 wants it as 32 bits)
   const uint32_t lds_base = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
@@ -235,12 +285,12 @@ __device__ __forceinline__ void gemm_body(const Args& a, unsigned char* smem, in
   // slice is the wave's A row group d, the rest its B row groups.
   const int nk = K / BK;
   auto dma = [&](int kslice, int d) {
-    const uint32_t k0 = static_cast<uint32_t>(min(kslice, nk - 1) * BK * 2);
+    const uint32_t ke = static_cast<uint32_t>(min(kslice, nk - 1) * BK);
     if (d < QA)
-      lds_dma16(rsrc_a, va[d], k0,
+      lds_dma16(rsrc_a, va[d], ke * 2,
                 lds_base + (kslice % S) * A_STRIDE + (wave * QA + d) * 1024);
     else
-      lds_dma16(rsrc_b, vb[d - QA], k0,
+      lds_dma16(rsrc_b, vb[d - QA], weight_k0(a, ke),
                 lds_base + B_BASE + (kslice % SB) * B_STRIDE + (wave * QB + d - QA) * 1024);
   };
   auto issue = [&](int kslice) {
@@ -696,16 +746,16 @@ __global__ __launch_bounds__(4 * MOE_WAVE) void gemm_skinny_kernel(Args a) {
     } else {
       wrow = nt * BN + row;
     }
-    vb = wrow * row_bytes + ch * 16;
+    vb = weight_off<MODE>(a, wrow, ch * 8);
   }
   const uint32_t lds_base = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char*)(smem))));
   const int nk = K / BK;
   auto issue = [&](int s) {
-    const uint32_t k0 = static_cast<uint32_t>(min(s, nk - 1) * BK * 2);
+    const uint32_t ke = static_cast<uint32_t>(min(s, nk - 1) * BK);
     const uint32_t st = lds_base + (s % S) * STAGE + wave * 1024;
-    lds_dma16(rsrc_a, va, k0, st);
-    lds_dma16(rsrc_b, vb, k0, st + SLICE_A);
+    lds_dma16(rsrc_a, va, ke * 2, st);
+    lds_dma16(rsrc_b, vb, weight_k0(a, ke), st + SLICE_A);
   };
   typedef __attribute__((address_space(3))) const bf16x8 lds_frag;
   typedef __attribute__((address_space(3))) const unsigned char lds_byte;
@@ -750,6 +800,252 @@ __global__ __launch_bounds__(4 * MOE_WAVE) void gemm_skinny_kernel(Args a) {
     pk.x = pack_bf16x2(acc[0], acc[1]);
     pk.y = pack_bf16x2(acc[2], acc[3]);
     if (live) *reinterpret_cast<uint2*>(&a.out[orow + nt * BN + 4 * g4]) = pk;
+  }
+}
+
+// ----------------------------------------------- decode tiles on panels
+// Decode batches are bound by the weight stream: each active expert's
+// panel is read once, and the rate at which those bytes arrive is the rate
+// of the layer.  With packed weights (the panel layout) each wave reads its
+// 32 weight rows of a K slice as NPW x 4 contiguous 1 KB loads straight into
+// its MFMA operand registers, L slices ahead of the slice it multiplies, so
+// the weight requests of a workgroup stay in flight across its barriers.
+// The token rows (x gathered by row_token for gate-up, h for down) are the
+// small operand: each thread loads its share of the next slice into
+// registers one slice ahead, and the workgroup stores it into a two-stage
+// LDS ring (rows of 128 bytes, 16-byte chunks XOR-swizzled) that every wave
+// reads its fragments from.  All loads are ordinary loads, so the compiler
+// places every wait.
+//
+// Workgroup: 4 waves, BN = 128 NPW weight rows (NPW panels), BM token rows
+// (32, 64 or 128, chosen on the device from the largest expert: one tile
+// per expert and panel when it fits), wave w owning weight rows
+// [32 w NPW, 32 (w+1) NPW) of the tile and every token row.
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
+
+template <int MODE, int BM, int NPW, int L>
+__device__ __forceinline__ void stream_body(const Args& a, unsigned char* smem, int j, int m0,
+                                            int nt, int Mj, int row0) {
+  constexpr int BK = 64, BN = 128 * NPW, FM = BM / 32, S = L + 1;
+  constexpr int CH = BM * BK * 2 / 16 / 256;  // 16-byte chunks of A per thread per slice
+  static_assert(CH >= 1 && FM >= 1, "token-row tile of 32, 64 or 128");
+  constexpr int A_STAGE = BM * BK * 2;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / MOE_WAVE);
+  const int K = a.K, nk = K / BK;
+  const int tile_rows = min(BM, Mj - m0);
+
+  // A: thread tid fills chunk c = idx % 8 of row idx / 8 of each stage,
+  // idx = q * 256 + tid.  Rows past the tile load the tile's first row (so
+  // that every load is issued by every lane and the compiler can count
+  // them) and store zeros.
+  const uint16_t* asrc[CH];
+  uint32_t alds[CH];
+  bool alive[CH];
+#pragma unroll
+  for (int q = 0; q < CH; ++q) {
+    const int idx = q * 256 + tid, row = idx / 8, c = idx % 8;
+    alive[q] = row < tile_rows;
+    const int rr = alive[q] ? row : 0;
+    const size_t r = MODE == GATEUP ? static_cast<size_t>(a.row_token[row0 + m0 + rr])
+                                    : static_cast<size_t>(row0 + m0 + rr);
+    asrc[q] = a.a + r * K + c * 8;
+    alds[q] = row * (BK * 2) + ((c ^ ((row >> 1) & 7)) << 4);
+  }
+  // B: fragment column f of this wave is tile-order rows t0 .. t0 + 31,
+  // t0 = nt * BN + (wave * NPW + f) * 32: block row group G of panel P
+  const unsigned char* wbase =
+      reinterpret_cast<const unsigned char*>(a.w + static_cast<size_t>(j) * a.w_stride);
+  const unsigned char* bsrc[NPW];
+#pragma unroll
+  for (int f = 0; f < NPW; ++f) {
+    const uint32_t t0 = nt * BN + (wave * NPW + f) * 32;
+    bsrc[f] = wbase + static_cast<size_t>(t0 / PANEL_ROWS) * (K / PANEL_K) * PANEL_BLOCK +
+              ((t0 % PANEL_ROWS) / 32) * 4 * 1024 + lane * 16;
+  }
+
+  u32x4v breg[S][NPW][4];
+  u32x4v areg[S][CH];
+  auto load_b = [&](int kt, auto slot) {
+    constexpr int SL = decltype(slot)::value;
+#pragma unroll
+    for (int f = 0; f < NPW; ++f)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        breg[SL][f][kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(
+            bsrc[f] + static_cast<size_t>(kt) * PANEL_BLOCK + kk * 1024));
+  };
+  auto load_a = [&](int kt, auto slot) {
+    constexpr int SL = decltype(slot)::value;
+#pragma unroll
+    for (int q = 0; q < CH; ++q)
+      areg[SL][q] = *reinterpret_cast<const u32x4v*>(asrc[q] + kt * BK);
+  };
+  typedef __attribute__((address_space(3))) u32x4v lds_u4;
+  typedef __attribute__((address_space(3))) unsigned char lds_byte;
+  lds_byte* lds0 = (lds_byte*)(smem);
+  auto store_a = [&](int kt, auto slot) {
+    constexpr int SL = decltype(slot)::value;
+    lds_byte* st = lds0 + (kt & 1) * A_STAGE;
+#pragma unroll
+    for (int q = 0; q < CH; ++q)
+      *(lds_u4*)(st + alds[q]) = alive[q] ? areg[SL][q] : u32x4v{0u, 0u, 0u, 0u};
+  };
+
+  f32x16 acc[FM][NPW];
+#pragma unroll
+  for (int x = 0; x < FM; ++x)
+#pragma unroll
+    for (int f = 0; f < NPW; ++f)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[x][f][r] = 0.f;
+  const int nfrag = min(FM, (tile_rows + 31) / 32);
+  const int frow = lane & 31, fhalf = lane >> 5;
+  auto mma_slice = [&](int kt, auto slot) {
+    constexpr int SL = decltype(slot)::value;
+    typedef __attribute__((address_space(3))) const bf16x8 lds_frag;
+    const lds_byte* st = lds0 + (kt & 1) * A_STAGE;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int sw = ((kk * 2 + fhalf) ^ ((frow >> 1) & 7)) << 4;
+      bf16x8 fa[FM];
+#pragma unroll
+      for (int x = 0; x < FM; ++x) fa[x] = *(lds_frag*)(st + (x * 32 + frow) * (BK * 2) + sw);
+#pragma unroll
+      for (int x = 0; x < FM; ++x)
+        if (x < nfrag)
+#pragma unroll
+          for (int f = 0; f < NPW; ++f)
+            acc[x][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, breg[SL][f][kk]), fa[x], acc[x][f], 0, 0, 0);
+    }
+  };
+
+  // Both operands are requested L slices ahead, the token rows of a slice
+  // just before its weights: a wait for the token rows of slice kt + 1
+  // (in-order completion) then leaves the weights of slices kt + 1 ..
+  // kt + L in flight.  Prologue: slices 0 .. L-1, and slice 0's token rows
+  // in LDS (nk >= 2: K is a multiple of 128).
+  static_for<L>([&](auto i) {
+    if (decltype(i)::value < nk) {
+      load_a(decltype(i)::value, i);
+      load_b(decltype(i)::value, i);
+    }
+  });
+  store_a(0, std::integral_constant<int, 0>{});
+  __syncthreads();
+  // iteration kt: request slice kt + L, multiply slice kt, store the token
+  // rows of slice kt + 1 into the LDS stage of slice kt - 1 (read by every
+  // wave before the last barrier), barrier; unrolled by S so that every ring
+  // slot is a compile-time register set.  The main loop runs while every
+  // request of its S iterations is in range, with no branch around a load,
+  // so the compiler's waits count exactly the loads still needed; the last
+  // slices follow with guarded requests.
+  int k0 = 0;
+  for (; k0 + S - 1 + L < nk; k0 += S) {
+    static_for<S>([&](auto u) {
+      constexpr int U = decltype(u)::value;
+      const int kt = k0 + U;
+      load_a(kt + L, std::integral_constant<int, (U + L) % S>{});
+      load_b(kt + L, std::integral_constant<int, (U + L) % S>{});
+      mma_slice(kt, u);
+      store_a(kt + 1, std::integral_constant<int, (U + 1) % S>{});
+      __syncthreads();
+    });
+  }
+  for (; k0 < nk; k0 += S) {
+    static_for<S>([&](auto u) {
+      constexpr int U = decltype(u)::value;
+      const int kt = k0 + U;
+      if (kt < nk) {
+        if (kt + L < nk) {
+          load_a(kt + L, std::integral_constant<int, (U + L) % S>{});
+          load_b(kt + L, std::integral_constant<int, (U + L) % S>{});
+        }
+        mma_slice(kt, u);
+        if (kt + 1 < nk) store_a(kt + 1, std::integral_constant<int, (U + 1) % S>{});
+        __syncthreads();
+      }
+    });
+  }
+
+  const int fr = lane & 31;
+#pragma unroll
+  for (int x = 0; x < FM; ++x) {
+    const int row = x * 32 + fr;
+    const bool live = row < tile_rows;
+    const size_t orow = static_cast<size_t>(row0 + m0 + row) * a.NC;
+#pragma unroll
+    for (int f = 0; f < NPW; ++f) {
+      const int g = wave * NPW + f;  // fragment column of the tile
+      if constexpr (MODE == GATEUP) {
+        // gate rows in registers 0..7, the matching up rows in 8..15
+        const int c0 = nt * (BN / 2) + g * 16;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = silu(acc[x][f][4 * q + i]) * acc[x][f][4 * q + i + 8];
+          uint2 pk;
+          pk.x = pack_bf16x2(v[0], v[1]);
+          pk.y = pack_bf16x2(v[2], v[3]);
+          if (live) *reinterpret_cast<uint2*>(&a.out[orow + c0 + 8 * q + 4 * fhalf]) = pk;
+        }
+      } else {
+        const int c0 = nt * BN + g * 32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint2 pk;
+          pk.x = pack_bf16x2(acc[x][f][4 * q], acc[x][f][4 * q + 1]);
+          pk.y = pack_bf16x2(acc[x][f][4 * q + 2], acc[x][f][4 * q + 3]);
+          if (live) *reinterpret_cast<uint2*>(&a.out[orow + c0 + 8 * q + 4 * fhalf]) = pk;
+        }
+      }
+    }
+  }
+}
+
+// The token-row tile height is chosen on the device from the largest
+// expert (every workgroup reads the same offsets, so all take the same
+// branch): 32, 64 or 128 rows, larger experts in several 128-row tiles.
+template <int MODE, int NPW, int L, int BMX>
+__global__ __launch_bounds__(4 * MOE_WAVE) void gemm_stream_kernel(Args a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int* cum = reinterpret_cast<int*>(smem);
+  int* s_most = cum + a.N + 2;
+  if (threadIdx.x < MOE_WAVE) {
+    int mx = 0;
+    for (int j0 = 0; j0 < a.N; j0 += MOE_WAVE) {
+      const int e = j0 + lane_id();
+      mx = max(mx, wave_max(e < a.N ? a.offsets[e + 1] - a.offsets[e] : 0));
+    }
+    if (threadIdx.x == 0) *s_most = mx;
+  }
+  __syncthreads();
+  const int most = *s_most;
+  __syncthreads();  // the tile search rewrites the table
+  int j, m0, nt, Mj, row0;
+  if (BMX == 32 || most <= 32) {
+    if (find_tile_s<32>(a, cum, j, m0, nt, Mj, row0))
+      stream_body<MODE, 32, NPW, L>(a, smem, j, m0, nt, Mj, row0);
+  } else if (BMX == 64 || most <= 64) {
+    if constexpr (BMX >= 64)
+      if (find_tile_s<64>(a, cum, j, m0, nt, Mj, row0))
+        stream_body<MODE, 64, NPW, L>(a, smem, j, m0, nt, Mj, row0);
+  } else {
+    if constexpr (BMX >= 128)
+      if (find_tile_s<128>(a, cum, j, m0, nt, Mj, row0))
+        stream_body<MODE, 128, NPW, L>(a, smem, j, m0, nt, Mj, row0);
   }
 }
 
@@ -929,6 +1225,75 @@ static int launch_gemm_skinny(Args a, int rows_cap, hipStream_t s) {
   return MOE_OK;
 }
 
+// ------------------------------------------------------- weight packing
+// One thread per 16-byte chunk (8 elements) of the packed matrix: chunk q of
+// an expert's block is (block, group G, K step kk, lane l), holding elements
+// 64 b + 16 kk + 8 (l / 32) .. +7 of tile-order row 128 P + 32 G + l % 32
+// (block P * K/64 + b), read from the source row that tile-order row stands
+// for.
+template <int MODE>
+__global__ __launch_bounds__(256) void pack_panels_kernel(const uint4* __restrict__ src,
+                                                          uint4* __restrict__ dst, long chunks,
+                                                          uint32_t rows, uint32_t K, uint32_t I) {
+  const long o = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  if (o >= chunks) return;
+  constexpr uint32_t CPB = PANEL_BLOCK / 16;             // chunks per block
+  const long per_expert = static_cast<long>(rows) * K / 8;
+  const long e = o / per_expert;
+  const uint32_t q = static_cast<uint32_t>(o % per_expert);
+  const uint32_t blk = q / CPB, w = q % CPB;
+  const uint32_t P = blk / (K / PANEL_K), b = blk % (K / PANEL_K);
+  const uint32_t G = w / 256, kk = (w / 64) % 4, l = w % 64;
+  const uint32_t t = P * PANEL_ROWS + G * 32 + l % 32;   // tile-order row
+  const uint32_t k = b * PANEL_K + kk * 16 + (l / 32) * 8;
+  uint32_t wrow = t;
+  if (MODE == GATEUP) {                                  // inverse of w13_tile_row
+    const uint32_t r = t % 32, c = (t / PANEL_ROWS) * 64 + ((t % PANEL_ROWS) / 32) * 16 + r % 16;
+    wrow = r < 16 ? c : I + c;
+  }
+  dst[o] = src[e * per_expert + (static_cast<long>(wrow) * K + k) / 8];
+}
+
+// Decode tiles on packed weights (gemm_stream_kernel), measured on MI355X
+// (qwen3 and Mixtral decode shapes and the 48-layer sweep layer at batches
+// 32, 128 and 256): weights requested 3 slices ahead (2 is as fast, 4 costs
+// occupancy); gate-up with token-row tiles up to 128 (one tile per expert
+// and panel: the large experts after SERE read their panel once), down
+// with tiles of 32 token rows (more workgroups per CU) and two panels per
+// workgroup when the panels of the experts that may be active number at
+// least twice the workgroup slots (4 per CU), else one.
+#ifndef MOE_STREAM_L
+#define MOE_STREAM_L 3
+#endif
+#ifndef MOE_STREAM_NPW_GU
+#define MOE_STREAM_NPW_GU 1
+#endif
+#ifndef MOE_STREAM_GU
+#define MOE_STREAM_GU 1
+#endif
+#ifndef MOE_STREAM_BMX_GU
+#define MOE_STREAM_BMX_GU 128
+#endif
+#ifndef MOE_STREAM_BMX_DN
+#define MOE_STREAM_BMX_DN 32
+#endif
+#ifndef MOE_STREAM_DN
+#define MOE_STREAM_DN 1
+#endif
+template <int MODE, int NPW, int L, int BMX>
+static int launch_gemm_stream(Args a, int rows_cap, hipStream_t s) {
+  constexpr int BN = 128 * NPW;
+  // two stages of the tallest token-row tile; the tile table shares them
+  const size_t lds = std::max<size_t>(2 * BMX * 64 * 2, (static_cast<size_t>(a.N) + 3) * 4);
+  a.n_tiles = (MODE == GATEUP ? 2 * a.I : a.NC) / BN;
+  const int mt_ub = (rows_cap + 31) / 32 + std::min(a.N, rows_cap);
+  long grid = static_cast<long>(mt_ub) * a.n_tiles;
+  grid = (grid + 7) / 8 * 8;
+  hipLaunchKernelGGL((gemm_stream_kernel<MODE, NPW, L, BMX>), dim3(grid), dim3(4 * MOE_WAVE), lds,
+                     s, a);
+  return MOE_OK;
+}
+
 }  // namespace ffn
 }  // namespace moe
 
@@ -1068,11 +1433,11 @@ static int check_ffn_shape(int T, int N, int k, int H, int I, int dtype) {
   if (T < 0 || T > (1 << 20) || N < 1 || N > 1024 || k < 1 || k > N ||
       H < 1 || I < 1)
     return MOE_EINVAL;
-  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_EUNSUP;
-  if (dtype == MOE_BF16 && (H % 256 != 0 || I % 128 != 0)) return MOE_EUNSUP;
+  if (dtype != MOE_F32 && dtype != MOE_BF16 && dtype != MOE_BF16_PANELS) return MOE_EUNSUP;
+  if (dtype != MOE_F32 && (H % 256 != 0 || I % 128 != 0)) return MOE_EUNSUP;
   // bf16 loads address x and one expert's weight block with 32-bit byte
   // offsets; x stays under 2^31 bytes so that OOB_OFF lies outside it
-  if (dtype == MOE_BF16 && (static_cast<uint64_t>(T) * H * 2 > (1ull << 31) ||
+  if (dtype != MOE_F32 && (static_cast<uint64_t>(T) * H * 2 > (1ull << 31) ||
                             static_cast<uint64_t>(I) * H * 4 >= (1ull << 32)))
     return MOE_EUNSUP;
   if (dtype == MOE_F32 && (H % 4 != 0 || I % 4 != 0)) return MOE_EUNSUP;
@@ -1123,10 +1488,13 @@ extern "C" int moe_ffn_gate_up(const void* x, const int32_t* row_token,
   g.NC = I;
   g.I = I;
   g.w_stride = 2L * I * H;
+  g.panels = dtype == MOE_BF16_PANELS;
   if (decode_tiles(T, N, k)) {
     int st;
     g.n_tiles = I / 64;
-    if (skinny_tiles(T, k, GATEUP)) {
+    if (MOE_STREAM_GU && g.panels && !skinny_tiles(T, k, GATEUP)) {
+      st = launch_gemm_stream<GATEUP, MOE_STREAM_NPW_GU, MOE_STREAM_L, MOE_STREAM_BMX_GU>(g, rows_cap, s);
+    } else if (skinny_tiles(T, k, GATEUP)) {
       st = launch_gemm_skinny<GATEUP>(g, rows_cap, s);
     } else if (H >= 4096) {
       constexpr DecCfg c = DEC_GU_WIDE;
@@ -1182,10 +1550,16 @@ extern "C" int moe_ffn_down(const void* h, const int32_t* expert_offsets,
   d.NC = H;
   d.I = I;
   d.w_stride = static_cast<long>(H) * I;
+  d.panels = dtype == MOE_BF16_PANELS;
   if (decode_tiles(T, N, k)) {
     int st;
     const bool narrow = narrow_decode_tiles(T, N, k, H / 256);
-    if (skinny_tiles(T, k, DOWN)) {
+    if (MOE_STREAM_DN && d.panels && !skinny_tiles(T, k, DOWN)) {
+      const long experts = std::min(static_cast<long>(N), static_cast<long>(T) * k);
+      st = experts * (H / 128) >= 8L * cu_count()
+               ? launch_gemm_stream<DOWN, 2, MOE_STREAM_L, MOE_STREAM_BMX_DN>(d, rows_cap, s)
+               : launch_gemm_stream<DOWN, 1, MOE_STREAM_L, MOE_STREAM_BMX_DN>(d, rows_cap, s);
+    } else if (skinny_tiles(T, k, DOWN)) {
       st = launch_gemm_skinny<DOWN>(d, rows_cap, s);
     } else if (I >= 4096) {
       constexpr DecCfg c = DEC_DN_WIDE;
@@ -1234,6 +1608,32 @@ extern "C" int moe_expert_ffn(const void* x, const int32_t* row_token,
   if (r != MOE_OK) return r;
   return moe_ffn_down(workspace, expert_offsets, w2, T, N, k, H, I, dtype,
                       out_rows, stream);
+}
+
+extern "C" int moe_pack_weights(const void* w13, const void* w2, int N, int H, int I,
+                                int dtype, void* w13_panels, void* w2_panels, void* stream) {
+  if (dtype == MOE_F32 || dtype == MOE_BF16_PANELS) return MOE_EUNSUP;
+  const int st = check_ffn_shape(0, N, 1, H, I, dtype);
+  if (st != MOE_OK) return st;
+  if ((w13 == nullptr) != (w13_panels == nullptr) || (w2 == nullptr) != (w2_panels == nullptr))
+    return MOE_EINVAL;
+  if ((w13 && w13 == w13_panels) || (w2 && w2 == w2_panels)) return MOE_EINVAL;
+  hipStream_t s = as_stream(stream);
+  if (w13) {
+    const long chunks = static_cast<long>(N) * 2 * I * H / 8;
+    hipLaunchKernelGGL(pack_panels_kernel<GATEUP>, dim3((chunks + 255) / 256), dim3(256), 0, s,
+                       static_cast<const uint4*>(w13), static_cast<uint4*>(w13_panels), chunks,
+                       static_cast<uint32_t>(2 * I), static_cast<uint32_t>(H),
+                       static_cast<uint32_t>(I));
+  }
+  if (w2) {
+    const long chunks = static_cast<long>(N) * H * I / 8;
+    hipLaunchKernelGGL(pack_panels_kernel<DOWN>, dim3((chunks + 255) / 256), dim3(256), 0, s,
+                       static_cast<const uint4*>(w2), static_cast<uint4*>(w2_panels), chunks,
+                       static_cast<uint32_t>(H), static_cast<uint32_t>(I),
+                       static_cast<uint32_t>(I));
+  }
+  return launch_status();
 }
 
 // ------------------------------------------------------- no allocation

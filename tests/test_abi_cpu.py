@@ -207,3 +207,26 @@ def test_noalloc_ffn_host_checks(lib):
              None) == -1
     assert f(None, None, None, None, None, 0, 8, 2, 2048, 768, 1, None,
              None) == 0                                    # T = 0: nothing
+
+
+def test_pack_weights_host_checks(lib):
+    P = ctypes.c_void_p
+    a, b, c, d = P(0x1000), P(0x2000), P(0x3000), P(0x4000)  # never touched
+    f = lib.moe_pack_weights
+    f.argtypes = [P, P] + [ctypes.c_int] * 4 + [P, P, P]
+    assert f(a, b, 8, 2048, 768, 0, c, d, None) == -2         # fp32: no panels
+    assert f(a, b, 8, 2048, 768, 2, c, d, None) == -2         # already packed
+    assert f(a, b, 8, 2000, 768, 1, c, d, None) == -2         # H % 256
+    assert f(a, b, 8, 2048, 700, 1, c, d, None) == -2         # I % 128
+    assert f(a, b, 0, 2048, 768, 1, c, d, None) == -1         # no experts
+    assert f(a, b, 8, 2048, 768, 1, None, d, None) == -1      # w13 unpaired
+    assert f(a, None, 8, 2048, 768, 1, c, d, None) == -1      # w2 unpaired
+    assert f(a, b, 8, 2048, 768, 1, a, d, None) == -1         # in place
+    assert f(a, b, 8, 2048, 768, 1, c, b, None) == -1
+    # the FFN calls accept the packed format code with the bf16 shape rules
+    g = lib.moe_expert_ffn_noalloc
+    g.argtypes = [P] * 5 + [ctypes.c_int] * 6 + [P, P]
+    assert g(a, a, a, a, a, 4, 8, 2, 200, 768, 2, a, None) == -2
+    assert g(a, a, a, a, a, 4, 8, 2, 2048, 768, 3, a, None) == -2  # unknown
+    assert g(None, None, None, None, None, 0, 8, 2, 2048, 768, 2, None,
+             None) == 0
