@@ -115,11 +115,11 @@ __device__ __forceinline__ uint32_t weight_k0(const Args& a, uint32_t kelem) {
   return a.panels ? (kelem / PANEL_K) * PANEL_BLOCK + ((kelem % PANEL_K) / 16) * 1024 : kelem * 2;
 }
 
-// Locate the tile of this workgroup.  cum: LDS [N+2], the cumulative tile
-// counts and then the total.  Returns false for surplus workgroups.
+// Tile table: cum (LDS [N+2]) receives the cumulative tile counts of the
+// experts (BM-row tiles times a.n_tiles column tiles) and then the total,
+// which is returned (after a barrier) to every thread.
 template <int BM>
-__device__ bool find_tile(const Args& a, int* cum, int& j, int& m0, int& nt,
-                          int& Mj, int& row0) {
+__device__ int tile_table(const Args& a, int* cum) {
   int* s_total = cum + a.N + 1;
   if (threadIdx.x < MOE_WAVE) {
     int acc = 0;
@@ -140,13 +140,14 @@ __device__ bool find_tile(const Args& a, int* cum, int& j, int& m0, int& nt,
     }
   }
   __syncthreads();
-  const int total = *s_total;
-  const int p = blockIdx.x;
-  const int q = (total + 7) / 8;  // tiles per XCD
-  const int slot = p / 8;
-  if (slot >= q) return false;
-  const int L = (p % 8) * q + slot;
-  if (L >= total) return false;
+  return *s_total;
+}
+
+// Tile L of the table: expert j (rows row0 .. row0 + Mj - 1), token rows
+// m0 .. m0 + BM - 1 of it, column tile nt.
+template <int BM>
+__device__ __forceinline__ void locate_tile(const Args& a, const int* cum, int L, int& j,
+                                            int& m0, int& nt, int& Mj, int& row0) {
   int lo = 0, hi = a.N - 1;  // last expert with cum[e] <= L
   while (lo < hi) {
     const int mid = (lo + hi + 1) / 2;
@@ -159,6 +160,21 @@ __device__ bool find_tile(const Args& a, int* cum, int& j, int& m0, int& nt,
   const int r = L - cum[j];
   nt = r / mt;
   m0 = (r % mt) * BM;
+}
+
+// Locate the tile of this workgroup.  cum: LDS [N+2], the cumulative tile
+// counts and then the total.  Returns false for surplus workgroups.
+template <int BM>
+__device__ bool find_tile(const Args& a, int* cum, int& j, int& m0, int& nt,
+                          int& Mj, int& row0) {
+  const int total = tile_table<BM>(a, cum);
+  const int p = blockIdx.x;
+  const int q = (total + 7) / 8;  // tiles per XCD
+  const int slot = p / 8;
+  if (slot >= q) return false;
+  const int L = (p % 8) * q + slot;
+  if (L >= total) return false;
+  locate_tile<BM>(a, cum, L, j, m0, nt, Mj, row0);
   return true;
 }
 
@@ -934,12 +950,16 @@ __device__ __forceinline__ void stream_body(const Args& a, unsigned char* smem, 
   // Both operands are requested L slices ahead, the token rows of a slice
   // just before its weights: a wait for the token rows of slice kt + 1
   // (in-order completion) then leaves the weights of slices kt + 1 ..
-  // kt + L in flight.  Prologue: slices 0 .. L-1, and slice 0's token rows
-  // in LDS (nk >= 2: K is a multiple of 128).
-  static_for<L>([&](auto i) {
-    if (decltype(i)::value < nk) {
-      load_a(decltype(i)::value, i);
-      load_b(decltype(i)::value, i);
+  // kt + L in flight.  Prologue: slices 0 .. L-1 (the weights of slice 0
+  // first: they need no row_token read), and slice 0's token rows in LDS
+  // (nk >= 2: K is a multiple of 128).
+  load_b(0, std::integral_constant<int, 0>{});
+  load_a(0, std::integral_constant<int, 0>{});
+  static_for<L - 1>([&](auto i) {
+    constexpr int I1 = decltype(i)::value + 1;
+    if (I1 < nk) {
+      load_b(I1, std::integral_constant<int, I1>{});
+      load_a(I1, std::integral_constant<int, I1>{});
     }
   });
   store_a(0, std::integral_constant<int, 0>{});
@@ -1015,37 +1035,39 @@ __device__ __forceinline__ void stream_body(const Args& a, unsigned char* smem, 
   }
 }
 
-// The token-row tile height is chosen on the device from the largest
-// expert (every workgroup reads the same offsets, so all take the same
-// branch): 32, 64 or 128 rows, larger experts in several 128-row tiles.
+// Experts are cut into tiles of up to BMX token rows; each tile runs the
+// body of the smallest height (32, 64 or 128) that holds its rows.  The
+// grid is at most the number of workgroups the CUs hold at once, and each
+// workgroup walks its XCD's range of tiles (the tiles of one expert and
+// panel stay on one XCD and share its L2), so no workgroup is launched
+// only to find that it has no tile.
 template <int MODE, int NPW, int L, int BMX>
 __global__ __launch_bounds__(4 * MOE_WAVE) void gemm_stream_kernel(Args a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  int* cum = reinterpret_cast<int*>(smem);
-  int* s_most = cum + a.N + 2;
-  if (threadIdx.x < MOE_WAVE) {
-    int mx = 0;
-    for (int j0 = 0; j0 < a.N; j0 += MOE_WAVE) {
-      const int e = j0 + lane_id();
-      mx = max(mx, wave_max(e < a.N ? a.offsets[e + 1] - a.offsets[e] : 0));
-    }
-    if (threadIdx.x == 0) *s_most = mx;
-  }
-  __syncthreads();
-  const int most = *s_most;
-  __syncthreads();  // the tile search rewrites the table
-  int j, m0, nt, Mj, row0;
-  if (BMX == 32 || most <= 32) {
-    if (find_tile_s<32>(a, cum, j, m0, nt, Mj, row0))
+  int* cum = reinterpret_cast<int*>(smem + 2 * BMX * 64 * 2);  // after the A stages
+  const int total = tile_table<BMX>(a, cum);
+  const int p = blockIdx.x;
+  const int q = (total + 7) / 8;  // tiles per XCD
+  const int step = gridDim.x / 8;
+  for (int slot = p / 8; slot < q; slot += step) {
+    const int Lt = (p % 8) * q + slot;
+    if (Lt >= total) break;
+    int j, m0, nt, Mj, row0;
+    locate_tile<BMX>(a, cum, Lt, j, m0, nt, Mj, row0);
+    j = __builtin_amdgcn_readfirstlane(j);
+    m0 = __builtin_amdgcn_readfirstlane(m0);
+    nt = __builtin_amdgcn_readfirstlane(nt);
+    Mj = __builtin_amdgcn_readfirstlane(Mj);
+    row0 = __builtin_amdgcn_readfirstlane(row0);
+    const int rows = min(BMX, Mj - m0);
+    if (BMX >= 128 && rows > 64) {
+      if constexpr (BMX >= 128) stream_body<MODE, 128, NPW, L>(a, smem, j, m0, nt, Mj, row0);
+    } else if (BMX >= 64 && rows > 32) {
+      if constexpr (BMX >= 64) stream_body<MODE, 64, NPW, L>(a, smem, j, m0, nt, Mj, row0);
+    } else {
       stream_body<MODE, 32, NPW, L>(a, smem, j, m0, nt, Mj, row0);
-  } else if (BMX == 64 || most <= 64) {
-    if constexpr (BMX >= 64)
-      if (find_tile_s<64>(a, cum, j, m0, nt, Mj, row0))
-        stream_body<MODE, 64, NPW, L>(a, smem, j, m0, nt, Mj, row0);
-  } else {
-    if constexpr (BMX >= 128)
-      if (find_tile_s<128>(a, cum, j, m0, nt, Mj, row0))
-        stream_body<MODE, 128, NPW, L>(a, smem, j, m0, nt, Mj, row0);
+    }
+    __syncthreads();  // the next tile's prologue rewrites the A stages
   }
 }
 
@@ -1256,14 +1278,15 @@ __global__ __launch_bounds__(256) void pack_panels_kernel(const uint4* __restric
 
 // Decode tiles on packed weights (gemm_stream_kernel), measured on MI355X
 // (qwen3 and Mixtral decode shapes and the 48-layer sweep layer at batches
-// 32, 128 and 256): weights requested 3 slices ahead (2 is as fast, 4 costs
-// occupancy); gate-up with token-row tiles up to 128 (one tile per expert
-// and panel: the large experts after SERE read their panel once), down
-// with tiles of 32 token rows (more workgroups per CU) and two panels per
-// workgroup when the panels of the experts that may be active number at
-// least twice the workgroup slots (4 per CU), else one.
+// 32, 128 and 256): operands requested 2 slices ahead (3 needs more than
+// 256 registers with the 128-row tiles, halving the workgroups per CU, and
+// is no faster where it fits); gate-up with token-row tiles up to 128 (one
+// tile per expert and panel: the large experts after SERE read their panel
+// once), down with tiles of 32 token rows (more workgroups per CU) and two
+// panels per workgroup when the panels of the experts that may be active
+// number at least twice the workgroup slots (4 per CU), else one.
 #ifndef MOE_STREAM_L
-#define MOE_STREAM_L 3
+#define MOE_STREAM_L 2
 #endif
 #ifndef MOE_STREAM_NPW_GU
 #define MOE_STREAM_NPW_GU 1
@@ -1283,11 +1306,24 @@ __global__ __launch_bounds__(256) void pack_panels_kernel(const uint4* __restric
 template <int MODE, int NPW, int L, int BMX>
 static int launch_gemm_stream(Args a, int rows_cap, hipStream_t s) {
   constexpr int BN = 128 * NPW;
-  // two stages of the tallest token-row tile; the tile table shares them
-  const size_t lds = std::max<size_t>(2 * BMX * 64 * 2, (static_cast<size_t>(a.N) + 3) * 4);
+  // two stages of the tallest token-row tile, then the tile table
+  const size_t lds = 2 * BMX * 64 * 2 + (static_cast<size_t>(a.N) + 2) * 4;
+  const void* fn = reinterpret_cast<const void*>(gemm_stream_kernel<MODE, NPW, L, BMX>);
+  // workgroups one CU holds at once, per device (at most 4 with the
+  // smallest tiles' registers)
+  static std::atomic<int> per_cu[64];
+  const int dev = current_device();
+  int wpc = dev >= 0 ? per_cu[dev].load(std::memory_order_acquire) : 0;
+  if (wpc == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&wpc, fn, 4 * MOE_WAVE, lds) !=
+            hipSuccess ||
+        wpc < 1)
+      wpc = 1;
+    if (dev >= 0) per_cu[dev].store(wpc, std::memory_order_release);
+  }
   a.n_tiles = (MODE == GATEUP ? 2 * a.I : a.NC) / BN;
-  const int mt_ub = (rows_cap + 31) / 32 + std::min(a.N, rows_cap);
-  long grid = static_cast<long>(mt_ub) * a.n_tiles;
+  const int mt_ub = (rows_cap + BMX - 1) / BMX + std::min(a.N, rows_cap);
+  long grid = std::min(static_cast<long>(mt_ub) * a.n_tiles, static_cast<long>(wpc) * cu_count());
   grid = (grid + 7) / 8 * 8;
   hipLaunchKernelGGL((gemm_stream_kernel<MODE, NPW, L, BMX>), dim3(grid), dim3(4 * MOE_WAVE), lds,
                      s, a);
