@@ -291,7 +291,7 @@ int moe_entropy_weights(const void* x, const uint8_t* is_visual, int T, int H,
  *   expert_offsets, row_token, row_slot, slot_row
  *                        as moe_dispatch.
  * kprime == 0 turns SERE off (sim and prot may then be NULL); gamma = +inf
- * turns capacity off.  The workspace holds a control word: fill it with
+ * turns capacity off.  The workspace holds control words: fill it with
  * zero bytes once before its first use; every call leaves it zero again.
  * The batch-wide steps run in one workgroup with every array in LDS, which
  * bounds the batch: moe_routing_workspace_size returns 0 for shapes the

@@ -162,6 +162,14 @@ __device__ __forceinline__ int read_lane(int v, int lane) {
 // counter at zero; LDS and export counters left alone).
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Store visible at agent scope once it completes (written through the
+// XCD's L2, which is not coherent with the other XCDs' L2s): a workgroup
+// that hands results to a workgroup on another XCD stores them this way and
+// waits for its stores, instead of writing back its whole L2.
+__device__ __forceinline__ void store_agent(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Monotone unsigned image of an fp32 value: a > b  <=>  key(a) > key(b);
 // -0.0 is folded onto +0.0 first so the two compare equal.
 __device__ __forceinline__ uint32_t f32_order_key(float f) {

@@ -239,13 +239,14 @@ __device__ __forceinline__ void run(const Args& a, unsigned char* dyn, Lds& L) {
 #pragma unroll
   for (int j = 0; j < SPT; ++j) {
     const int i = tid + j * NT;
-    e_in[j] = i < Tk ? a.topk[i] : -1;
+    // (clamped: an id out of range could never index past an array)
+    e_in[j] = i < Tk ? min(max(a.topk[i], 0), N - 1) : -1;
   }
   int fbv[FPT];
 #pragma unroll
   for (int j = 0; j < FPT; ++j) {
     const int i = tid + j * NT;
-    fbv[j] = i < TR ? a.fb[i] : 0;
+    fbv[j] = i < TR ? min(max(a.fb[i], 0), N - 1) : 0;
   }
   const uint8_t vis = tid < T ? a.vis[tid] : 0;
   const float ew = tid < T ? a.ew[tid] : 0.f;

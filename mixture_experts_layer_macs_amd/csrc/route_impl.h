@@ -45,7 +45,9 @@ __device__ __forceinline__ float group_reduce(float v, float* red) {
 // Route token t, whose N logits start at `row` (global memory or LDS;
 // live == false: a padding group that only joins the workgroup barriers and
 // reads nothing).  Writes topk_ids[t][0..k), topk_gates[t][0..k) and
-// fallback_ids[t][0..R) in rank order.
+// fallback_ids[t][0..R) in rank order; the ids with agent-scope stores, so
+// that another workgroup of the same launch can read them after a
+// hand-off without a write-back of this XCD's L2.
 template <int GT>
 __device__ void route_token(const float* __restrict__ row, int N, int k,
                             int R, int t, bool live, unsigned char* lds,
@@ -114,11 +116,11 @@ __device__ void route_token(const float* __restrict__ row, int N, int k,
     for (int e = g; e < N; e += GT) {
       const int r = rank[e];
       if (r < k) {
-        topk_ids[static_cast<size_t>(t) * k + r] = e;
+        store_agent(&topk_ids[static_cast<size_t>(t) * k + r], e);
         topk_gates[static_cast<size_t>(t) * k + r] =
             expf(rank_key_value(key[e]) - mx) / se;
       } else if (r < k + R) {
-        fallback_ids[static_cast<size_t>(t) * R + (r - k)] = e;
+        store_agent(&fallback_ids[static_cast<size_t>(t) * R + (r - k)], e);
       }
     }
 }
@@ -205,10 +207,10 @@ __device__ void route_token_wave(const float* __restrict__ row, int N, int k,
     for (int c2 = 0; c2 < M; ++c2) r += cand[c2] > kc ? 1 : 0;
     const int e = rank_key_index(kc);
     if (r < k) {
-      topk_ids[static_cast<size_t>(t) * k + r] = e;
+      store_agent(&topk_ids[static_cast<size_t>(t) * k + r], e);
       topk_gates[static_cast<size_t>(t) * k + r] = expf(rank_key_value(kc) - mx) / se;
     } else {
-      fallback_ids[static_cast<size_t>(t) * R + (r - k)] = e;
+      store_agent(&fallback_ids[static_cast<size_t>(t) * R + (r - k)], e);
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");

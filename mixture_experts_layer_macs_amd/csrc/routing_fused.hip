@@ -226,6 +226,9 @@ __device__ void tail(const Args& f, const cap::Args& cg, const disp::Args& dg,
 
 // DT: the batch-wide steps run as dtail::run (decode batches within its
 // limits), else as tail() above.
+// Counters of the hand-off, one per 128 bytes.
+constexpr unsigned TICKET_STRIDE = 32;
+
 template <int GT, bool DT>
 __global__ __launch_bounds__(FT) void routing_kernel(Args f, cap::Args ca,
                                                        disp::Args da, dtail::Args dta) {
@@ -254,23 +257,51 @@ __global__ __launch_bounds__(FT) void routing_kernel(Args f, cap::Args ca,
       pf_on = true;
     }
   }
+  // The tail's arguments are first read by the last workgroup, after the
+  // hand-off; a cold read of the argument block there costs about 1 us.
+  // Every workgroup reads one word of each 64-byte line of it now, so that
+  // the line sits in the scalar cache of the CU that runs the tail.
+  constexpr int ARG_WORDS =
+      static_cast<int>((sizeof(Args) + sizeof(cap::Args) + sizeof(disp::Args) +
+                        sizeof(dtail::Args)) / 4);
+  typedef __attribute__((address_space(4))) const uint32_t karg_word;
+  const karg_word* kargs = (const karg_word*)(__builtin_amdgcn_kernarg_segment_ptr());
+  uint32_t kacc = 0;
+#pragma unroll
+  for (int i = 0; i < ARG_WORDS; i += 16) kacc ^= kargs[i];
   rt::route_token<GT>(f.logits + static_cast<size_t>(t) * f.N, f.N, f.k, f.R, t, t < f.T,
                       smem + grp * rt::token_lds_bytes(f.N, GT), f.topk_ids,
                       f.topk_gates, f.fallback_ids);
 
-  // Hand-off to the last workgroup.  On gfx950 an agent-scope fence writes
-  // back (release) or invalidates (acquire) the XCD's L2, so it is issued
-  // once per workgroup, not once per wave: every wave first waits for its
-  // own stores, the barrier joins them, and one thread fences and counts.
+  // Hand-off to the last workgroup.  The tail reads only the ranked ids of
+  // the route step, which route_token writes with agent-scope stores
+  // (through the XCD's L2): once every wave has waited for its stores they
+  // are visible on every XCD, so the workgroup counts itself without a
+  // release fence (on gfx950 that writes back the whole XCD L2, about 2 us
+  // at this point of a decode step).  More than 8 workgroups count in two
+  // levels, so that no more than a few increments of one counter queue
+  // behind each other: workgroup p counts on counter p % 8 (128 bytes
+  // apart), and the last of each such group on the top counter.  Each count
+  // wraps to zero (atomicInc's limit), leaving the workspace zero.  The last
+  // workgroup invalidates its L2 (acquire) before reading the ids; a single
+  // workgroup reads its own stores.
   wait_stores();
   // never true (T >= 0): only keeps the warming loads from being dropped
   if (pf_on && f.T < 0 && (pf.x | pf.y | pf.z | pf.w) == 0) s_last = 0;
+  if (f.T < 0 && kacc == 0) s_last = 0;
   __syncthreads();
   if (threadIdx.x == 0) {
-    __threadfence();
-    const unsigned prev = atomicInc(f.ticket, gridDim.x - 1);
-    s_last = prev == gridDim.x - 1;
-    if (s_last) __threadfence();  // see every other workgroup's results
+    const unsigned G = gridDim.x, x = blockIdx.x % 8;
+    bool last = true;  // a single workgroup hands off to itself
+    if (G > 8) {
+      const unsigned nx = G / 8 + (x < G % 8 ? 1u : 0u);  // members of group x
+      last = atomicInc(f.ticket + TICKET_STRIDE * (1 + x), nx - 1) == nx - 1 &&
+             atomicInc(f.ticket, 7u) == 7u;
+    } else if (G > 1) {
+      last = atomicInc(f.ticket, G - 1) == G - 1;
+    }
+    s_last = last;
+    if (last && G > 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
   if (!s_last) return;
@@ -297,7 +328,7 @@ inline bool supported(int T, int N, int k, int R) {
   return tail_layout(T, N, k, R, FT / MOE_WAVE).bytes <= TAIL_LDS_MAX;
 }
 
-constexpr size_t WS_BYTES = 256;  // the ticket
+constexpr size_t WS_BYTES = 9 * TICKET_STRIDE * 4;  // the two-level ticket
 
 }  // namespace fused
 }  // namespace moe
