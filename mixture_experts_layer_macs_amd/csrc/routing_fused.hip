@@ -226,6 +226,9 @@ __device__ void tail(const Args& f, const cap::Args& cg, const disp::Args& dg,
 
 // DT: the batch-wide steps run as dtail::run (decode batches within its
 // limits), else as tail() above.
+#ifndef MOE_SIM_LDS_MIN_SLOTS
+#define MOE_SIM_LDS_MIN_SLOTS 64
+#endif
 // Counters of the hand-off, one per 128 bytes.
 constexpr unsigned TICKET_STRIDE = 32;
 
@@ -460,7 +463,9 @@ extern "C" int moe_routing_fused(
     d.gamma = gamma;
     d.lam = lam;
     d.cap_on = !std::isinf(gamma);
-    d.sim_lds = kprime > 0 && N <= dtail::SIM_LDS_N;
+    // S and Prot go to LDS for the SERE step unless the batch is so small
+    // that the few rows it reads cost less from memory than the copy
+    d.sim_lds = kprime > 0 && N <= dtail::SIM_LDS_N && T * k > MOE_SIM_LDS_MIN_SLOTS;
     d.slot_sere = slot_sere;
     d.slot_expert = slot_expert;
     d.flags = flags;
