@@ -140,23 +140,28 @@ __device__ void route_token(const float* __restrict__ row, int N, int k,
 //      this wave's own) and each one's rank is the number of selected keys
 //      that beat it.
 // A dead token (live == false) returns at once: the wave takes no part in
-// any workgroup barrier.
+// any workgroup barrier.  ranked (optional, LDS or global): the k + R ids in
+// rank order, for a consumer in the same workgroup.
 template <int KPL>
 __device__ void route_token_wave(const float* __restrict__ row, int N, int k,
                                  int R, int t, bool live, uint64_t* cand,
                                  int32_t* __restrict__ topk_ids,
                                  float* __restrict__ topk_gates,
-                                 int32_t* __restrict__ fallback_ids) {
+                                 int32_t* __restrict__ fallback_ids,
+                                 int32_t* ranked = nullptr) {
   if (!live) return;
   const int lane = lane_id();
   const int M = k + R;
   float v[KPL];
   uint32_t u[KPL];
   float mx = -INFINITY;
+  // every load issued before the first use (clamped index: a lane past N
+  // reads a valid logit and ignores it)
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) v[i] = row[min(lane + MOE_WAVE * i, N - 1)];
 #pragma unroll
   for (int i = 0; i < KPL; ++i) {
     const int j = lane + MOE_WAVE * i;
-    v[i] = j < N ? row[j] : 0.f;
     u[i] = j < N ? f32_order_key(v[i]) : 0u;  // 0: below every finite key
     if (j < N) mx = fmaxf(mx, v[i]);
   }
@@ -206,6 +211,7 @@ __device__ void route_token_wave(const float* __restrict__ row, int N, int k,
     int r = 0;
     for (int c2 = 0; c2 < M; ++c2) r += cand[c2] > kc ? 1 : 0;
     const int e = rank_key_index(kc);
+    if (ranked) ranked[r] = e;
     if (r < k) {
       store_agent(&topk_ids[static_cast<size_t>(t) * k + r], e);
       topk_gates[static_cast<size_t>(t) * k + r] = expf(rank_key_value(kc) - mx) / se;

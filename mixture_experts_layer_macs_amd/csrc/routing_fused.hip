@@ -29,6 +29,7 @@
 #include "dtail_impl.h"
 #include "route_impl.h"
 #include "sere_impl.h"
+#include "tiny_impl.h"
 
 namespace moe {
 namespace fused {
@@ -477,6 +478,26 @@ extern "C" int moe_routing_fused(
     d.row_token = row_token;
     d.row_slot = row_slot;
     d.slot_row = slot_row;
+  }
+  // Batches of at most 8 tokens and 64 slots: one workgroup, every
+  // batch-wide step in one wave.
+#ifndef MOE_TINY_ROUTING
+#define MOE_TINY_ROUTING 1
+#endif
+  if (MOE_TINY_ROUTING && tiny::supported(T, N, k, R)) {
+    tiny::Args ta{};
+    ta.d = d;
+    ta.logits = logits;
+    ta.topk_ids = topk_ids;
+    ta.topk_gates = topk_gates;
+    ta.fallback_ids = fallback_ids;
+    auto launch_tiny = [&](auto kern) -> int {
+      hipLaunchKernelGGL(kern, dim3(1), dim3(tiny::threads(T)), 0, s, ta);
+      return launch_status();
+    };
+    if (N <= 64) return launch_tiny(tiny::routing_kernel<1>);
+    if (N <= 128) return launch_tiny(tiny::routing_kernel<2>);
+    return launch_tiny(tiny::routing_kernel<4>);
   }
   const size_t route_lds = static_cast<size_t>(TPB) * rt::token_lds_bytes(N, GT);
   const size_t lds = dt ? std::max(route_lds, dtail::dyn_lds(N, d.sim_lds))

@@ -303,6 +303,54 @@ def test_adversarial_routing(variant, fused):
     assert_routing_equal(g, rt, inp)
 
 
+# Batches of at most 8 tokens and 64 slots take the one-workgroup path of
+# the fused launch.  These shapes walk its limits and branches: S and Prot
+# copied to LDS (N <= 128; N*N a multiple of 16 or not) or read from memory
+# (N > 128), SERE off / on / K' = k, capacity off, R = 0, expert groups,
+# capacities tight enough to run the fallback rounds, tied logits and
+# similarities, NaN and out-of-range entropy weights.
+TINY_CASES = [
+    # name, T, N, k, R, group, gamma, K', rho, seed
+    ("t1_n12_k4", 1, 12, 4, 3, 12, 0.3, 1, 0.5, 500),
+    ("t2_n12_k4_tight", 2, 12, 4, 3, 12, 0.3, 1, 0.25, 501),
+    ("t3_n50_groups", 3, 50, 4, 6, 10, 0.5, 2, 0.0, 502),
+    ("t5_n12_k8", 5, 12, 8, 4, 12, 0.2, 2, 0.25, 503),
+    ("t8_n12_64_slots", 8, 12, 8, 4, 12, 0.3, 1, 0.5, 504),
+    ("t8_n128_r8", 8, 128, 8, 8, 128, 0.5, 2, 0.25, 505),
+    ("t4_n99_odd", 4, 99, 5, 8, 33, 0.4, 2, 0.0, 506),
+    ("t6_n200_sere_from_memory", 6, 200, 6, 8, 200, 0.4, 3, 0.0, 507),
+    ("t8_n256_groups", 8, 256, 8, 8, 64, 0.3, 2, 0.0, 508),
+    ("t7_cap_off", 7, 40, 8, 8, 40, math.inf, 2, 0.0, 509),
+    ("t3_r0", 3, 24, 6, 0, 24, 0.3, 1, 0.0, 510),
+    ("t8_sere_off", 8, 64, 8, 8, 16, 0.4, 0, 0.5, 511),
+    ("t2_kprime_eq_k", 2, 16, 4, 4, 16, 0.3, 4, 0.0, 512),
+    ("t1_k1", 1, 8, 1, 7, 8, 1.0, 1, 0.0, 513),
+    ("t8_k1_tight", 8, 9, 1, 8, 9, 0.25, 1, 0.0, 514),
+    # many fallback placements (15, 16, 11), and under expert groups (13, 11)
+    ("t8_n32_placed", 8, 32, 8, 8, 32, 0.7, 1, 0.25, 902),
+    ("t8_n32_placed_sere_off", 8, 32, 8, 8, 32, 0.5, 0, 0.25, 902),
+    ("t6_n16_placed", 6, 16, 8, 8, 16, 0.9, 1, 0.25, 900),
+    ("t8_n32_placed_groups", 8, 32, 8, 8, 16, 0.9, 0, 0.25, 900),
+    ("t8_n16_placed_groups", 8, 16, 4, 8, 8, 1.2, 0, 0.25, 903),
+]
+
+
+@pytest.mark.parametrize("case", TINY_CASES, ids=[c[0] for c in TINY_CASES])
+def test_tiny_batch_routing(case):
+    """Tiny batches: the fused launch equals the separate calls bit for bit
+    (gates included) and the oracle."""
+    name, T, N, k, R, group, gamma, kprime, rho, seed = case
+    say(f"tiny-batch routing {name} T={T} N={N} k={k} R={R} K'={kprime}")
+    inp = _adversarial_inputs(seed, T=T, N=N, k=k, R=R)
+    inp.update(group=group, gamma=gamma, kprime=kprime, rho=rho)
+    rt = O.layer_routing(inp)
+    a = run_gpu_layer(inp, tokens_out=False, fused=False)
+    b = run_gpu_layer(inp, tokens_out=False, fused=True)
+    for key in a:
+        np.testing.assert_array_equal(np.asarray(a[key]), np.asarray(b[key]), key)
+    assert_routing_equal(b, rt, inp)
+
+
 def test_fused_workspace_reuse():
     """One fused-routing workspace serves batches of different sizes and
     routing settings back to back (its control words reset themselves)."""
