@@ -819,6 +819,143 @@ __global__ __launch_bounds__(4 * MOE_WAVE) void gemm_skinny_kernel(Args a) {
   }
 }
 
+// ------------------------------------------- decode GEMV on packed panels
+// With a few token rows per active expert (a decode batch of a few tokens)
+// the product is a matrix-vector product per expert: the weight bytes are
+// everything and a 32 x 32 MFMA tile would be mostly empty.  In the panel
+// layout a 32-row group of a 64-wide K slice is 4 KB of contiguous bytes,
+// four 1 KB loads of one wave (lane l: row l % 32, elements 8 (l / 32) ..
+// +7 of each 16-wide K step), so a wave that owns a row group streams long
+// contiguous runs, and holds every load of its share in registers at once.
+//
+// Workgroup: one (expert, chunk of up to MR token rows, 32-row group); its
+// 4 waves split the K slices into quarters.  The token operand is staged in
+// LDS: for gate-up every token of the batch (at most GEMV_MAX_T, so that no
+// load waits for row_token), for down the tile's rows of h.  Its loads are
+// issued first and the weight loads right after; the workgroup waits for
+// the token rows only, so it crosses the barrier with every weight load in
+// flight and the multiply of a K slice waits for that slice alone.  Each
+// lane accumulates, per token row, its row's dot product over its half of
+// every K step in fp32 (v_dot2 on bf16 pairs); the two halves are added
+// across lanes l and l + 32, the four quarters in LDS in wave order, and
+// wave 0 writes the outputs: for gate-up the group's 16 gate rows and 16 up
+// rows give 16 h columns (silu(gate) * up), for down 32 output columns.
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+constexpr int GEMV_MAX_K = 2048;  // K <= 2048: a wave's K slices fit its registers
+constexpr int GEMV_MAX_T = 8;     // gate-up: tokens staged whole
+
+// 8 bf16 products added to acc in element order (pairs by v_dot2).  The
+// words are copied out of the vectors first: a bit cast of a subscripted
+// vector element compiles to a read of element 0.
+__device__ __forceinline__ float dot8(const u32x4 w, const u32x4 x, float acc) {
+  const uint32_t wa[4] = {w.x, w.y, w.z, w.w}, xa[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, wa[i]),
+                                          __builtin_bit_cast(bf16x2v, xa[i]), acc, false);
+  return acc;
+}
+
+// NBW = K / 256: the K slices of one wave (a compile-time count, so that
+// the compiler's wait for the token rows leaves every weight load alone).
+template <int MODE, int MR, int NBW>
+__global__ __launch_bounds__(4 * MOE_WAVE) void gemv_kernel(Args a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int XR = MODE == GATEUP ? GEMV_MAX_T : MR;  // staged token rows
+  const int K = a.K;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / MOE_WAVE);
+  unsigned char* xs = smem;                                                       // [XR][K] bf16
+  float* red = reinterpret_cast<float*>(smem + static_cast<size_t>(XR) * K * 2);  // [4][MR][32]
+  int* cum = reinterpret_cast<int*>(red + 4 * MR * 32);                          // [N + 2]
+  int j, m0, gi, Mj, row0;
+  if (!find_tile_s<MR>(a, cum, j, m0, gi, Mj, row0)) return;
+  const int rows = min(MR, Mj - m0);
+  const int nstage = MODE == GATEUP ? a.a_rows : rows;
+
+  // token rows: thread i stages 16-byte chunk i of every row (K <= 2048:
+  // at most 256 chunks a row; clamped loads, the extra ones unused)
+  const int cpr = K / 8;  // chunks per row
+  const int ch = min(tid, cpr - 1);
+  u32x4 xv[XR];
+#pragma unroll
+  for (int r = 0; r < XR; ++r) {
+    const int rr = min(r, nstage - 1);
+    const int src = MODE == GATEUP ? rr : row0 + m0 + rr;
+    xv[r] = *reinterpret_cast<const u32x4*>(a.a + static_cast<size_t>(src) * K + ch * 8);
+  }
+  // this wave's K slices
+  const int nb = 4 * NBW, b0 = wave * NBW;
+  const unsigned char* wb =
+      reinterpret_cast<const unsigned char*>(a.w + static_cast<size_t>(j) * a.w_stride) +
+      (static_cast<size_t>(gi / 4) * nb + b0) * PANEL_BLOCK + ((gi % 4) * 4 * 64 + lane) * 16;
+  u32x4 wv[NBW][4];
+#pragma unroll
+  for (int i = 0; i < NBW; ++i)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      wv[i][kk] = *reinterpret_cast<const u32x4*>(wb + static_cast<size_t>(i) * PANEL_BLOCK + kk * 1024);
+  __builtin_amdgcn_sched_barrier(0);  // keep every weight request ahead of the waits
+  // gate-up: the staged row of each tile row (scalar loads)
+  int xrow[MR];
+#pragma unroll
+  for (int r = 0; r < MR; ++r)
+    xrow[r] = MODE == GATEUP ? min(max(a.row_token[row0 + m0 + min(r, rows - 1)], 0), nstage - 1)
+                             : r;
+#pragma unroll
+  for (int r = 0; r < XR; ++r)
+    if (r < nstage && tid < cpr)
+      *reinterpret_cast<u32x4*>(xs + (static_cast<size_t>(r) * cpr + tid) * 16) = xv[r];
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // this thread's LDS stores (lgkmcnt 0)
+  wg_barrier();                        // the weight loads stay in flight
+
+  typedef __attribute__((address_space(3))) const u32x4 lds_u4;
+  typedef __attribute__((address_space(3))) const unsigned char lds_b;
+  const int half = lane / 32;
+  float acc[MR];
+#pragma unroll
+  for (int r = 0; r < MR; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int i = 0; i < NBW; ++i) {
+    const int kb = (b0 + i) * 64 + half * 8;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int r = 0; r < MR; ++r)
+        if (r < rows) {
+          const u32x4 x = *(lds_u4*)((lds_b*)(xs) + (static_cast<size_t>(xrow[r]) * K + kb + kk * 16) * 2);
+          acc[r] = dot8(wv[i][kk], x, acc[r]);
+        }
+  }
+  // halves (lanes l, l + 32), then the quarters in wave order
+#pragma unroll
+  for (int r = 0; r < MR; ++r) acc[r] += __shfl_xor(acc[r], 32);
+  if (lane < 32)
+#pragma unroll
+    for (int r = 0; r < MR; ++r) red[(wave * MR + r) * 32 + lane] = acc[r];
+  __syncthreads();
+  if (wave != 0) return;
+  const int t = lane % 32;
+#pragma unroll
+  for (int r = 0; r < MR; ++r) {
+    if (r >= rows) break;
+    float v = red[r * 32 + t];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) v += red[(w * MR + r) * 32 + t];
+    const size_t orow = static_cast<size_t>(row0 + m0 + r) * a.NC;
+    if constexpr (MODE == GATEUP) {
+      // tile rows 0..15 of the group: gate of h columns 64 P + 16 G + t, 16..31: up
+      const float up = __shfl(v, (lane & 15) + 16);
+      if (lane < 16) {
+        const uint32_t hv = pack_bf16x2(silu(v) * up, 0.f);
+        a.out[orow + (gi / 4) * 64 + (gi % 4) * 16 + lane] = static_cast<uint16_t>(hv);
+      }
+    } else {
+      if (lane < 32) a.out[orow + gi * 32 + lane] = static_cast<uint16_t>(pack_bf16x2(v, 0.f));
+    }
+  }
+}
+
 // ----------------------------------------------- decode tiles on panels
 // Decode batches are bound by the weight stream: each active expert's
 // panel is read once, and the rate at which those bytes arrive is the rate
@@ -1247,6 +1384,60 @@ static int launch_gemm_skinny(Args a, int rows_cap, hipStream_t s) {
   return MOE_OK;
 }
 
+// Decode GEMV on packed panels (see gemv_kernel): one workgroup per
+// (expert, MR token rows, 32-row group).
+template <int MODE, int MR, int NBW>
+static int launch_gemv(Args a, int rows_cap, hipStream_t s) {
+  a.n_tiles = (MODE == GATEUP ? 2 * a.I : a.NC) / 32;
+  constexpr int XR = MODE == GATEUP ? GEMV_MAX_T : MR;
+  const size_t lds = static_cast<size_t>(XR) * a.K * 2 + 4 * MR * 32 * 4 +
+                     static_cast<size_t>(a.N + 2) * 4;
+  const void* fn = reinterpret_cast<const void*>(gemv_kernel<MODE, MR, NBW>);
+  if (lds > 65536 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         static_cast<int>(lds)) != hipSuccess)
+    return MOE_EHIP;
+  const int mt_ub = (rows_cap + MR - 1) / MR + std::min(a.N, rows_cap);
+  long grid = static_cast<long>(mt_ub) * a.n_tiles;
+  grid = (grid + 7) / 8 * 8;
+  hipLaunchKernelGGL((gemv_kernel<MODE, MR, NBW>), dim3(grid), dim3(4 * MOE_WAVE), lds, s, a);
+  return MOE_OK;
+}
+
+// GEMV for decode batches of at most MOE_GEMV_ROWS dispatch rows (and, for
+// gate-up, at most GEMV_MAX_T tokens) on packed weights whose reduction
+// length is a multiple of 256 up to GEMV_MAX_K.  Each workgroup makes one
+// pass over its weights, so the path pays off while its workgroups fit the
+// CUs at once: measured on the qwen3 shape in a chain of layers, batch 1
+// (8 rows) 33.6 -> 32.5 us per layer, batch 2 (16 rows) 47.1 -> 41.7 us,
+// but batch 8 (64 rows, ~1400 workgroups) 69.7 -> 78.1 us.
+#ifndef MOE_GEMV_ROWS
+#define MOE_GEMV_ROWS 16
+#endif
+static bool gemv_nbw_ok(int K) {
+  const int nbw = K / 256;
+  return K % 256 == 0 && (nbw == 1 || nbw == 2 || nbw == 3 || nbw == 4 || nbw == 8);
+}
+static bool gemv_ok(int mode, int T, int k, int K, bool panels) {
+  return panels && static_cast<long>(T) * k <= MOE_GEMV_ROWS && gemv_nbw_ok(K) &&
+         (mode == DOWN || T <= GEMV_MAX_T);
+}
+template <int MODE, int MR>
+static int launch_gemv_k(const Args& a, int rows_cap, hipStream_t s) {
+  switch (a.K / 256) {
+    case 1: return launch_gemv<MODE, MR, 1>(a, rows_cap, s);
+    case 2: return launch_gemv<MODE, MR, 2>(a, rows_cap, s);
+    case 3: return launch_gemv<MODE, MR, 3>(a, rows_cap, s);
+    case 4: return launch_gemv<MODE, MR, 4>(a, rows_cap, s);
+    default: return launch_gemv<MODE, MR, 8>(a, rows_cap, s);
+  }
+}
+template <int MODE>
+static int launch_gemv_rows(const Args& a, int rows_cap, hipStream_t s) {
+  static_assert(MOE_GEMV_ROWS <= 64, "token-row chunks of 4 or 16");
+  return rows_cap <= 16 ? launch_gemv_k<MODE, 4>(a, rows_cap, s)
+                        : launch_gemv_k<MODE, 16>(a, rows_cap, s);
+}
+
 // ------------------------------------------------------- weight packing
 // One thread per 16-byte chunk (8 elements) of the packed matrix: chunk q of
 // an expert's block is (block, group G, K step kk, lane l), holding elements
@@ -1528,7 +1719,9 @@ extern "C" int moe_ffn_gate_up(const void* x, const int32_t* row_token,
   if (decode_tiles(T, N, k)) {
     int st;
     g.n_tiles = I / 64;
-    if (MOE_STREAM_GU && g.panels && !skinny_tiles(T, k, GATEUP)) {
+    if (gemv_ok(GATEUP, T, k, H, g.panels)) {
+      st = launch_gemv_rows<GATEUP>(g, rows_cap, s);
+    } else if (MOE_STREAM_GU && g.panels && !skinny_tiles(T, k, GATEUP)) {
       st = launch_gemm_stream<GATEUP, MOE_STREAM_NPW_GU, MOE_STREAM_L, MOE_STREAM_BMX_GU>(g, rows_cap, s);
     } else if (skinny_tiles(T, k, GATEUP)) {
       st = launch_gemm_skinny<GATEUP>(g, rows_cap, s);
@@ -1590,7 +1783,9 @@ extern "C" int moe_ffn_down(const void* h, const int32_t* expert_offsets,
   if (decode_tiles(T, N, k)) {
     int st;
     const bool narrow = narrow_decode_tiles(T, N, k, H / 256);
-    if (MOE_STREAM_DN && d.panels && !skinny_tiles(T, k, DOWN)) {
+    if (gemv_ok(DOWN, T, k, I, d.panels)) {
+      st = launch_gemv_rows<DOWN>(d, rows_cap, s);
+    } else if (MOE_STREAM_DN && d.panels && !skinny_tiles(T, k, DOWN)) {
       const long experts = std::min(static_cast<long>(N), static_cast<long>(T) * k);
       st = experts * (H / 128) >= 8L * cu_count()
                ? launch_gemm_stream<DOWN, 2, MOE_STREAM_L, MOE_STREAM_BMX_DN>(d, rows_cap, s)

@@ -6,9 +6,12 @@
    stored as blocks of 64 K elements in MFMA operand order), independent of
    the kernel's index arithmetic, and compared bit for bit.
 2. The expert FFN on packed weights equals the FFN on the row layout bit for
-   bit on every kernel path (16-row panels, decode tiles of both heights,
-   256-row down tiles, reductions of 4096 and more, prefill tiles), since
-   only the addresses of the weight loads differ.
+   bit on every kernel path the two layouts share (16-row panels, decode
+   tiles of both heights, 256-row down tiles, reductions of 4096 and more,
+   prefill tiles), since only the addresses of the weight loads differ.
+   Decode batches of a few rows per expert take the GEMV on packed weights
+   (fp32 sums in another order): there the packed result agrees with the
+   row layout to the bf16 bound, and its three entry points bit for bit.
 3. A whole layer on packed weights matches the oracle to the bf16 bound.
 """
 import numpy as np
@@ -64,26 +67,28 @@ def _mid(**kw):
 
 
 PATH_CASES = [
+    # name, workload, both layouts on the same kernels
     # decode tiles (device-chosen heights), 256-row down tiles
-    ("qwen3_decode_b128", configs.QWEN3_DECODE),
+    ("qwen3_decode_b128", configs.QWEN3_DECODE, True),
     # few active experts after SERE: one wave of tiles, 128-row down tiles
-    ("sweep_b128_k2", configs.SWEEP_LAYER.with_(T=128, kprime=2)),
-    ("sweep_b32", configs.SWEEP_LAYER.with_(T=32, kprime=0)),
-    # 16-row weight panels (gate-up and down), then gate-up only
-    ("sweep_b1", configs.SWEEP_LAYER.with_(T=1, kprime=1)),
-    ("sweep_b4", configs.SWEEP_LAYER.with_(T=4, kprime=0)),
-    ("skinny_h4096", _mid(T=3, H=4096, I=512, k=2)),
-    ("skinny_i4096", _mid(T=2, H=512, I=4096)),
+    ("sweep_b128_k2", configs.SWEEP_LAYER.with_(T=128, kprime=2), True),
+    ("sweep_b32", configs.SWEEP_LAYER.with_(T=32, kprime=0), True),
+    # packed: the decode GEMV (both halves); rows: 16-row weight panels
+    ("sweep_b1", configs.SWEEP_LAYER.with_(T=1, kprime=1), False),
+    ("sweep_b4", configs.SWEEP_LAYER.with_(T=4, kprime=0), False),
+    # packed: 16-row panels for the K = 4096 half, the GEMV for the other
+    ("skinny_h4096", _mid(T=3, H=4096, I=512, k=2), False),
+    ("skinny_i4096", _mid(T=2, H=512, I=4096), False),
     # reductions of 4096 and more on the decode tiles
-    ("mixtral_decode_t64", configs.MIXTRAL_DECODE),
+    ("mixtral_decode_t64", configs.MIXTRAL_DECODE, True),
     # prefill tiles, ragged tails, 6 panels of 64-wide K blocks
-    ("mid_prefill", _mid()),
-    ("mid_prefill_h768_i384", _mid(H=768, I=384, T=300)),
+    ("mid_prefill", _mid(), True),
+    ("mid_prefill_h768_i384", _mid(H=768, I=384, T=300), True),
 ]
 
 
-@pytest.mark.parametrize("name,wl", PATH_CASES, ids=[c[0] for c in PATH_CASES])
-def test_panels_ffn_equals_row_layout(name, wl):
+@pytest.mark.parametrize("name,wl,same", PATH_CASES, ids=[c[0] for c in PATH_CASES])
+def test_panels_ffn_equals_row_layout(name, wl, same):
     B = load_binding()
     say(f"panels ffn {name} T={wl.T} H={wl.H} N={wl.N} k={wl.k} I={wl.I}")
     inp = synth.make_inputs(wl, 0)
@@ -107,15 +112,21 @@ def test_panels_ffn_equals_row_layout(name, wl):
     torch.cuda.synchronize()
     M = int(off[-1].item())
     assert M > 0
-    a = ref[:M].contiguous().view(torch.int16)
-    assert torch.equal(a, out[:M].contiguous().view(torch.int16))
-    assert torch.equal(a, out2[:M].contiguous().view(torch.int16))
+    bits = lambda t: t[:M].contiguous().view(torch.int16)
+    a = bits(out)
+    assert torch.equal(a, bits(out2))
     if wl.T * wl.k * wl.I * 2 <= B.FFN_NOALLOC_MAX_BYTES:
         out3 = torch.full_like(ref, float("nan"))
         B.moe_expert_ffn_noalloc(d["x"], rt, off, p13, p2, wl.k, out3, panels=True)
         torch.cuda.synchronize()
-        assert torch.equal(a, out3[:M].contiguous().view(torch.int16))
-    say(f"  {M} rows bit-identical")
+        assert torch.equal(a, bits(out3))
+    if same:
+        assert torch.equal(bits(ref), a)
+        say(f"  {M} rows bit-identical")
+    else:
+        f64 = lambda t: t[:M].float().cpu().numpy().astype(np.float64)
+        assert_y_close(f64(out), f64(ref), "bf16")
+        say(f"  {M} rows: packed entry points bit-identical, rows to the bf16 bound")
 
 
 @pytest.mark.parametrize("name,wl", [
