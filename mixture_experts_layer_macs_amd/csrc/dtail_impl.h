@@ -27,6 +27,7 @@
 #pragma once
 
 #include <cmath>
+#include <type_traits>
 
 #include "common.h"
 
@@ -112,6 +113,17 @@ __device__ __forceinline__ uint32_t peer_prefix(uint64_t peers, bool valid, uint
     local += static_cast<uint32_t>(__popcll(m & plane)) << b;
   }
   return local;
+}
+
+// Makes a loaded value live in a register at this point: a batch of
+// independent LDS reads followed by pin() of each value costs one wait,
+// where the compiler would otherwise sink each read into the branch that
+// uses it and wait for each in turn.
+template <class T>
+__device__ __forceinline__ void pin(T& v) {
+  int x = static_cast<int>(v);
+  asm volatile("" : "+v"(x));
+  v = static_cast<T>(x);
 }
 
 __device__ __forceinline__ bool beats(float ov, int op, float v, int p) {
@@ -471,35 +483,60 @@ __device__ __forceinline__ void run(const Args& a, unsigned char* dyn, Lds& L) {
     }
     __syncthreads();
 
-    // ---- fallback rounds: thread t owns token t
+    // ---- fallback rounds: thread t owns token t.  Every LDS read below is
+    // issued unconditionally (clamped index) and its value pinned right after
+    // the batch (pin), so that the compiler cannot sink each read into the
+    // branch that uses it and wait for it there: a batch costs one round trip.
     const bool tok = tid < T;
     int cur[MK];
     uint32_t over = 0u, placed = 0u;
+    {
+      int cv[MK];
+      uint8_t sv[MK];
 #pragma unroll
-    for (int s = 0; s < MK; ++s) {
-      cur[s] = -1;
-      if (tok && s < k) {
-        cur[s] = s_cur[tid * k + s];
-        if (s_st[tid * k + s] & ST_OVER) over |= 1u << s;
+      for (int s = 0; s < MK; ++s) {
+        const int i = min(tid * k + s, MAX_SLOTS - 1);
+        cv[s] = s_cur[i];
+        sv[s] = s_st[i];
+      }
+#pragma unroll
+      for (int s = 0; s < MK; ++s) {
+        pin(cv[s]);
+        pin(sv[s]);
+      }
+#pragma unroll
+      for (int s = 0; s < MK; ++s) {
+        const bool own = tok && s < k;
+        cur[s] = own ? cv[s] : -1;
+        if (own && (sv[s] & ST_OVER)) over |= 1u << s;
       }
     }
-    const bool one_group = a.group >= N;
     const int tw = (T + MOE_WAVE - 1) / MOE_WAVE;  // waves holding tokens
     int fbr[MR];
 #pragma unroll
-    for (int q = 0; q < MR; ++q) fbr[q] = tok && q < R ? s_fb[tid * R + q] : 0;
+    for (int q = 0; q < MR; ++q) {
+      fbr[q] = s_fb[min(tid * R + q, MAX_FB - 1)];
+    }
+#pragma unroll
+    for (int q = 0; q < MR; ++q) pin(fbr[q]);
+#pragma unroll
+    for (int q = 0; q < MR; ++q) fbr[q] = tok && q < R ? fbr[q] : 0;
     // A (experts with a round-0 proposer) as four 64-bit words, the same in
-    // every lane
+    // every lane (entries past N are zero)
     uint64_t am[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) am[q] = __ballot(q * 64 + lane < N && s_active[q * 64 + lane]);
+    for (int q = 0; q < 4; ++q) {
+      const bool f = s_active[q * 64 + lane] != 0;
+      am[q] = __ballot(f);
+    }
     // the token's fallback ranks that could still be offered: in A and not
     // held for good by a kept slot (A is fixed; a kept or placed slot never
     // moves, so its expert stays held; an overflowed slot's expert is held
     // only until that slot is placed elsewhere, so it does not rule a rank
     // out here); the full held test and the group test stay at the offer.
     // Rounds stop once no token with an unplaced overflowed slot has a
-    // candidate left: no later round could offer anything.
+    // candidate left: no later round could offer anything.  A token's
+    // fallback ids are distinct, so placing a slot rules out no other rank.
     uint32_t cand = 0u;
     if (tok && over) {
 #pragma unroll
@@ -512,75 +549,115 @@ __device__ __forceinline__ void run(const Args& a, unsigned char* dyn, Lds& L) {
         if (q < R && ((aw >> (c & 63)) & 1u) && !held) cand |= 1u << q;
       }
     }
-    for (int r = 1; r <= R; ++r) {
-      bool offer = false;
-      int c = 0;
-      uint32_t* tab = s_tab + (r & 1) * 4 * MAX_N;
-      const uint32_t tag = static_cast<uint32_t>(r) << TAG_SHIFT;
-      uint32_t local = 0;
-      if (wave < tw) {  // uniform: waves without tokens only meet the barrier
-      if (tok && over && ((cand >> (r - 1)) & 1u)) {
-        const int s0 = __builtin_ctz(over);
+    // ONE: every expert in one group (no group test, no division).  The
+    // rounds are unrolled, so the candidate of round r and the earlier
+    // rounds' admissions are static register and LDS indices.
+    auto rounds = [&](auto one_tag) {
+      constexpr bool ONE = decltype(one_tag)::value;
+      int fbg[MR], cg[MK];  // expert groups, up front
+      if constexpr (!ONE) {
 #pragma unroll
-        for (int q = 0; q < MR; ++q)
-          if (q == r - 1) c = fbr[q];
-        bool held = false;
-        int e0 = 0;  // the offered slot's expert (register array, static indices)
+        for (int q = 0; q < MR; ++q) fbg[q] = fbr[q] / a.group;
 #pragma unroll
-        for (int s = 0; s < MK; ++s) {
-          held |= cur[s] == c;
-          if (s == s0) e0 = cur[s];
+        for (int s = 0; s < MK; ++s) cg[s] = cur[s] < 0 ? 0 : cur[s] / a.group;
+      }
+#pragma unroll
+      for (int r = 1; r <= MR; ++r) {
+        if (r > R) break;
+        bool offer = false;
+        const int c = fbr[r - 1];
+        int s0 = 0;
+        uint32_t* tab = s_tab + (r & 1) * 4 * MAX_N;
+        const uint32_t tag = static_cast<uint32_t>(r) << TAG_SHIFT;
+        uint32_t local = 0;
+        if (wave < tw) {  // uniform: waves without tokens only meet the barrier
+          if (tok && over && ((cand >> (r - 1)) & 1u)) {
+            s0 = __builtin_ctz(over);
+            bool held = false;
+#pragma unroll
+            for (int s = 0; s < MK; ++s) held |= cur[s] == c;
+            bool same_group = true;
+            if constexpr (!ONE) {
+              int g0 = 0;  // the offered slot's group (static indices)
+#pragma unroll
+              for (int s = 0; s < MK; ++s)
+                if (s == s0) g0 = cg[s];
+              same_group = g0 == fbg[r - 1];
+            }
+            offer = !held && same_group;
+          }
+          // running weight of this wave's offers to each expert, in token
+          // order, and the last offering lane of each expert
+          const uint64_t om = __ballot(offer);
+          bool last = false;
+          if (om != 0ull && __popcll(om) <= 8) {
+            // few offers: one step per offering lane
+            for (uint64_t m = om; m; m &= m - 1) {
+              const int j = __builtin_ctzll(m);
+              const int cj = __builtin_amdgcn_readlane(c, j);
+              const uint32_t wj = static_cast<uint32_t>(__builtin_amdgcn_readlane(wq, j));
+              const bool same = offer && c == cj;
+              if (same && j <= lane) local += wj;
+              if (same) last = j == lane;
+            }
+          } else if (om != 0ull) {
+            const uint64_t peers = match_any(c, offer, a.nbits);
+            local = peer_prefix(peers, offer, static_cast<uint32_t>(wq));
+            last = lane == 63 - __clzll(static_cast<long long>(peers));
+          }
+          if (offer && last) tab[wave * MAX_N + c] = tag | local;
+          // this wave's pending flag for round r (parity slot)
+          const bool pend = __ballot(over != 0u && (cand >> (r - 1)) != 0u) != 0ull;
+          if (lane == 0) s_pend[(r & 1) * 4 + wave] = pend;
         }
-        const uint64_t aw = c < 64 ? am[0] : c < 128 ? am[1] : c < 192 ? am[2] : am[3];
-        offer = ((aw >> (c & 63)) & 1u) && !held &&
-                (one_group || c / a.group == e0 / a.group);
-      }
-      const uint64_t peers = match_any(c, offer, a.nbits);
-      local = peer_prefix(peers, offer, static_cast<uint32_t>(wq));
-      if (offer && lane == 63 - __clzll(static_cast<long long>(peers)))
-        tab[wave * MAX_N + c] = tag | local;
-      // this wave's pending flag for round r (parity slot)
-      const bool pend = __ballot(over != 0u && (cand >> (r - 1)) != 0u) != 0ull;  // whole wave
-      if (lane == 0) s_pend[(r & 1) * 4 + wave] = pend;
-      }
-      // publishes the table and the flags: stop once no token has an
-      // unplaced overflowed slot (no later round could offer anything)
-      __syncthreads();
-      bool any = false;
+        // publishes the table and the flags: stop once no token has an
+        // unplaced overflowed slot (no later round could offer anything)
+        __syncthreads();
+        bool any = false;
+        {
+          uint8_t pv[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) any |= v < tw && s_pend[(r & 1) * 4 + v] != 0;
-      if (!any) break;
-      if (offer) {
-        // every read of the round at once: the other token waves' totals,
-        // the capacity, round 0's load and the earlier rounds' admissions
-        uint32_t x[3], u[MR];
+          for (int v = 0; v < 4; ++v) pv[v] = s_pend[(r & 1) * 4 + v];
 #pragma unroll
-        for (int v = 0; v < 3; ++v) x[v] = tab[v * MAX_N + c];
-        const int32_t cap = s_cap[c], l0 = static_cast<int32_t>(s_load0[c]);
+          for (int v = 0; v < 4; ++v) any |= v < tw && pv[v] != 0;
+        }
+        if (!any) break;
+        if (offer) {
+          // every read of the round at once: the other token waves' totals,
+          // the capacity, round 0's load and the earlier rounds' admissions
+          uint32_t x[3], u[MR];
 #pragma unroll
-        for (int q = 1; q < MR; ++q) u[q] = s_U[q * MAX_N + c];
-        uint32_t base = 0;
+          for (int v = 0; v < 3; ++v) x[v] = tab[v * MAX_N + c];
+          const int32_t cap = s_cap[c], l0 = static_cast<int32_t>(s_load0[c]);
 #pragma unroll
-        for (int v = 0; v < 3; ++v)
-          if (v < wave && v < tw && (x[v] & ~VAL_MASK) == tag) base += x[v] & VAL_MASK;
-        int32_t rem = cap - l0;
+          for (int q = 1; q < MR; ++q)
+            if (q < r) u[q] = s_U[q * MAX_N + c];
+          uint32_t base = 0;
 #pragma unroll
-        for (int q = 1; q < MR; ++q)
-          if (q < r) rem -= static_cast<int32_t>(u[q]);
-        if (static_cast<int32_t>(base + local) <= rem) {
-          const int s0 = __builtin_ctz(over);
+          for (int v = 0; v < 3; ++v)
+            if (v < wave && v < tw && (x[v] & ~VAL_MASK) == tag) base += x[v] & VAL_MASK;
+          int32_t rem = cap - l0;
 #pragma unroll
-          for (int s = 0; s < MK; ++s)
-            if (s == s0) cur[s] = c;
-          over &= ~(1u << s0);
-          placed |= 1u << s0;
+          for (int q = 1; q < MR; ++q)
+            if (q < r) rem -= static_cast<int32_t>(u[q]);
+          if (static_cast<int32_t>(base + local) <= rem) {
 #pragma unroll
-          for (int q = 0; q < MR; ++q)
-            if (fbr[q] == c) cand &= ~(1u << q);  // now held
-          atomicAdd(&s_U[r * MAX_N + c], static_cast<uint32_t>(wq));
+            for (int s = 0; s < MK; ++s)
+              if (s == s0) {
+                cur[s] = c;
+                if constexpr (!ONE) cg[s] = fbg[r - 1];
+              }
+            over &= ~(1u << s0);
+            placed |= 1u << s0;
+            atomicAdd(&s_U[r * MAX_N + c], static_cast<uint32_t>(wq));
+          }
         }
       }
-    }
+    };
+    if (a.group >= N)
+      rounds(std::true_type{});
+    else
+      rounds(std::false_type{});
     if (tok) {
 #pragma unroll
       for (int s = 0; s < MK; ++s)
