@@ -56,9 +56,9 @@ DIFF_REPS = 5  # timed-region pairs per in-step kernel duration
 
 HBM_COUNTERS = {
     "qwen3_decode_b128": dict(
-        kernel="gate_up_swiglu", fetch_kib=130576.674, write_kib=1536.0,
+        kernel="gate_up_swiglu", fetch_kib=130569.0, write_kib=1536.9,
         fetch_scale=2.0, write_scale=1.0,
-        sources_sha256="1b3922dc86448d537f3c6717116a56f0d830d7a3c6845e3aebb9d2a5cdcee9df"),
+        sources_sha256="98727dc8084ea2addb6c531a94fcb0551bf1020d3a6d6ddea3305a05653fed33"),
 }
 
 
@@ -107,6 +107,12 @@ def parse():
                    help="the 48-layer decode sweep: batch x visual fraction x "
                         "SERE setting, one JSON line with the whole table")
     p.add_argument("--layers", type=int, default=48)
+    p.add_argument("--batches", default="1,8,32,64,128,256",
+                   help="sweep: batch sizes (comma-separated)")
+    p.add_argument("--fracs", default="0.1,0.5,0.9",
+                   help="sweep: visual fractions (comma-separated)")
+    p.add_argument("--kprimes", default="0,1,2",
+                   help="sweep: SERE settings K' (0 = off; comma-separated)")
     p.add_argument("--entropy", action="store_true",
                    help="time the entropy-weight producer on the multimodal "
                         "prefill batch (T=8192, H=2048, bf16) and exit")
@@ -205,12 +211,12 @@ def run_sweep(args):
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
     rows = []
-    for T in (1, 8, 32, 64, 128, 256):
+    for T in [int(v) for v in args.batches.split(",")]:
         x = elem_tensor(synth.activations(base.with_(T=T), args.seed), "bf16", dev)
         lay = B.Layer(T, H, N, k, I, R, torch.bfloat16, dev)
         h = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
-        for frac in (0.1, 0.5, 0.9):
-            for kp in (0, 1, 2):
+        for frac in [float(v) for v in args.fracs.split(",")]:
+            for kp in [int(v) for v in args.kprimes.split(",")]:
                 wl = base.with_(T=T, visual=f"frac:{frac}", kprime=kp)
                 inps = [to_device(synth.make_inputs(wl, args.seed, layer=l,
                                                     weights=False), dev, weights=False)
