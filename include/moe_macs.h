@@ -297,7 +297,9 @@ int moe_entropy_weights(const void* x, const uint8_t* is_visual, int T, int H,
  * bounds the batch: moe_routing_workspace_size returns 0 for shapes the
  * fused launch does not cover (about T*k <= 4096 at N = 128, k = R = 8),
  * and moe_routing_fused returns MOE_EUNSUP for them; the separate calls
- * cover every shape.
+ * cover every shape.  A batch of at most 8 tokens and 64 slots (k <= 8,
+ * R <= 8, N <= 256) is routed by a single workgroup from start to end; the
+ * outputs are the same.
  * Errors: as the separate calls, plus MOE_EUNSUP as above.
  */
 size_t moe_routing_workspace_size(int T, int N, int k, int R);
@@ -334,7 +336,13 @@ int moe_routing_fused(const float* logits, const uint8_t* is_visual,
  *                 accumulation; h and out_rows are rounded to bf16), or
  *                 MOE_BF16_PANELS: MOE_BF16 arithmetic, with w13 and w2 as
  *                 moe_pack_weights wrote them; the results equal those of
- *                 MOE_BF16 on the unpacked weights bit for bit.
+ *                 MOE_BF16 on the unpacked weights bit for bit, except for
+ *                 decode batches of at most 16 dispatch rows (T*k <= 16)
+ *                 whose reduction length (H for the gate-up half, I for the
+ *                 down half) is 256, 512, 768, 1024 or 2048 (gate-up also
+ *                 T <= 8): those run as GEMVs with fp32 dot products of bf16
+ *                 pairs summed in another order, within the bf16 rounding
+ *                 of the row layout's results (deterministic run to run).
  * The workspace holds h ([T*k, I] of dtype).
  * Shapes: the bf16 formats need H % 256 == 0, I % 128 == 0, x of at most 2 GiB
  * (T*H*2 <= 2^31 bytes) and one expert's w13 under 4 GiB (I*H*4 < 2^32
