@@ -214,7 +214,8 @@ def run_sweep(args):
     for T in [int(v) for v in args.batches.split(",")]:
         x = elem_tensor(synth.activations(base.with_(T=T), args.seed), "bf16", dev)
         lay = B.Layer(T, H, N, k, I, R, torch.bfloat16, dev)
-        h = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
+        ws = B.new_workspace(B.moe_ffn_combine_workspace_size(T, N, k, H, I, torch.bfloat16),
+                             dev)
         for frac in [float(v) for v in args.fracs.split(",")]:
             for kp in [int(v) for v in args.kprimes.split(",")]:
                 wl = base.with_(T=T, visual=f"frac:{frac}", kprime=kp)
@@ -227,13 +228,10 @@ def run_sweep(args):
                     lay.routing(d["logits"], d["is_visual"], d["entropy_w"],
                                 d["modality"], d["sim"], d["prot"], kp, wl.rho,
                                 wl.gamma, wl.lam, wl.group)
-                    B.moe_ffn_gate_up(x, lay.disp["row_token"],
-                                      lay.disp["expert_offsets"], w13[l], k, h,
-                                      panels=panels)
-                    B.moe_ffn_down(h, lay.disp["expert_offsets"], w2[l], T, k,
-                                   lay.out_rows, panels=panels)
-                    B.moe_combine(lay.out_rows, lay.disp["slot_row"],
-                                  lay.topk_gates, lay.y)
+                    B.moe_expert_ffn_combine(x, lay.disp["row_token"],
+                                             lay.disp["expert_offsets"], w13[l], w2[l],
+                                             lay.disp["slot_row"], lay.topk_gates, k, ws,
+                                             lay.out_rows, lay.y, panels=panels)
 
                 # union sizes and weight bytes, layer by layer (untimed)
                 ub = us = uf = 0

@@ -18,7 +18,8 @@
  *   moe_route -> moe_sere_reroute -> moe_capacity_assign -> moe_dispatch
  *   -> moe_expert_ffn -> moe_combine
  * Decode-sized batches can replace the first four calls by one
- * moe_routing_fused launch.
+ * moe_routing_fused launch, and moe_expert_ffn_combine makes the last two
+ * one call.
  *
  * Conventions shared by every entry point
  *   - Every array argument is a DEVICE pointer owned by the caller; the
@@ -47,12 +48,12 @@
  *     reductions only where order cannot matter.
  *
  * Workspaces
- *   moe_router_topk, moe_capacity_assign, moe_dispatch, moe_routing_fused
- *   and moe_expert_ffn take a workspace of at least the size their
- *   *_workspace_size() query returns.  The router, capacity, dispatch and
- *   fused-routing workspaces hold a few control words: they must be filled
- *   with zero bytes once, before their first use (e.g. allocated zeroed);
- *   every call leaves those words zero again.  A workspace must not be
+ *   moe_router_topk, moe_capacity_assign, moe_dispatch, moe_routing_fused,
+ *   moe_expert_ffn and moe_expert_ffn_combine take a workspace of at least
+ *   the size their *_workspace_size() query returns.  The router, capacity,
+ *   dispatch, fused-routing and FFN-combine workspaces hold a few control
+ *   words: they must be filled with zero bytes once, before their first use
+ *   (e.g. allocated zeroed); every call leaves those words zero again.  A workspace must not be
  *   shared by calls that may run concurrently.
  */
 #ifndef MOE_MACS_H
@@ -365,6 +366,33 @@ int moe_ffn_gate_up(const void* x, const int32_t* row_token,
 int moe_ffn_down(const void* h, const int32_t* expert_offsets, const void* w2,
                  int T, int N, int k, int H, int I, int dtype, void* out_rows,
                  void* stream);
+
+/*
+ * moe_expert_ffn_combine -- moe_expert_ffn followed by moe_combine (MACS
+ * §3.1 Eq. 1, the whole sum over the kept experts) in one call: out_rows
+ * and y equal those of the two calls bit for bit.  For decode batches on
+ * packed weights whose down half runs as a GEMV (dtype MOE_BF16_PANELS,
+ * T*k <= 16, I as listed above) the combine is folded into that GEMV: the
+ * last workgroup to finish a group of 32 output columns, told by a ticket
+ * in the workspace, combines those columns of every token, which saves a
+ * launch and a pass over out_rows; other calls enqueue the two.
+ *
+ * Arguments: those of moe_expert_ffn, plus slot_row i32[T,k] (moe_dispatch
+ * output) and topk_gates f32[T,k] as for moe_combine, and y [T,H] out
+ * (dtype; bf16 for the packed formats).  The workspace holds the tickets
+ * (H/32 words, rounded up to 256 bytes) and then h; its size is
+ * moe_ffn_combine_workspace_size(), and the ticket words must be filled
+ * with zero bytes once before the first use (every call leaves them zero).
+ * Shapes as moe_expert_ffn, and H % 8 == 0; errors as moe_expert_ffn.
+ */
+size_t moe_ffn_combine_workspace_size(int T, int N, int k, int H, int I, int dtype);
+int moe_expert_ffn_combine(const void* x, const int32_t* row_token,
+                           const int32_t* expert_offsets, const void* w13,
+                           const void* w2, const int32_t* slot_row,
+                           const float* topk_gates, int T, int N, int k, int H,
+                           int I, int dtype, void* out_rows, void* y,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /*
  * moe_pack_weights -- the expert weights in the panel layout that the

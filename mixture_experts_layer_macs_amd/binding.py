@@ -60,6 +60,9 @@ _SIGS = {
     "moe_ffn_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "moe_expert_ffn": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P,
                             _P, _SZ, _P]),
+    "moe_ffn_combine_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "moe_expert_ffn_combine": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I,
+                                    _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "moe_expert_ffn_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
                                     _P, _P]),
     "moe_ffn_gate_up": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
@@ -258,6 +261,10 @@ def moe_ffn_workspace_size(T, N, k, H, I, dtype) -> int:
     return int(_lib.moe_ffn_workspace_size(T, N, k, H, I, _elem(dtype)))
 
 
+def moe_ffn_combine_workspace_size(T, N, k, H, I, dtype) -> int:
+    return int(_lib.moe_ffn_combine_workspace_size(T, N, k, H, I, _elem(dtype)))
+
+
 def new_workspace(nbytes: int, device) -> torch.Tensor:
     """Zero-filled workspace (the control words must start at zero)."""
     return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -394,6 +401,35 @@ def moe_expert_ffn(x, row_token, expert_offsets, w13, w2, k, workspace,
     return out_rows
 
 
+def moe_expert_ffn_combine(x, row_token, expert_offsets, w13, w2, slot_row,
+                           topk_gates, k, workspace, out_rows=None, y=None,
+                           panels=False):
+    """moe_expert_ffn then moe_combine in one call (the combine folded into
+    the down GEMV of decode batches on packed weights).  The workspace's
+    ticket words start at zero (new_workspace allocates it zeroed)."""
+    T, H = x.shape
+    N, I2, H2 = w13.shape
+    I = I2 // 2
+    if H2 != H or tuple(w2.shape) != (N, H, I):
+        raise ValueError("expert weight shapes do not match x")
+    dt = _ffn_format(x.dtype, panels)
+    if out_rows is None:
+        out_rows = _empty((T * k, H), x.dtype, x)
+    if y is None:
+        y = _empty((T, H), x.dtype, x)
+    rc = _lib.moe_expert_ffn_combine(
+        _dev(x, x.dtype, "x"), _dev(row_token, torch.int32, "row_token", (T * k,)),
+        _dev(expert_offsets, torch.int32, "expert_offsets", (N + 1,)),
+        _dev(w13, x.dtype, "w13"), _dev(w2, x.dtype, "w2"),
+        _dev(slot_row, torch.int32, "slot_row", (T, k)),
+        _dev(topk_gates, torch.float32, "topk_gates", (T, k)),
+        T, N, k, H, I, dt, _dev(out_rows, x.dtype, "out_rows", (T * k, H)),
+        _dev(y, x.dtype, "y", (T, H)),
+        _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
+    _check(rc, "moe_expert_ffn_combine")
+    return y
+
+
 def moe_expert_ffn_noalloc(x, row_token, expert_offsets, w13, w2, k,
                            out_rows=None, panels=False):
     """moe_expert_ffn with h in the library's fixed device buffer (no
@@ -459,7 +495,7 @@ def moe_combine(out_rows, slot_row, topk_gates, y=None):
 class Layer:
     """Preallocated buffers for one layer shape; ``forward`` enqueues the
     calls on the current stream (route -> SERE -> capacity -> dispatch ->
-    expert FFN -> combine) with no host synchronisation.  Decode-sized
+    expert FFN and combine in one call) with no host synchronisation.  Decode-sized
     batches route with the single fused launch unless ``fused=False``."""
 
     def __init__(self, T, H, N, k, I, R, dtype, device="cuda"):
@@ -484,7 +520,7 @@ class Layer:
         self.y = e((T, H), dtype)
         self.ws_cap = new_workspace(moe_capacity_workspace_size(T, N, k), dev)
         self.ws_disp = new_workspace(moe_dispatch_workspace_size(T, N, k), dev)
-        self.ws_ffn = new_workspace(moe_ffn_workspace_size(T, N, k, H, I, dtype), dev)
+        self.ws_ffn = new_workspace(moe_ffn_combine_workspace_size(T, N, k, H, I, dtype), dev)
         ws_route = moe_routing_workspace_size(T, N, k, R)
         self.can_fuse = ws_route > 0
         self.ws_route = new_workspace(ws_route, dev) if self.can_fuse else None
@@ -523,7 +559,7 @@ class Layer:
         k = self.k
         self.routing(logits, is_visual, entropy_w, modality, sim, prot, kprime,
                      rho, gamma, lam, group, fused)
-        moe_expert_ffn(x, self.disp["row_token"], self.disp["expert_offsets"],
-                       w13, w2, k, self.ws_ffn, self.out_rows, panels=panels)
-        moe_combine(self.out_rows, self.disp["slot_row"], self.topk_gates, self.y)
+        moe_expert_ffn_combine(x, self.disp["row_token"], self.disp["expert_offsets"],
+                               w13, w2, self.disp["slot_row"], self.topk_gates, k,
+                               self.ws_ffn, self.out_rows, self.y, panels=panels)
         return self.y

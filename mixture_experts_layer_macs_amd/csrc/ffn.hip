@@ -51,6 +51,15 @@ struct Args {
   int panels;              // 1: w in the panel layout (moe_pack_weights)
 };
 
+// The gate-weighted combine folded into the down GEMV (moe_expert_ffn_combine).
+struct Comb {
+  const int32_t* slot_row;  // [T,k] dispatch row of each slot, -1 = dropped
+  const float* gates;       // [T,k]
+  uint16_t* y;              // [T,H] bf16
+  unsigned* ticket;         // [H/32] arrivals per output column group (zero between calls)
+  int T, k;
+};
+
 // Two fp32 values to a packed bf16 pair (round to nearest even), one
 // v_cvt_pk_bf16_f32 on gfx950; the first value lands in the low half.
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -176,6 +185,67 @@ __device__ bool find_tile(const Args& a, int* cum, int& j, int& m0, int& nt,
   if (L >= total) return false;
   locate_tile<BM>(a, cum, L, j, m0, nt, Mj, row0);
   return true;
+}
+
+// The same search held in registers, for N < 64 * REG_CHUNKS experts: each
+// wave reads the expert offsets itself in one batch of loads, counts tiles
+// with a prefix scan, and finds the expert of tile L by a ballot (the
+// number of experts whose inclusive tile count is at most L), so no LDS
+// table, no workgroup barrier and no chain of dependent reads comes before
+// the first weight request.  Lane l of chunk c stands for expert l + 64 c.
+constexpr int REG_CHUNKS = 5;
+struct TileRegs {
+  int cum[REG_CHUNKS];  // inclusive tile counts
+  int o0[REG_CHUNKS];   // offsets[e]
+  int o1[REG_CHUNKS];   // offsets[e + 1]
+  int total;
+};
+
+template <int BM>
+__device__ __forceinline__ void tile_regs(const Args& a, TileRegs& tr) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int c = 0; c < REG_CHUNKS; ++c) {
+    const int e = lane + 64 * c;
+    tr.o0[c] = a.offsets[min(e, a.N)];
+    tr.o1[c] = a.offsets[min(e + 1, a.N)];
+  }
+  int carry = 0;
+#pragma unroll
+  for (int c = 0; c < REG_CHUNKS; ++c) {
+    const int e = lane + 64 * c;
+    const int m = e < a.N ? tr.o1[c] - tr.o0[c] : 0;
+    const int inc = wave_incl_scan(((m + BM - 1) / BM) * a.n_tiles);
+    tr.cum[c] = carry + inc;
+    carry += read_lane(inc, MOE_WAVE - 1);
+  }
+  tr.total = __builtin_amdgcn_readfirstlane(carry);
+}
+
+template <int BM>
+__device__ __forceinline__ void locate_regs(const Args& a, const TileRegs& tr, int L, int& j,
+                                            int& m0, int& nt, int& Mj, int& row0) {
+  const int lane = lane_id();
+  int jj = 0;
+#pragma unroll
+  for (int c = 0; c < REG_CHUNKS; ++c)
+    jj += __popcll(__ballot(lane + 64 * c < a.N && tr.cum[c] <= L));
+  j = jj;  // L < total, so j < N
+  const int cj = j / 64, lj = j % 64;
+  int cum = 0, o0 = 0, o1 = 0;
+#pragma unroll
+  for (int c = 0; c < REG_CHUNKS; ++c)
+    if (c == cj) {
+      cum = read_lane(tr.cum[c], lj);
+      o0 = read_lane(tr.o0[c], lj);
+      o1 = read_lane(tr.o1[c], lj);
+    }
+  row0 = o0;
+  Mj = o1 - o0;
+  const int mt = (Mj + BM - 1) / BM;
+  const int r = L - (cum - mt * a.n_tiles);
+  nt = r / mt;
+  m0 = (r % mt) * BM;
 }
 
 // ------------------------------------------------- direct-to-LDS pipeline
@@ -602,8 +672,25 @@ __device__ __forceinline__ void gemm_body(const Args& a, unsigned char* smem, in
 // workgroups.  cum: LDS [N + 1].
 template <int BM>
 __device__ __forceinline__ bool find_tile_s(const Args& a, int* cum, int& j, int& m0, int& nt,
-                                            int& Mj, int& row0) {
+                                            int& Mj, int& row0, int* total = nullptr) {
+  if (a.N < 64 * REG_CHUNKS) {  // registers only, every wave on its own
+    TileRegs tr;
+    tile_regs<BM>(a, tr);
+    if (total) *total = tr.total;
+    const int p = blockIdx.x;
+    const int q = (tr.total + 7) / 8;  // tiles per XCD, as find_tile
+    const int L = (p % 8) * q + p / 8;
+    if (p / 8 >= q || L >= tr.total) return false;
+    locate_regs<BM>(a, tr, L, j, m0, nt, Mj, row0);
+    j = __builtin_amdgcn_readfirstlane(j);
+    m0 = __builtin_amdgcn_readfirstlane(m0);
+    nt = __builtin_amdgcn_readfirstlane(nt);
+    Mj = __builtin_amdgcn_readfirstlane(Mj);
+    row0 = __builtin_amdgcn_readfirstlane(row0);
+    return true;
+  }
   const bool live = find_tile<BM>(a, cum, j, m0, nt, Mj, row0);
+  if (total) *total = cum[a.N + 1];
   // cum lives at the start of the ring, which the first loads overwrite:
   // every wave must be done with the search first (surplus workgroups
   // return together, all their waves having found no tile)
@@ -858,8 +945,8 @@ __device__ __forceinline__ float dot8(const u32x4 w, const u32x4 x, float acc) {
 
 // NBW = K / 256: the K slices of one wave (a compile-time count, so that
 // the compiler's wait for the token rows leaves every weight load alone).
-template <int MODE, int MR, int NBW>
-__global__ __launch_bounds__(4 * MOE_WAVE) void gemv_kernel(Args a) {
+template <int MODE, int MR, int NBW, bool COMB = false>
+__global__ __launch_bounds__(4 * MOE_WAVE) void gemv_kernel(Args a, Comb c) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int XR = MODE == GATEUP ? GEMV_MAX_T : MR;  // staged token rows
   const int K = a.K;
@@ -868,10 +955,26 @@ __global__ __launch_bounds__(4 * MOE_WAVE) void gemv_kernel(Args a) {
   unsigned char* xs = smem;                                                       // [XR][K] bf16
   float* red = reinterpret_cast<float*>(smem + static_cast<size_t>(XR) * K * 2);  // [4][MR][32]
   int* cum = reinterpret_cast<int*>(red + 4 * MR * 32);                          // [N + 2]
-  int j, m0, gi, Mj, row0;
-  if (!find_tile_s<MR>(a, cum, j, m0, gi, Mj, row0)) return;
+  int j, m0, gi, Mj, row0, total;
+  if (!find_tile_s<MR>(a, cum, j, m0, gi, Mj, row0, &total)) {
+    // every slot dropped: no workgroup has a tile, and y is zero
+    if constexpr (COMB)
+      if (total == 0 && static_cast<int>(blockIdx.x) < a.n_tiles && tid < 64)
+        for (int t = tid / 32; t < c.T; t += 2)
+          c.y[static_cast<size_t>(t) * a.NC + blockIdx.x * 32 + tid % 32] = 0;
+    return;
+  }
   const int rows = min(MR, Mj - m0);
   const int nstage = MODE == GATEUP ? a.a_rows : rows;
+  // combine: the slots' rows and gates (at most 64 slots, one per lane),
+  // requested before the weight stream and used after it
+  int slot_r = 0;
+  float slot_g = 0.f;
+  if constexpr (COMB) {
+    const int q = min(lane, c.T * c.k - 1);
+    slot_r = c.slot_row[q];
+    slot_g = c.gates[q];
+  }
 
   // token rows: thread i stages 16-byte chunk i of every row (K <= 2048:
   // at most 256 chunks a row; clamped loads, the extra ones unused)
@@ -950,8 +1053,59 @@ __global__ __launch_bounds__(4 * MOE_WAVE) void gemv_kernel(Args a) {
         const uint32_t hv = pack_bf16x2(silu(v) * up, 0.f);
         a.out[orow + (gi / 4) * 64 + (gi % 4) * 16 + lane] = static_cast<uint16_t>(hv);
       }
-    } else {
-      if (lane < 32) a.out[orow + gi * 32 + lane] = static_cast<uint16_t>(pack_bf16x2(v, 0.f));
+    } else if (lane < 32) {
+      const uint16_t o = static_cast<uint16_t>(pack_bf16x2(v, 0.f));
+      if constexpr (COMB)  // written through to the device-coherent level
+        __hip_atomic_store(&a.out[orow + gi * 32 + lane], o, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      else
+        a.out[orow + gi * 32 + lane] = o;
+    }
+  }
+  if constexpr (COMB) {
+    // The last of the workgroups that write output columns 32 gi .. +31
+    // (one per expert tile; an arrival ticket that wraps back to zero)
+    // combines those columns of every token: y[t] = sum over the kept slots,
+    // in slot order, of gate * out_rows[row], fp32 fused multiply-adds from
+    // zero, rounded to bf16 to nearest even -- the arithmetic of moe_combine.
+    // The rows travel as device-scope atomic stores and loads, which the L2
+    // of each XCD keeps coherent by themselves; the ticket is taken once
+    // this wave's stores have completed (vmcnt 0) and the loads are issued
+    // after its value has returned, so no L2 writeback or invalidation (a
+    // device-scope fence) is needed in any of the workgroups.
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the row stores are done
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const unsigned live = static_cast<unsigned>(total / a.n_tiles);
+    unsigned prev = 0;
+    if (lane == 0) prev = atomicInc(c.ticket + gi, live - 1);
+    if (__builtin_amdgcn_readfirstlane(prev) != live - 1) return;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const int col = gi * 32 + lane % 32;
+    for (int t0 = 0; t0 < c.T; t0 += 2) {
+      const int t = min(t0 + lane / 32, c.T - 1);
+      float acc = 0.f;
+      for (int s0 = 0; s0 < c.k; s0 += 8) {
+        // the shuffles run in every lane: a lane reads the slot data of
+        // its own token from lanes that hold it, which must be active
+        int r[8];
+        float g[8];
+        uint32_t q[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int src = t * c.k + min(s0 + u, c.k - 1);
+          r[u] = __shfl(slot_r, src);
+          g[u] = __shfl(slot_g, src);
+          q[u] = __hip_atomic_load(&a.out[static_cast<size_t>(max(r[u], 0)) * a.NC + col],
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (s0 + u < c.k && r[u] >= 0) acc = __builtin_fmaf(g[u], __uint_as_float(q[u] << 16), acc);
+      }
+      uint32_t ua = __float_as_uint(acc);
+      ua += 0x7fffu + ((ua >> 16) & 1u);
+      if (t0 + lane / 32 < c.T) c.y[static_cast<size_t>(t) * a.NC + col] = static_cast<uint16_t>(ua >> 16);
     }
   }
 }
@@ -1386,20 +1540,21 @@ static int launch_gemm_skinny(Args a, int rows_cap, hipStream_t s) {
 
 // Decode GEMV on packed panels (see gemv_kernel): one workgroup per
 // (expert, MR token rows, 32-row group).
-template <int MODE, int MR, int NBW>
-static int launch_gemv(Args a, int rows_cap, hipStream_t s) {
+template <int MODE, int MR, int NBW, bool COMB>
+static int launch_gemv(Args a, const Comb& c, int rows_cap, hipStream_t s) {
   a.n_tiles = (MODE == GATEUP ? 2 * a.I : a.NC) / 32;
   constexpr int XR = MODE == GATEUP ? GEMV_MAX_T : MR;
   const size_t lds = static_cast<size_t>(XR) * a.K * 2 + 4 * MR * 32 * 4 +
                      static_cast<size_t>(a.N + 2) * 4;
-  const void* fn = reinterpret_cast<const void*>(gemv_kernel<MODE, MR, NBW>);
+  const void* fn = reinterpret_cast<const void*>(gemv_kernel<MODE, MR, NBW, COMB>);
   if (lds > 65536 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                          static_cast<int>(lds)) != hipSuccess)
     return MOE_EHIP;
   const int mt_ub = (rows_cap + MR - 1) / MR + std::min(a.N, rows_cap);
   long grid = static_cast<long>(mt_ub) * a.n_tiles;
   grid = (grid + 7) / 8 * 8;
-  hipLaunchKernelGGL((gemv_kernel<MODE, MR, NBW>), dim3(grid), dim3(4 * MOE_WAVE), lds, s, a);
+  hipLaunchKernelGGL((gemv_kernel<MODE, MR, NBW, COMB>), dim3(grid), dim3(4 * MOE_WAVE), lds, s,
+                     a, c);
   return MOE_OK;
 }
 
@@ -1421,21 +1576,24 @@ static bool gemv_ok(int mode, int T, int k, int K, bool panels) {
   return panels && static_cast<long>(T) * k <= MOE_GEMV_ROWS && gemv_nbw_ok(K) &&
          (mode == DOWN || T <= GEMV_MAX_T);
 }
-template <int MODE, int MR>
-static int launch_gemv_k(const Args& a, int rows_cap, hipStream_t s) {
+template <int MODE, int MR, bool COMB>
+static int launch_gemv_k(const Args& a, const Comb& c, int rows_cap, hipStream_t s) {
   switch (a.K / 256) {
-    case 1: return launch_gemv<MODE, MR, 1>(a, rows_cap, s);
-    case 2: return launch_gemv<MODE, MR, 2>(a, rows_cap, s);
-    case 3: return launch_gemv<MODE, MR, 3>(a, rows_cap, s);
-    case 4: return launch_gemv<MODE, MR, 4>(a, rows_cap, s);
-    default: return launch_gemv<MODE, MR, 8>(a, rows_cap, s);
+    case 1: return launch_gemv<MODE, MR, 1, COMB>(a, c, rows_cap, s);
+    case 2: return launch_gemv<MODE, MR, 2, COMB>(a, c, rows_cap, s);
+    case 3: return launch_gemv<MODE, MR, 3, COMB>(a, c, rows_cap, s);
+    case 4: return launch_gemv<MODE, MR, 4, COMB>(a, c, rows_cap, s);
+    default: return launch_gemv<MODE, MR, 8, COMB>(a, c, rows_cap, s);
   }
 }
-template <int MODE>
-static int launch_gemv_rows(const Args& a, int rows_cap, hipStream_t s) {
-  static_assert(MOE_GEMV_ROWS <= 64, "token-row chunks of 4 or 16");
-  return rows_cap <= 16 ? launch_gemv_k<MODE, 4>(a, rows_cap, s)
-                        : launch_gemv_k<MODE, 16>(a, rows_cap, s);
+// COMB (down only): the combine folded in; needs T * k <= 64 (one slot per
+// lane) -- every GEMV batch.
+template <int MODE, bool COMB = false>
+static int launch_gemv_rows(const Args& a, int rows_cap, hipStream_t s, const Comb& c = Comb{}) {
+  static_assert(MOE_GEMV_ROWS <= 64, "token-row chunks of 4 or 16; a slot per lane");
+  static_assert(!COMB || MODE == DOWN, "the combine follows the down projection");
+  return rows_cap <= 16 ? launch_gemv_k<MODE, 4, COMB>(a, c, rows_cap, s)
+                        : launch_gemv_k<MODE, 16, COMB>(a, c, rows_cap, s);
 }
 
 // ------------------------------------------------------- weight packing
@@ -1746,6 +1904,30 @@ extern "C" int moe_ffn_gate_up(const void* x, const int32_t* row_token,
   return launch_status();
 }
 
+// bf16 down-projection arguments (row or panel layout)
+static Args down_args(const void* h, const int32_t* expert_offsets, const void* w2, int T,
+                      int N, int k, int H, int I, int dtype, void* out_rows) {
+  Args d{};
+  d.a = static_cast<const uint16_t*>(h);
+  d.a_rows = T * k;
+  d.row_token = nullptr;
+  d.offsets = expert_offsets;
+  d.w = static_cast<const uint16_t*>(w2);
+  d.out = static_cast<uint16_t*>(out_rows);
+  d.N = N;
+  d.K = I;
+  d.NC = H;
+  d.I = I;
+  d.w_stride = static_cast<long>(H) * I;
+  d.panels = dtype == MOE_BF16_PANELS;
+  return d;
+}
+
+// The down GEMV with the combine folded in applies (see gemv_kernel).
+static bool down_combine_fused(int T, int N, int k, int I, int dtype) {
+  return dtype == MOE_BF16_PANELS && decode_tiles(T, N, k) && gemv_ok(DOWN, T, k, I, true);
+}
+
 extern "C" int moe_ffn_down(const void* h, const int32_t* expert_offsets,
                             const void* w2, int T, int N, int k, int H, int I,
                             int dtype, void* out_rows, void* stream) {
@@ -1767,19 +1949,7 @@ extern "C" int moe_ffn_down(const void* h, const int32_t* expert_offsets,
                                  static_cast<const float*>(w2), static_cast<float*>(out_rows),
                                  rows_cap, s);
   }
-  Args d{};
-  d.a = static_cast<const uint16_t*>(h);
-  d.a_rows = rows_cap;
-  d.row_token = nullptr;
-  d.offsets = expert_offsets;
-  d.w = static_cast<const uint16_t*>(w2);
-  d.out = static_cast<uint16_t*>(out_rows);
-  d.N = N;
-  d.K = I;
-  d.NC = H;
-  d.I = I;
-  d.w_stride = static_cast<long>(H) * I;
-  d.panels = dtype == MOE_BF16_PANELS;
+  Args d = down_args(h, expert_offsets, w2, T, N, k, H, I, dtype, out_rows);
   if (decode_tiles(T, N, k)) {
     int st;
     const bool narrow = narrow_decode_tiles(T, N, k, H / 256);
@@ -1839,6 +2009,51 @@ extern "C" int moe_expert_ffn(const void* x, const int32_t* row_token,
   if (r != MOE_OK) return r;
   return moe_ffn_down(workspace, expert_offsets, w2, T, N, k, H, I, dtype,
                       out_rows, stream);
+}
+
+// Arrival tickets of the fused combine at the start of its workspace, one
+// per 32 output columns, then h.
+static size_t ticket_bytes(int H) {
+  return ((static_cast<size_t>(H) + 31) / 32 * 4 + 255) & ~size_t(255);
+}
+
+extern "C" size_t moe_ffn_combine_workspace_size(int T, int N, int k, int H, int I,
+                                                 int dtype) {
+  if (T < 0 || k < 1 || H < 1 || I < 1) return 0;
+  return ticket_bytes(H) + moe_ffn_workspace_size(T, N, k, H, I, dtype);
+}
+
+extern "C" int moe_expert_ffn_combine(const void* x, const int32_t* row_token,
+                                      const int32_t* expert_offsets, const void* w13,
+                                      const void* w2, const int32_t* slot_row,
+                                      const float* topk_gates, int T, int N, int k, int H,
+                                      int I, int dtype, void* out_rows, void* y,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_ffn_shape(T, N, k, H, I, dtype);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (H % 8 != 0) return MOE_EUNSUP;  // the combine's row vectors
+  if (!workspace || workspace_bytes < moe_ffn_combine_workspace_size(T, N, k, H, I, dtype))
+    return MOE_EINVAL;
+  if (!x || !row_token || !expert_offsets || !w13 || !w2 || !slot_row || !topk_gates ||
+      !out_rows || !y)
+    return MOE_EINVAL;
+  unsigned* tickets = static_cast<unsigned*>(workspace);
+  void* h = static_cast<unsigned char*>(workspace) + ticket_bytes(H);
+  const int r = moe_ffn_gate_up(x, row_token, expert_offsets, w13, T, N, k, H, I, dtype, h,
+                                stream);
+  if (r != MOE_OK) return r;
+  if (down_combine_fused(T, N, k, I, dtype)) {
+    const Args d = down_args(h, expert_offsets, w2, T, N, k, H, I, dtype, out_rows);
+    const Comb c{slot_row, topk_gates, static_cast<uint16_t*>(y), tickets, T, k};
+    if (launch_gemv_rows<DOWN, true>(d, T * k, as_stream(stream), c) != MOE_OK)
+      return MOE_EHIP;
+    return launch_status();
+  }
+  const int r2 = moe_ffn_down(h, expert_offsets, w2, T, N, k, H, I, dtype, out_rows, stream);
+  if (r2 != MOE_OK) return r2;
+  return moe_combine(out_rows, slot_row, topk_gates, T, k, H,
+                     dtype == MOE_F32 ? MOE_F32 : MOE_BF16, y, stream);
 }
 
 extern "C" int moe_pack_weights(const void* w13, const void* w2, int N, int H, int I,

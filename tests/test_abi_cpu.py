@@ -89,6 +89,21 @@ def test_host_side_argument_errors(lib):
                               1, fake, fake, 1 << 30, None) == -2
     assert lib.moe_expert_ffn(fake, fake, fake, fake, fake, 4, 8, 2, 2048, 768,
                               7, fake, fake, 1 << 30, None) == -2   # dtype
+    lib.moe_ffn_combine_workspace_size.restype = ctypes.c_size_t
+    lib.moe_ffn_workspace_size.restype = ctypes.c_size_t
+    ws_c = lib.moe_ffn_combine_workspace_size(4, 8, 2, 2048, 768, 2)
+    ws_f = lib.moe_ffn_workspace_size(4, 8, 2, 2048, 768, 2)
+    assert ws_c == ws_f + 256     # 64 ticket words, then h
+    lib.moe_expert_ffn_combine.argtypes = ([P] * 7 + [ctypes.c_int] * 6 +
+                                           [P, P, P, ctypes.c_size_t, P])
+    args = [fake] * 7 + [4, 8, 2, 2048, 768, 2, fake, fake, fake]
+    assert lib.moe_expert_ffn_combine(*args, ws_c - 1, None) == -1   # workspace short
+    args = [fake] * 5 + [None, fake] + [4, 8, 2, 2048, 768, 2, fake, fake, fake]
+    assert lib.moe_expert_ffn_combine(*args, ws_c, None) == -1       # no slot_row
+    args = [fake] * 7 + [4, 8, 2, 2048, 768, 5, fake, fake, fake]
+    assert lib.moe_expert_ffn_combine(*args, 1 << 30, None) == -2    # dtype
+    args = [fake] * 7 + [4, 8, 2, 4, 4, 0, fake, fake, fake]
+    assert lib.moe_expert_ffn_combine(*args, 1 << 30, None) == -2    # f32, H % 8
     lib.moe_combine.argtypes = [P, P, P] + [ctypes.c_int] * 4 + [P, P]
     assert lib.moe_combine(fake, fake, fake, 4, 2, 100, 1, fake, None) == -2
     assert lib.moe_combine(None, fake, fake, 4, 2, 64, 1, fake, None) == -1

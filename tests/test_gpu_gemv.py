@@ -10,6 +10,12 @@ the gate-up and the down projections).  Each dispatch row of h and of the
 output is compared with the fp64 value to the bf16 bound; the fused and the
 no-allocation entry points give the same bits as the two halves called
 separately; the row-layout kernels (tile MFMA) agree to the same bound.
+
+moe_expert_ffn_combine (the combine folded into the down GEMV) is checked
+against moe_expert_ffn + moe_combine bit for bit -- out_rows and y -- with
+dropped slots, every slot dropped, and shapes that take the two-call path,
+over two calls in a row on one workspace whose arrival tickets must be zero
+again after each; y also against the oracle's combine of the same rows.
 """
 import numpy as np
 import pytest
@@ -105,3 +111,67 @@ def test_gemv_rows_match_oracle(case):
     assert_y_close(f64(out), y_ref, "bf16")
     assert_y_close(f64(out_r), y_ref, "bf16")
     say(f"  {M} rows within the bf16 bound")
+
+
+COMBINE_CASES = [
+    # name, T, H, N, k, I, slot assignment, share of slots dropped, packed
+    ("b1_qwen3_shape", 1, 2048, 128, 8, 768, "spread", 0.0, True),
+    ("b2_qwen3_some_dropped", 2, 2048, 128, 8, 768, "spread", 0.3, True),
+    ("one_expert_16_rows", 8, 1024, 4, 2, 768, "one", 0.0, True),
+    ("repeated_expert_dropped", 5, 256, 5, 3, 512, "repeat", 0.4, True),
+    ("t16_k1", 16, 512, 4, 1, 256, "repeat", 0.2, True),
+    ("k2048_down", 4, 512, 3, 2, 2048, "spread", 0.0, True),
+    ("every_slot_dropped", 2, 512, 8, 4, 256, "spread", 1.0, True),
+    # two calls: more rows than the GEMV takes, and the row layout
+    ("b8_qwen3_shape_tiles", 8, 2048, 128, 8, 768, "spread", 0.1, False),
+    ("b2_rows_layout", 2, 512, 8, 4, 256, "spread", 0.0, False),
+]
+
+
+@pytest.mark.parametrize("case", COMBINE_CASES, ids=[c[0] for c in COMBINE_CASES])
+def test_ffn_combine_matches_two_calls(case):
+    name, T, H, N, k, I, mode, drop, packed = case
+    B = load_binding()
+    say(f"ffn+combine {name} T={T} H={H} N={N} k={k} I={I} drop={drop}")
+    rng = np.random.default_rng(7100 + COMBINE_CASES.index(case))
+    dev = torch.device("cuda")
+    x = synth.f32_to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    w13 = synth.f32_to_bf16_bits(0.02 * rng.standard_normal((N, 2 * I, H), dtype=np.float32))
+    w2 = synth.f32_to_bf16_bits(0.02 * rng.standard_normal((N, H, I), dtype=np.float32))
+    xd, w13d, w2d = (elem_tensor(a, "bf16", dev) for a in (x, w13, w2))
+    if packed:
+        w13d, w2d = B.moe_pack_weights(w13d, w2d)
+    ws = B.new_workspace(B.moe_ffn_combine_workspace_size(T, N, k, H, I, torch.bfloat16), dev)
+    ws_two = B.new_workspace(B.moe_ffn_workspace_size(T, N, k, H, I, torch.bfloat16), dev)
+    # two calls on the same workspace: the second keeps fewer slots
+    for call, dropped in enumerate((drop, min(1.0, drop + 0.25))):
+        slot = _slots(T, N, k, mode, rng)
+        slot[rng.random((T, k)) < dropped] = -1
+        offsets, row_token, _, slot_row = O.dispatch(slot, N)
+        M = int(offsets[-1])
+        gates = rng.uniform(0.01, 1.0, (T, k)).astype(np.float32)
+        off_d = torch.from_numpy(offsets).to(dev)
+        rt = np.zeros(T * k, dtype=np.int32)  # rows past M are not read
+        rt[:M] = row_token
+        rt_d = torch.from_numpy(rt).to(dev)
+        sr_d = torch.from_numpy(slot_row).to(dev)
+        g_d = torch.from_numpy(gates).to(dev)
+
+        rows_f = torch.full((T * k, H), float("nan"), dtype=torch.bfloat16, device=dev)
+        y_f = torch.full((T, H), float("nan"), dtype=torch.bfloat16, device=dev)
+        B.moe_expert_ffn_combine(xd, rt_d, off_d, w13d, w2d, sr_d, g_d, k, ws, rows_f, y_f,
+                                 panels=packed)
+        rows_2 = torch.full_like(rows_f, float("nan"))
+        B.moe_expert_ffn(xd, rt_d, off_d, w13d, w2d, k, ws_two, rows_2, panels=packed)
+        y_2 = B.moe_combine(rows_2, sr_d, g_d)
+        torch.cuda.synchronize()
+
+        bits = lambda t: t.contiguous().view(torch.int16)
+        assert torch.equal(bits(rows_f[:M]), bits(rows_2[:M])), f"call {call}: out_rows differ"
+        assert torch.equal(bits(y_f), bits(y_2)), f"call {call}: y differs from moe_combine"
+        tickets = ws[: (H // 32) * 4].view(torch.int32)
+        assert int(tickets.abs().sum().item()) == 0, f"call {call}: tickets not back to zero"
+        rows64 = rows_f[:M].float().cpu().numpy().astype(np.float64)
+        y_ref = O.combine(range(T), slot, slot_row, gates.astype(np.float64), rows64, H)
+        assert_y_close(y_f.float().cpu().numpy().astype(np.float64), y_ref, "bf16")
+        say(f"  call {call}: {M} rows kept, y equal to the two calls")
