@@ -490,9 +490,23 @@ def measure(wl, args, with_cpu=False):
                           lay.disp["expert_offsets"], w13s[i % len(w13s)], k, h,
                           panels=panels)
 
+    # decode batches of at most 16 dispatch rows on packed weights whose down
+    # half runs as a GEMV (I / 256 in 1, 2, 3, 4, 8): the combine is folded
+    # into it (moe_ffn_down_combine), so "down" below times both
+    fold = (panels and decode and T * k <= 16 and I % 256 == 0
+            and I // 256 in (1, 2, 3, 4, 8))
+    ws_comb = (B.new_workspace(B.moe_ffn_combine_workspace_size(
+        T, N, k, H, I, torch_elem_dtype(wl.dtype)), dev) if fold else None)
+
     def down(i):
-        B.moe_ffn_down(h, lay.disp["expert_offsets"], w2s[i % len(w2s)], T, k,
-                       lay.out_rows, panels=panels)
+        if fold:
+            B.moe_ffn_down_combine(h, lay.disp["row_token"], lay.disp["expert_offsets"],
+                                   w2s[i % len(w2s)], lay.disp["slot_row"],
+                                   lay.topk_gates, T, k, ws_comb, lay.out_rows, lay.y,
+                                   panels=panels)
+        else:
+            B.moe_ffn_down(h, lay.disp["expert_offsets"], w2s[i % len(w2s)], T, k,
+                           lay.out_rows, panels=panels)
 
     def step(i, skip=()):
         lay.routing(d["logits"], d["is_visual"], d["entropy_w"], d["modality"],
@@ -502,7 +516,8 @@ def measure(wl, args, with_cpu=False):
             gate_up(i)
         if "down" not in skip:
             down(i)
-        B.moe_combine(lay.out_rows, lay.disp["slot_row"], lay.topk_gates, lay.y)
+        if not fold:
+            B.moe_combine(lay.out_rows, lay.disp["slot_row"], lay.topk_gates, lay.y)
 
     for i in range(args.warmup):
         step(i)
@@ -590,6 +605,7 @@ def measure(wl, args, with_cpu=False):
         mode="eager" if graph_ms is None or eager_ms <= graph_ms else "hip-graph",
         steps=steps,
         routing="fused" if fused else "separate",
+        combine="folded into down" if fold else "separate",
         weights="panels" if panels else "rows",
         union_baseline=int(len(np.unique(topk))),
         union_sere=int(len(np.unique(slot_sere))),
@@ -666,7 +682,7 @@ def _brief(m):
     keys = ("step_us", "tokens_per_s", "graph_step_us_p10_p50_p90", "kernels_us",
             "kernels_roofline", "step_roofline", "union_baseline", "union_sere",
             "union_final", "kept_rows", "dropped", "macs_rerouted",
-            "max_load_tokens", "mean_active_load_tokens", "mode", "routing")
+            "max_load_tokens", "mean_active_load_tokens", "mode", "routing", "combine")
     return {"workload": m["workload"], **{k: m[k] for k in keys if k in m}}
 
 
@@ -732,7 +748,7 @@ def main():
             "kept_rows": head["kept_rows"], "dropped": head["dropped"],
             "macs_rerouted": head["macs_rerouted"],
             "weight_copies": args.copies, "routing": head["routing"],
-            "mode": head["mode"],
+            "combine": head["combine"], "mode": head["mode"],
         },
         "roofline": head["roofline"],
         "step_roofline": head["step_roofline"],

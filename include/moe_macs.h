@@ -384,6 +384,11 @@ int moe_ffn_down(const void* h, const int32_t* expert_offsets, const void* w2,
  * moe_ffn_combine_workspace_size(), and the ticket words must be filled
  * with zero bytes once before the first use (every call leaves them zero).
  * Shapes as moe_expert_ffn, and H % 8 == 0; errors as moe_expert_ffn.
+ *
+ * moe_ffn_down_combine is the second half (moe_ffn_down then moe_combine,
+ * h passed explicitly, [T*k, I] of dtype, with the tickets at the start of
+ * its workspace: moe_ffn_combine_workspace_size() bytes suffice), for
+ * callers that schedule or time the halves separately.
  */
 size_t moe_ffn_combine_workspace_size(int T, int N, int k, int H, int I, int dtype);
 int moe_expert_ffn_combine(const void* x, const int32_t* row_token,
@@ -393,6 +398,12 @@ int moe_expert_ffn_combine(const void* x, const int32_t* row_token,
                            int I, int dtype, void* out_rows, void* y,
                            void* workspace, size_t workspace_bytes,
                            void* stream);
+int moe_ffn_down_combine(const void* h, const int32_t* row_token,
+                         const int32_t* expert_offsets, const void* w2,
+                         const int32_t* slot_row, const float* topk_gates, int T,
+                         int N, int k, int H, int I, int dtype, void* out_rows,
+                         void* y, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /*
  * moe_pack_weights -- the expert weights in the panel layout that the

@@ -63,6 +63,8 @@ _SIGS = {
     "moe_ffn_combine_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "moe_expert_ffn_combine": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I,
                                     _I, _I, _I, _P, _P, _P, _SZ, _P]),
+    "moe_ffn_down_combine": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                                  _I, _P, _P, _P, _SZ, _P]),
     "moe_expert_ffn_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
                                     _P, _P]),
     "moe_ffn_gate_up": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
@@ -427,6 +429,26 @@ def moe_expert_ffn_combine(x, row_token, expert_offsets, w13, w2, slot_row,
         _dev(y, x.dtype, "y", (T, H)),
         _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
     _check(rc, "moe_expert_ffn_combine")
+    return y
+
+
+def moe_ffn_down_combine(h, row_token, expert_offsets, w2, slot_row, topk_gates,
+                         T, k, workspace, out_rows, y, panels=False):
+    """Second half of moe_expert_ffn_combine: the down GEMM and the combine
+    (folded in where moe_expert_ffn_combine folds it), h given."""
+    N, H, I = w2.shape
+    dt = _ffn_format(h.dtype, panels)
+    rc = _lib.moe_ffn_down_combine(
+        _dev(h, h.dtype, "h", (T * k, I)),
+        _dev(row_token, torch.int32, "row_token", (T * k,)),
+        _dev(expert_offsets, torch.int32, "expert_offsets", (N + 1,)),
+        _dev(w2, h.dtype, "w2"),
+        _dev(slot_row, torch.int32, "slot_row", (T, k)),
+        _dev(topk_gates, torch.float32, "topk_gates", (T, k)),
+        T, N, k, H, I, dt, _dev(out_rows, h.dtype, "out_rows", (T * k, H)),
+        _dev(y, h.dtype, "y", (T, H)),
+        _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
+    _check(rc, "moe_ffn_down_combine")
     return y
 
 

@@ -1336,15 +1336,42 @@ template <int MODE, int NPW, int L, int BMX>
 __global__ __launch_bounds__(4 * MOE_WAVE) void gemm_stream_kernel(Args a) {
   extern __shared__ __align__(16) unsigned char smem[];
   int* cum = reinterpret_cast<int*>(smem + 2 * BMX * 64 * 2);  // after the A stages
-  const int total = tile_table<BMX>(a, cum);
+  // The first tile is located from the table in registers (no barrier or
+  // LDS round trips before its loads), which wave 0 also leaves in LDS for
+  // the later tiles; past 64 * REG_CHUNKS experts the LDS table serves all.
+  const bool regs = a.N < 64 * REG_CHUNKS;
+  int total, j1 = 0, m01 = 0, nt1 = 0, Mj1 = 0, r01 = 0;
   const int p = blockIdx.x;
+  if (regs) {
+    TileRegs tr;
+    tile_regs<BMX>(a, tr);
+    total = tr.total;
+    if (threadIdx.x < MOE_WAVE) {
+#pragma unroll
+      for (int c = 0; c < REG_CHUNKS; ++c)
+        if (lane_id() + 64 * c < a.N) cum[lane_id() + 64 * c + 1] = tr.cum[c];
+      if (threadIdx.x == 0) cum[0] = 0;
+    }
+    const int q1 = (total + 7) / 8, L1 = (p % 8) * q1 + p / 8;
+    if (p / 8 < q1 && L1 < total) locate_regs<BMX>(a, tr, L1, j1, m01, nt1, Mj1, r01);
+  } else {
+    total = tile_table<BMX>(a, cum);
+  }
   const int q = (total + 7) / 8;  // tiles per XCD
   const int step = gridDim.x / 8;
   for (int slot = p / 8; slot < q; slot += step) {
     const int Lt = (p % 8) * q + slot;
     if (Lt >= total) break;
     int j, m0, nt, Mj, row0;
-    locate_tile<BMX>(a, cum, Lt, j, m0, nt, Mj, row0);
+    if (regs && slot == p / 8) {
+      j = j1;
+      m0 = m01;
+      nt = nt1;
+      Mj = Mj1;
+      row0 = r01;
+    } else {
+      locate_tile<BMX>(a, cum, Lt, j, m0, nt, Mj, row0);  // after a workgroup barrier
+    }
     j = __builtin_amdgcn_readfirstlane(j);
     m0 = __builtin_amdgcn_readfirstlane(m0);
     nt = __builtin_amdgcn_readfirstlane(nt);
@@ -1928,6 +1955,16 @@ static bool down_combine_fused(int T, int N, int k, int I, int dtype) {
   return dtype == MOE_BF16_PANELS && decode_tiles(T, N, k) && gemv_ok(DOWN, T, k, I, true);
 }
 
+// Down tiles streamed from packed weights (decode batches past the GEMV and
+// the 16-row tiles): 256 output columns a tile when the tiles fill the CUs
+// 8 times over, else 128.
+static int launch_down_stream(const Args& d, int T, int N, int k, int H, hipStream_t s) {
+  const long experts = std::min(static_cast<long>(N), static_cast<long>(T) * k);
+  return experts * (H / 128) >= 8L * cu_count()
+             ? launch_gemm_stream<DOWN, 2, MOE_STREAM_L, MOE_STREAM_BMX_DN>(d, T * k, s)
+             : launch_gemm_stream<DOWN, 1, MOE_STREAM_L, MOE_STREAM_BMX_DN>(d, T * k, s);
+}
+
 extern "C" int moe_ffn_down(const void* h, const int32_t* expert_offsets,
                             const void* w2, int T, int N, int k, int H, int I,
                             int dtype, void* out_rows, void* stream) {
@@ -1956,10 +1993,7 @@ extern "C" int moe_ffn_down(const void* h, const int32_t* expert_offsets,
     if (gemv_ok(DOWN, T, k, I, d.panels)) {
       st = launch_gemv_rows<DOWN>(d, rows_cap, s);
     } else if (MOE_STREAM_DN && d.panels && !skinny_tiles(T, k, DOWN)) {
-      const long experts = std::min(static_cast<long>(N), static_cast<long>(T) * k);
-      st = experts * (H / 128) >= 8L * cu_count()
-               ? launch_gemm_stream<DOWN, 2, MOE_STREAM_L, MOE_STREAM_BMX_DN>(d, rows_cap, s)
-               : launch_gemm_stream<DOWN, 1, MOE_STREAM_L, MOE_STREAM_BMX_DN>(d, rows_cap, s);
+      st = launch_down_stream(d, T, N, k, H, s);
     } else if (skinny_tiles(T, k, DOWN)) {
       st = launch_gemm_skinny<DOWN>(d, rows_cap, s);
     } else if (I >= 4096) {
@@ -2023,6 +2057,32 @@ extern "C" size_t moe_ffn_combine_workspace_size(int T, int N, int k, int H, int
   return ticket_bytes(H) + moe_ffn_workspace_size(T, N, k, H, I, dtype);
 }
 
+extern "C" int moe_ffn_down_combine(const void* h, const int32_t* row_token,
+                                    const int32_t* expert_offsets, const void* w2,
+                                    const int32_t* slot_row, const float* topk_gates, int T,
+                                    int N, int k, int H, int I, int dtype, void* out_rows,
+                                    void* y, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  const int st = check_ffn_shape(T, N, k, H, I, dtype);
+  if (st != MOE_OK) return st;
+  if (H % 8 != 0) return MOE_EUNSUP;  // the combine's row vectors
+  if (T == 0) return MOE_OK;
+  if (!workspace || workspace_bytes < ticket_bytes(H)) return MOE_EINVAL;
+  if (!h || !row_token || !expert_offsets || !w2 || !slot_row || !topk_gates || !out_rows || !y)
+    return MOE_EINVAL;
+  if (down_combine_fused(T, N, k, I, dtype)) {
+    const Args d = down_args(h, expert_offsets, w2, T, N, k, H, I, dtype, out_rows);
+    const Comb c{slot_row, topk_gates, static_cast<uint16_t*>(y),
+                 static_cast<unsigned*>(workspace), T, k};
+    if (launch_gemv_rows<DOWN, true>(d, T * k, as_stream(stream), c) != MOE_OK) return MOE_EHIP;
+    return launch_status();
+  }
+  const int r = moe_ffn_down(h, expert_offsets, w2, T, N, k, H, I, dtype, out_rows, stream);
+  if (r != MOE_OK) return r;
+  return moe_combine(out_rows, slot_row, topk_gates, T, k, H,
+                     dtype == MOE_F32 ? MOE_F32 : MOE_BF16, y, stream);
+}
+
 extern "C" int moe_expert_ffn_combine(const void* x, const int32_t* row_token,
                                       const int32_t* expert_offsets, const void* w13,
                                       const void* w2, const int32_t* slot_row,
@@ -2031,29 +2091,20 @@ extern "C" int moe_expert_ffn_combine(const void* x, const int32_t* row_token,
                                       void* workspace, size_t workspace_bytes, void* stream) {
   const int st = check_ffn_shape(T, N, k, H, I, dtype);
   if (st != MOE_OK) return st;
-  if (T == 0) return MOE_OK;
   if (H % 8 != 0) return MOE_EUNSUP;  // the combine's row vectors
+  if (T == 0) return MOE_OK;
   if (!workspace || workspace_bytes < moe_ffn_combine_workspace_size(T, N, k, H, I, dtype))
     return MOE_EINVAL;
   if (!x || !row_token || !expert_offsets || !w13 || !w2 || !slot_row || !topk_gates ||
       !out_rows || !y)
     return MOE_EINVAL;
-  unsigned* tickets = static_cast<unsigned*>(workspace);
-  void* h = static_cast<unsigned char*>(workspace) + ticket_bytes(H);
+  const size_t tb = ticket_bytes(H);
+  void* h = static_cast<unsigned char*>(workspace) + tb;
   const int r = moe_ffn_gate_up(x, row_token, expert_offsets, w13, T, N, k, H, I, dtype, h,
                                 stream);
   if (r != MOE_OK) return r;
-  if (down_combine_fused(T, N, k, I, dtype)) {
-    const Args d = down_args(h, expert_offsets, w2, T, N, k, H, I, dtype, out_rows);
-    const Comb c{slot_row, topk_gates, static_cast<uint16_t*>(y), tickets, T, k};
-    if (launch_gemv_rows<DOWN, true>(d, T * k, as_stream(stream), c) != MOE_OK)
-      return MOE_EHIP;
-    return launch_status();
-  }
-  const int r2 = moe_ffn_down(h, expert_offsets, w2, T, N, k, H, I, dtype, out_rows, stream);
-  if (r2 != MOE_OK) return r2;
-  return moe_combine(out_rows, slot_row, topk_gates, T, k, H,
-                     dtype == MOE_F32 ? MOE_F32 : MOE_BF16, y, stream);
+  return moe_ffn_down_combine(h, row_token, expert_offsets, w2, slot_row, topk_gates, T, N, k,
+                              H, I, dtype, out_rows, y, workspace, tb, stream);
 }
 
 extern "C" int moe_pack_weights(const void* w13, const void* w2, int N, int H, int I,

@@ -13,9 +13,10 @@ separately; the row-layout kernels (tile MFMA) agree to the same bound.
 
 moe_expert_ffn_combine (the combine folded into the down GEMV) is checked
 against moe_expert_ffn + moe_combine bit for bit -- out_rows and y -- with
-dropped slots, every slot dropped, and shapes that take the two-call path,
-over two calls in a row on one workspace whose arrival tickets must be zero
-again after each; y also against the oracle's combine of the same rows.
+dropped slots, tokens or whole batches with every slot dropped, and shapes
+that take the two-call path, over two calls in a row on one workspace whose
+arrival tickets must be zero again after each; y also against the oracle's
+combine of the same rows.
 """
 import numpy as np
 import pytest
@@ -122,8 +123,11 @@ COMBINE_CASES = [
     ("t16_k1", 16, 512, 4, 1, 256, "repeat", 0.2, True),
     ("k2048_down", 4, 512, 3, 2, 2048, "spread", 0.0, True),
     ("every_slot_dropped", 2, 512, 8, 4, 256, "spread", 1.0, True),
-    # two calls: more rows than the GEMV takes, and the row layout
-    ("b8_qwen3_shape_tiles", 8, 2048, 128, 8, 768, "spread", 0.1, False),
+    # two calls: more rows than the GEMV takes (streamed down tiles, with
+    # tokens whose every slot is dropped), and the row layout
+    ("b8_qwen3_shape_stream", 8, 2048, 128, 8, 768, "spread", 0.1, True),
+    ("b64_dropped_tokens_stream", 64, 1024, 16, 4, 512, "spread", 0.5, True),
+    ("b8_qwen3_shape_rows", 8, 2048, 128, 8, 768, "spread", 0.1, False),
     ("b2_rows_layout", 2, 512, 8, 4, 256, "spread", 0.0, False),
 ]
 
