@@ -56,9 +56,9 @@ DIFF_REPS = 5  # timed-region pairs per in-step kernel duration
 
 HBM_COUNTERS = {
     "qwen3_decode_b128": dict(
-        kernel="gate_up_swiglu", fetch_kib=130569.0, write_kib=1536.9,
+        kernel="gate_up_swiglu", fetch_kib=130573.1, write_kib=1536.6,
         fetch_scale=2.0, write_scale=1.0,
-        sources_sha256="98727dc8084ea2addb6c531a94fcb0551bf1020d3a6d6ddea3305a05653fed33"),
+        sources_sha256="896c908a151d0d51f73c2835683116d6d8575aff9451e3a6766e8e65d94b586f"),
 }
 
 
