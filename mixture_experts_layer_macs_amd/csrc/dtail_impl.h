@@ -376,19 +376,20 @@ __device__ __forceinline__ void run(const Args& a, unsigned char* dyn, Lds& L) {
         const int p0 = sub * 32, rot = e & 31;
         float v[32];
 #pragma unroll
-        for (int q = 0; q < 32; ++q) {
-          const int p = p0 + ((q + rot) & 31);
-          v[q] = p < N ? srow[p] : 0.f;
-        }
+        for (int q = 0; q < 32; ++q)  // (clamped: columns past N have no primary bit)
+          v[q] = srow[min(p0 + ((q + rot) & 31), N - 1)];
         const uint64_t pw = sub < 2 ? pm0 : pm1;
         const uint32_t bits = static_cast<uint32_t>(pw >> ((sub & 1) * 32));
+        // branch-free: the test of beats() with bitwise operators and two
+        // selects per column (short-circuit forms compile to a divergent
+        // branch per column)
 #pragma unroll
         for (int q = 0; q < 32; ++q) {
-          const int c = (q + rot) & 31;
-          if (((bits >> c) & 1u) && beats(v[q], p0 + c, bv, bp)) {
-            bv = v[q];
-            bp = p0 + c;
-          }
+          const int c = (q + rot) & 31, pc = p0 + c;
+          const bool take = ((bits >> c) & 1u) != 0u &
+                            ((v[q] > bv) | ((v[q] == bv) & (pc < bp)));
+          bv = take ? v[q] : bv;
+          bp = take ? pc : bp;
         }
       }
     } else if (mv) {

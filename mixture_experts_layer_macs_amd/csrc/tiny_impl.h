@@ -203,13 +203,14 @@ __global__ __launch_bounds__(MAX_THREADS) void routing_kernel(Args A) {
           v[q] = a.sim[row + ps[q]];
           pr[q] = a.prot[row + ps[q]];
         }
+        // branch-free (short-circuit forms compile to a branch per entry)
 #pragma unroll
-        for (int q = 0; q < 16; ++q)
-          if (c0 + q < np && (bp < 0 || v[q] > bv)) {
-            bv = v[q];
-            bp = ps[q];
-            bpr = pr[q];
-          }
+        for (int q = 0; q < 16; ++q) {
+          const bool take = (c0 + q < np) & ((bp < 0) | (v[q] > bv));
+          bv = take ? v[q] : bv;
+          bp = take ? ps[q] : bp;
+          bpr = take ? pr[q] : bpr;
+        }
       }
       moved = bv > a.rho && bpr == 0u;  // np >= 1 whenever a slot is movable
       if (moved) cur = bp;
