@@ -462,6 +462,48 @@ def test_graph_replay_matches_eager(fused):
         assert torch.equal(lay.y, ref_y)
 
 
+@pytest.mark.parametrize("T", [1, 2])
+def test_graph_replay_packed_small_batch(T):
+    """A decode layer of one or two tokens on packed weights (the one-workgroup
+    routing, the GEMVs and the combine folded into the down GEMV, whose
+    arrival tickets live in the layer's workspace) captured in a HIP graph:
+    every replay, with eager work between replays, reproduces the eager y
+    bit for bit, and the tickets are zero after each."""
+    import torch
+    from mixture_experts_layer_macs_amd import binding as B
+    from mixture_experts_layer_macs_amd.staging import to_device
+    wl = configs.SWEEP_LAYER.with_(T=T, kprime=2)
+    say(f"graph replay, packed weights, T={T}")
+    inp = synth.make_inputs(wl, 5)
+    d = to_device(inp, "cuda")
+    p13, p2 = B.moe_pack_weights(d["w13"], d["w2"])
+    lay = B.Layer(wl.T, wl.H, wl.N, wl.k, wl.I, wl.R, torch.bfloat16)
+    args = (d["logits"], d["x"], p13, p2, d["is_visual"], d["entropy_w"],
+            d["modality"], d["sim"], d["prot"], wl.kprime, wl.rho, wl.gamma,
+            wl.lam, wl.group)
+    tickets = lambda: lay.ws_ffn[: (wl.H // 32) * 4].view(torch.int32)
+    lay.forward(*args, panels=True)
+    torch.cuda.synchronize()
+    ref_y = lay.y.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=s):
+        lay.forward(*args, panels=True)
+    for i in range(4):
+        lay.y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(lay.y.view(torch.int16), ref_y.view(torch.int16)), f"replay {i}: y"
+        assert int(tickets().abs().sum().item()) == 0, f"replay {i}: tickets"
+        lay.forward(*args, panels=True)  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(lay.y.view(torch.int16), ref_y.view(torch.int16))
+    # the eager result against the oracle's layer
+    _, y_ref = O.layer_forward(inp)
+    assert_y_close(lay.y.float().cpu().numpy().astype(np.float64), y_ref, "bf16")
+
+
 ENTROPY_CASES = [
     ("bf16_t8192_h2048", 8192, 2048, "bf16", "runs70", 1.0, 0),
     ("bf16_t333_h768_delta3", 333, 768, "bf16", "half", 3.0, 1),
