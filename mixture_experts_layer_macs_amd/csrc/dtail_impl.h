@@ -246,27 +246,49 @@ __device__ __forceinline__ void run(const Args& a, unsigned char* dyn, Lds& L) {
   float* s_sim = reinterpret_cast<float*>(dyn);
   uint8_t* s_prot = dyn + static_cast<size_t>(N) * N * 4;
 
-  // ---- every input, one batch of loads
-  int e_in[SPT];
+  // ---- every input, one batch of loads: each issued unconditionally at a
+  // clamped index and held (pin) until all are issued, so the batch costs
+  // one round trip (a load behind a per-lane condition is waited for on its
+  // own); the lane conditions apply afterwards.  (Ids are clamped to
+  // [0, N): an id out of range could never index past an array.)
+  int e_in[SPT], fbv[FPT];
+  uint8_t vis;
+  float ew;
+  int mod;
+  {
+    int re[SPT], rf[FPT];
 #pragma unroll
-  for (int j = 0; j < SPT; ++j) {
-    const int i = tid + j * NT;
-    // (clamped: an id out of range could never index past an array)
-    e_in[j] = i < Tk ? min(max(a.topk[i], 0), N - 1) : -1;
-  }
-  int fbv[FPT];
+    for (int j = 0; j < SPT; ++j) re[j] = a.topk[min(tid + j * NT, Tk - 1)];
+    const int32_t* fbp = TR > 0 ? a.fb : a.topk;  // (R = 0: no fallback array)
+    const int fbn = TR > 0 ? TR : Tk;
 #pragma unroll
-  for (int j = 0; j < FPT; ++j) {
-    const int i = tid + j * NT;
-    fbv[j] = i < TR ? min(max(a.fb[i], 0), N - 1) : 0;
+    for (int j = 0; j < FPT; ++j) rf[j] = fbp[min(tid + j * NT, fbn - 1)];
+    int rv = a.vis[min(tid, T - 1)];
+    float rw = a.ew[min(tid, T - 1)];
+    int rm = a.mod[min(tid, N - 1)];
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) pin(re[j]);
+#pragma unroll
+    for (int j = 0; j < FPT; ++j) pin(rf[j]);
+    pin(rv);
+    pin(rm);
+    int rwi = __float_as_int(rw);
+    pin(rwi);
+#pragma unroll
+    for (int j = 0; j < SPT; ++j)
+      e_in[j] = tid + j * NT < Tk ? min(max(re[j], 0), N - 1) : -1;
+#pragma unroll
+    for (int j = 0; j < FPT; ++j)
+      fbv[j] = tid + j * NT < TR ? min(max(rf[j], 0), N - 1) : 0;
+    vis = tid < T ? static_cast<uint8_t>(rv) : 0;
+    ew = tid < T ? __int_as_float(rwi) : 0.f;
+    mod = tid < N ? rm : 0;
   }
-  const uint8_t vis = tid < T ? a.vis[tid] : 0;
-  const float ew = tid < T ? a.ew[tid] : 0.f;
-  const int mod = tid < N ? a.mod[tid] : 0;
   if (sere && a.sim_lds) {
     // N <= 128: every thread issues all its 16-byte loads (8 of the rows,
     // 2 of the protection bytes) before the first store, so the copy costs
-    // one memory round trip
+    // one memory round trip (issued after the batch above, not with it:
+    // one batch of both measured slower)
     const int nn = N * N;
     if ((nn & 15) == 0 && ((reinterpret_cast<uintptr_t>(a.sim) |
                            reinterpret_cast<uintptr_t>(a.prot)) & 15) == 0) {
