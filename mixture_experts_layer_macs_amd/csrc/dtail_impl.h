@@ -303,6 +303,14 @@ __device__ __forceinline__ void run(const Args& a, unsigned char* dyn, Lds& L) {
 #pragma unroll
       for (int j = 0; j < QP; ++j)
         pv[j] = reinterpret_cast<const uint4*>(a.prot)[min(tid + j * NT, n16 - 1)];
+      // held until all are issued (each value's only use is a guarded store,
+      // into which the compiler would otherwise sink its load and wait)
+#pragma unroll
+      for (int j = 0; j < QS; ++j)
+        asm volatile("" : "+v"(sv[j].x), "+v"(sv[j].y), "+v"(sv[j].z), "+v"(sv[j].w));
+#pragma unroll
+      for (int j = 0; j < QP; ++j)
+        asm volatile("" : "+v"(pv[j].x), "+v"(pv[j].y), "+v"(pv[j].z), "+v"(pv[j].w));
 #pragma unroll
       for (int j = 0; j < QS; ++j) {
         const int q = tid + j * NT;
