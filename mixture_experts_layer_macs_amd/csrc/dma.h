@@ -16,6 +16,7 @@
 namespace moe {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // A byte offset past every resource of at most 2^31 bytes: loads there fill
 // LDS with zeros and fetch nothing.
@@ -39,6 +40,22 @@ __device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t voff, uint32_t so
   asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc),
                "s"(soff), "{m0}"(m0)
                : "memory");
+}
+
+// 16-byte store through a buffer resource over [base, base + bytes).
+// Offsets outside the range are dropped by the hardware, so a store of rows
+// past a tile's end needs no branch and every lane issues the same number of
+// vector-memory instructions (the counted waits of a ring that also holds
+// loads rely on that count).  Written with the compiler's builtin, not as
+// inline assembly, so that the compiler knows the instruction reads its
+// data registers and keeps later writes of them at the required distance.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t store_rsrc(void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
+                                            u32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, static_cast<int>(voff), 0, 0);
 }
 
 // s_waitcnt with only the vector-memory counter limited (gfx9 encoding:

@@ -723,6 +723,313 @@ void gemm_dma_kernel(Args a) {
   gemm_tile<MODE, BM, BN, BK, WM, WN, S, SB>(a, smem, reinterpret_cast<int*>(smem));
 }
 
+// ------------------------------------------------ persistent prefill down
+// One workgroup per CU walks a fixed list of 256 x 256 tiles, and the ring
+// runs on across tile boundaries: slice g of the workgroup's whole sequence
+// (tile g / nk, K slice g % nk) lands in A stage g % SA and B stage g % SB,
+// the token rows one slice ahead and the weights two, whatever tile they
+// belong to.  The next tile's first slices are therefore in flight while
+// the current tile's last slices are multiplied and its results stored,
+// where a workgroup per tile pays a launch slot, the ring fill and the
+// output store back to back.  The down reduction (K = I, e.g. 12 slices of
+// 64 for I = 768) is short enough for that to matter.
+//
+// Tiles: the table of find_tile (experts' row tiles times column tiles), XCD
+// x owning the contiguous range [x q, x q + q), q = ceil(total / 8); slot s
+// of an XCD (workgroup p = 8 s + x) takes tiles x q + s, x q + s + G / 8,
+// ..., so tiles of one expert run side by side on one XCD and share its L2.
+// The grid G is a multiple of 8; every (slot, XCD) pair is one workgroup,
+// so the lists partition the tiles.
+//
+// Output: when a tile's last slice has been multiplied, the A and B stages
+// of that slice are free until the next iteration requests into them (the
+// requests in flight target the other stages).  The tile leaves through
+// them in two halves of 128 rows: the waves of that half write their bf16
+// results (rows 0-63 of the half in the A stage, 64-127 in the B stage, 16-
+// byte chunks XOR-swizzled by row), then every wave stores whole rows with
+// 16-byte stores through a buffer resource over the tile's rows, so rows
+// past the tile's end are dropped without a branch and every lane issues
+// exactly NST stores per tile.  The wait after a tile's stores counts them:
+// A(g + 1), issued before B(g + SB - 1) and the stores, has landed once at
+// most QB + NST of the wave's vector-memory instructions are outstanding
+// (gfx9 retires vector loads and stores in issue order).  Spreading the
+// output over whole 512-byte rows matters: every CU reaches a tile's end at
+// about the same time, and per-lane 8-byte stores of the MFMA layout (32
+// rows per instruction) made the stores alone cost about a quarter of the
+// kernel.
+template <int BM, int BN, int BK, int WM, int WN, int SA, int SB>
+__global__ __launch_bounds__(WM * WN * MOE_WAVE)
+__attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
+void gemm_persist_down_kernel(Args a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int W = WM * WN;
+  static_assert(W == 4 || W == 8, "4 or 8 waves");
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int CPR = BK / 8;
+  constexpr int SWZ = CPR - 1;
+  constexpr int SWS = BK == 64 ? 1 : (BK == 32 ? 2 : 0);
+  constexpr int RPJ = MOE_WAVE / CPR;
+  constexpr int NA = BM / RPJ, NB = BN / RPJ;
+  static_assert(NA % W == 0 && NB % W == 0, "split over the waves");
+  constexpr int QA = NA / W, QB = NB / W, LPW = QA + QB;
+  constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+  constexpr int B_BASE = SA * A_BYTES;
+  static_assert(SA == 2 && SB >= 3, "token rows one slice ahead, weights two or more");
+  constexpr int NTH = W * MOE_WAVE;
+  constexpr int NST = 2 * (BM / 2) * BN * 2 / (NTH * 16);  // 16-byte stores per lane per tile
+  static_assert(QB + NST < 64, "vmcnt range");
+  static_assert(BM == 256 && BN == 256 && BK == 64 && WM == 2 && A_BYTES == 32768 &&
+                    B_BYTES == 32768,
+                "output staging: half a tile (128 rows) in one free A and one free B stage");
+  constexpr int KK = BK / 16;
+  constexpr int NFR = FM + FN, NMF = FM * FN;
+
+  TileRegs tr;
+  tile_regs<BM>(a, tr);
+  const int total = tr.total;
+  const int p = blockIdx.x, nslot = gridDim.x / 8;
+  const int q = (total + 7) / 8;
+  const int lo = (p % 8) * q, hi = min(lo + q, total);
+  const int first = lo + p / 8;
+  if (first >= hi) return;
+  const int ntile = (hi - first + nslot - 1) / nslot;
+  const int nk = a.K / BK;
+
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / MOE_WAVE);
+  const int wm = wave / WN, wn = wave % WN;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.K) * 2;
+  const int lrow = lane / CPR, lslot = lane % CPR;
+
+  struct Tile {
+    int j, m0, nt, Mj, row0;
+  };
+  auto tile_at = [&](int n, Tile& t) {
+    locate_regs<BM>(a, tr, first + n * nslot, t.j, t.m0, t.nt, t.Mj, t.row0);
+    t.j = __builtin_amdgcn_readfirstlane(t.j);
+    t.m0 = __builtin_amdgcn_readfirstlane(t.m0);
+    t.nt = __builtin_amdgcn_readfirstlane(t.nt);
+    t.Mj = __builtin_amdgcn_readfirstlane(t.Mj);
+    t.row0 = __builtin_amdgcn_readfirstlane(t.row0);
+  };
+
+  // A: the tile's own rows of h; the per-lane offsets do not depend on the
+  // tile (rows past its end fall outside the resource and read as zeros).
+  uint32_t va[QA];
+#pragma unroll
+  for (int d = 0; d < QA; ++d) {
+    const int row = (wave * QA + d) * RPJ + lrow;
+    va[d] = static_cast<uint32_t>(row) * row_bytes + (lslot ^ ((row >> SWS) & SWZ)) * 16;
+  }
+  // B: rows of the tile's column block of w2.
+  uint32_t vb[QB];
+  i32x4 rsrc_a, rsrc_b;
+  auto set_a = [&](const Tile& t) {
+    rsrc_a = buffer_rsrc(a.a + static_cast<size_t>(t.row0 + t.m0) * a.K,
+                         static_cast<uint32_t>(min(BM, t.Mj - t.m0)) * row_bytes);
+  };
+  auto set_b = [&](const Tile& t) {
+    rsrc_b = buffer_rsrc(a.w + static_cast<size_t>(t.j) * a.w_stride,
+                         static_cast<uint32_t>(a.w_stride) * 2);
+#pragma unroll
+    for (int d = 0; d < QB; ++d) {
+      const int row = (wave * QB + d) * RPJ + lrow;
+      vb[d] = weight_off<DOWN>(a, t.nt * BN + row, (lslot ^ ((row >> SWS) & SWZ)) * 8);
+    }
+  };
+  const uint32_t lds_base = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char*)(smem))));
+
+  // Issue cursors: tile ordinal and K slice of the next A and B requests.
+  // Past the last slice they stay on it, so the surplus requests at the end
+  // re-fetch it into stages that are never read again and every iteration
+  // issues the same number of loads.
+  int na = 0, ka = 0, nb = 0, kb = 0;
+  {
+    Tile t0;
+    tile_at(0, t0);
+    set_a(t0);
+    set_b(t0);
+  }
+  auto issue_a = [&](int g) {
+#pragma unroll
+    for (int d = 0; d < QA; ++d)
+      lds_dma16(rsrc_a, va[d], static_cast<uint32_t>(ka * BK) * 2,
+                lds_base + (g % SA) * A_BYTES + (wave * QA + d) * 1024);
+  };
+  auto issue_b = [&](int g) {
+#pragma unroll
+    for (int d = 0; d < QB; ++d)
+      lds_dma16(rsrc_b, vb[d], weight_k0(a, static_cast<uint32_t>(kb * BK)),
+                lds_base + B_BASE + (g % SB) * B_BYTES + (wave * QB + d) * 1024);
+  };
+  auto next_a = [&]() {
+    if (++ka == nk) {
+      if (na + 1 < ntile) {
+        ka = 0;
+        Tile t;
+        tile_at(++na, t);
+        set_a(t);
+      } else {
+        ka = nk - 1;
+      }
+    }
+  };
+  auto next_b = [&]() {
+    if (++kb == nk) {
+      if (nb + 1 < ntile) {
+        kb = 0;
+        Tile t;
+        tile_at(++nb, t);
+        set_b(t);
+      } else {
+        kb = nk - 1;
+      }
+    }
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int x = 0; x < FM; ++x)
+#pragma unroll
+    for (int y = 0; y < FN; ++y)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.f;
+
+  const int frow = lane & 31, fhalf = lane >> 5;
+  const int a_lane = (wm * TM + frow) * BK;
+  const int b_lane = (wn * TN + frow) * BK;
+  typedef __attribute__((address_space(3))) const bf16x8 lds_frag;
+  typedef __attribute__((address_space(3))) const unsigned char lds_byte;
+  lds_byte* lds0 = (lds_byte*)(smem);
+  bf16x8 fa[2][FM], fb[2][FN];
+  auto read_frags = [&](int g, int kk, bf16x8* pa, bf16x8* pb) {
+    lds_byte* A_ = lds0 + (g % SA) * A_BYTES;
+    lds_byte* B_ = lds0 + B_BASE + (g % SB) * B_BYTES;
+    const int sw = ((kk * 2 + fhalf) ^ ((frow >> SWS) & SWZ)) << 4;
+#pragma unroll
+    for (int x = 0; x < FM; ++x) pa[x] = *(lds_frag*)(A_ + (a_lane + x * 32 * BK) * 2 + sw);
+#pragma unroll
+    for (int y = 0; y < FN; ++y) pb[y] = *(lds_frag*)(B_ + (b_lane + y * 32 * BK) * 2 + sw);
+  };
+
+  int nfrag = FM;  // fragments of this wave with tile rows
+
+  // One slice: the A and B requests of later slices, then the MFMAs of
+  // slice g (all fragments, or only those with tile rows).
+  auto slice = [&](int g, auto full) {
+    constexpr bool FULL = decltype(full)::value;
+    issue_a(g + 1);
+    issue_b(g + SB - 1);
+    read_frags(g, 0, fa[0], fb[0]);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      if (kk + 1 < KK) read_frags(g, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+#pragma unroll
+      for (int x = 0; x < FM; ++x)
+        if (FULL || x < nfrag)
+#pragma unroll
+          for (int y = 0; y < FN; ++y)
+            acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk & 1][y], fa[kk & 1][x],
+                                                               acc[x][y], 0, 0, 0);
+      if constexpr (FULL) {
+        if (kk == 0) {
+          __builtin_amdgcn_sched_group_barrier(0x0020, LPW, 0);  // VMEM (DMA)
+          __builtin_amdgcn_sched_group_barrier(0x0100, NFR, 0);  // first reads
+        }
+        if (kk + 1 < KK) interleave_groups<NMF, NFR>();
+        else __builtin_amdgcn_sched_group_barrier(0x0008, NMF, 0);
+      }
+    }
+  };
+
+  // prologue: A(0), B(0) .. B(SB - 2)
+  issue_a(0);
+  next_a();
+#pragma unroll
+  for (int t = 0; t + 1 < SB; ++t) {
+    issue_b(t);
+    next_b();
+  }
+  const int fr = lane & 31;
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) u32x2 lds_u2;
+  typedef __attribute__((address_space(3))) const u32x4_t lds_u4r;
+  typedef __attribute__((address_space(3))) unsigned char lds_wbyte;
+  int g = 0;  // slice of the whole sequence
+  for (int nc = 0; nc < ntile; ++nc) {
+    Tile tc;
+    tile_at(nc, tc);
+    const int rows = min(BM, tc.Mj - tc.m0);
+    nfrag = min(FM, max(0, (rows - wm * TM + 31) / 32));
+    // the K loop of one tile, all fragments or only those with tile rows
+    auto run = [&](auto full) {
+      for (int kc = 0; kc < nk; ++kc, ++g) {
+        // A(g) was issued before the newest QB requests (B(g + SB - 2))
+        // and, in a tile's first slice, the previous tile's NST stores;
+        // B(g) before A(g)
+        if (kc == 0 && nc > 0) wait_vmcnt<QB + NST>();
+        else wait_vmcnt<QB>();
+        wg_barrier();
+        slice(g, full);
+        next_a();
+        next_b();
+      }
+    };
+    if (nfrag == FM) run(std::true_type{});
+    else run(std::false_type{});
+    // the tile's results through the stages of its last slice, g - 1
+    const __amdgpu_buffer_rsrc_t rsrc_o =
+        store_rsrc(a.out + static_cast<size_t>(tc.row0 + tc.m0) * a.NC + tc.nt * BN,
+                   static_cast<uint32_t>(rows) * static_cast<uint32_t>(a.NC) * 2);
+    lds_wbyte* st0 = (lds_wbyte*)(smem) + ((g - 1) % SA) * A_BYTES;
+    lds_wbyte* st1 = (lds_wbyte*)(smem) + B_BASE + ((g - 1) % SB) * B_BYTES;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      wg_barrier();  // slice g - 1's fragments, or the previous half, consumed
+      if (wm == half) {
+#pragma unroll
+        for (int x = 0; x < FM; ++x) {
+          const int r = (x % 2) * 32 + fr;  // row in its stage
+          lds_wbyte* st = x < 2 ? st0 : st1;
+#pragma unroll
+          for (int y = 0; y < FN; ++y)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+              const int ch = wn * (TN / 8) + y * 4 + qq;  // 16-byte chunk of the row
+              u32x2 pk;
+              pk.x = pack_bf16x2(acc[x][y][4 * qq], acc[x][y][4 * qq + 1]);
+              pk.y = pack_bf16x2(acc[x][y][4 * qq + 2], acc[x][y][4 * qq + 3]);
+              *(lds_u2*)(st + r * (BN * 2) + ((ch ^ (r & 31)) << 4) + fhalf * 8) = pk;
+            }
+        }
+      }
+      // this wave's LDS writes done, then everyone's
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < NST / 2; ++i) {
+        const int e = i * NTH + tid;           // 16-byte chunk of the half
+        const int r = e / (BN / 8), ch = e % (BN / 8);
+        lds_wbyte* st = r < 64 ? st0 : st1;
+        const int rr = r % 64;
+        const u32x4_t v = *(lds_u4r*)(st + rr * (BN * 2) + ((ch ^ (rr & 31)) << 4));
+        buf_store16(rsrc_o,
+                    static_cast<uint32_t>(half * 128 + r) * static_cast<uint32_t>(a.NC) * 2 +
+                        ch * 16,
+                    v);
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < FM; ++x)
+#pragma unroll
+      for (int y = 0; y < FN; ++y)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.f;
+  }
+  wait_vmcnt<0>();  // no DMA write may land after the workgroup ends
+}
+
 // Decode gate-up with the tile height chosen on the device: tiles of BMA
 // token rows (SA token-row stages, SAB weight stages) when they number at
 // most a.dual_limit, i.e. when every tile gets a workgroup slot at once,
@@ -1520,6 +1827,26 @@ static int launch_gemm_dma(const Args& a, int rows_cap, hipStream_t s) {
   return MOE_OK;
 }
 
+// Persistent prefill down GEMM: one workgroup per CU (a multiple of 8, so
+// that every XCD has the same number of tile lists).
+template <int BM, int BN, int BK, int WM, int WN, int SA, int SB>
+static int launch_gemm_persist_down(const Args& a, hipStream_t s) {
+  constexpr size_t lds = (static_cast<size_t>(SA) * BM + static_cast<size_t>(SB) * BN) * BK * 2;
+  static std::atomic<bool> attr_set[64];
+  const void* fn = reinterpret_cast<const void*>(gemm_persist_down_kernel<BM, BN, BK, WM, WN, SA, SB>);
+  const int dev = current_device();
+  if (dev < 0 || !attr_set[dev].load(std::memory_order_acquire)) {
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(lds)) != hipSuccess)
+      return MOE_EHIP;
+    if (dev >= 0) attr_set[dev].store(true, std::memory_order_release);
+  }
+  const int grid = std::max(8, cu_count() / 8 * 8);
+  hipLaunchKernelGGL((gemm_persist_down_kernel<BM, BN, BK, WM, WN, SA, SB>), dim3(grid),
+                     dim3(WM * WN * MOE_WAVE), lds, s, a);
+  return MOE_OK;
+}
+
 template <int MODE, int BN, int BK, int BMA, int SA, int SAB, int BMB, int SB, int SBB,
           int WPE>
 static int launch_gemm_dual(Args a, int rows_cap, hipStream_t s) {
@@ -1743,6 +2070,11 @@ using namespace moe::ffn;
 #endif
 #ifndef MOE_DN_STAGES_B
 #define MOE_DN_STAGES_B 3
+#endif
+// Prefill down tiles walked by one persistent workgroup per CU (below 320
+// experts, the register tile search) instead of a workgroup per tile.
+#ifndef MOE_PERSIST_DN
+#define MOE_PERSIST_DN 1
 #endif
 // Decode tiles: 32 or 128 token rows x 128 or 256 weight rows (1 x 4
 // waves), K through a streaming ring.  Measured on MI355X (qwen3 and
@@ -2020,9 +2352,12 @@ extern "C" int moe_ffn_down(const void* h, const int32_t* expert_offsets,
     if (st != MOE_OK) return MOE_EHIP;
   } else {
     d.n_tiles = H / DN_BN;
-    if (launch_gemm_dma<DOWN, DN_BM, DN_BN, DN_BK, DN_WM, DN_WN, MOE_DN_STAGES, MOE_DN_WPE,
-                        MOE_DN_STAGES_B>(d, rows_cap, s) != MOE_OK)
-      return MOE_EHIP;
+    const int st = MOE_PERSIST_DN && N < 64 * REG_CHUNKS
+                       ? launch_gemm_persist_down<DN_BM, DN_BN, DN_BK, DN_WM, DN_WN, MOE_DN_STAGES,
+                                                  MOE_DN_STAGES_B>(d, s)
+                       : launch_gemm_dma<DOWN, DN_BM, DN_BN, DN_BK, DN_WM, DN_WN, MOE_DN_STAGES,
+                                         MOE_DN_WPE, MOE_DN_STAGES_B>(d, rows_cap, s);
+    if (st != MOE_OK) return MOE_EHIP;
   }
   return launch_status();
 }
