@@ -47,6 +47,9 @@ FULL_Y_CASES = [
     ("mid_bf16_small_decode", _mid_bf16(T=7, kprime=1, n_protected=2,
                                         gamma=1.25), 6),
     ("mid_bf16_h768_i384", _mid_bf16(H=768, I=384, T=300), 7),
+    # about 1000 prefill down tiles: each persistent workgroup walks three
+    # to five, ragged ones included, so the ring crosses tile boundaries
+    ("mid_bf16_multi_tile", _mid_bf16(T=3000, N=64, k=8, H=2048, I=256), 16),
     ("qwen3_decode_b128", configs.QWEN3_DECODE, 0),
     ("qwen3_decode_b128_s1", configs.QWEN3_DECODE, 1),
     ("sweep_layer_macs_b64", configs.SWEEP_LAYER.with_(T=64, kprime=2), 0),
