@@ -56,9 +56,9 @@ DIFF_REPS = 5  # timed-region pairs per in-step kernel duration
 
 HBM_COUNTERS = {
     "qwen3_decode_b128": dict(
-        kernel="gate_up_swiglu", fetch_kib=130573.1, write_kib=1536.6,
+        kernel="gate_up_swiglu", fetch_kib=130582.0, write_kib=1536.8,
         fetch_scale=2.0, write_scale=1.0,
-        sources_sha256="896c908a151d0d51f73c2835683116d6d8575aff9451e3a6766e8e65d94b586f"),
+        sources_sha256="8e2ed701da26d2d73f0aec77c63fc73244d0d78776e312c687ff4042c12f5457"),
 }
 
 
