@@ -15,13 +15,13 @@
 //     id find a lane's peers, 17 ballot bit planes give its weighted prefix
 //     among them, a per-wave running table carries the prefix across the
 //     wave's chunks, and one scan over the waves joins them;
-//   - a fallback round costs one barrier: a token's state (its slots'
+//   - a fallback round costs two barriers: a token's state (its slots'
 //     experts, which are still overflowed, its fallback ranks) stays in the
-//     registers of one thread, the offers to one expert within a wave are
-//     joined by ballots, the per-wave totals go to a table tagged with the
-//     round number (double-buffered, so no clearing), and admitted weight
-//     is added to a per-round array, so the capacity left before round r is
-//     the capacity minus round 0's load minus rounds 1..r-1.
+//     registers of one thread, which sets the token's bit in the offer mask
+//     of the expert it offers to; one lane per expert then takes that
+//     expert's offers in token order and admits them while the running
+//     weight fits the capacity left (kept in the lane's registers across
+//     rounds), and each offering token reads its bit back.
 // Integer sums in units of 2^-16 token make every order of summation give
 // the same result as the sequential rule.
 #pragma once
@@ -41,8 +41,7 @@ constexpr int MAX_SLOTS = 2048, MAX_FB = 4096;
 constexpr int SPT = MAX_SLOTS / NT;     // slots per thread
 constexpr int FPT = MAX_FB / NT;        // fallback entries per thread
 constexpr int SIM_LDS_N = 128;          // similarity rows kept in LDS up to this N
-constexpr uint32_t TAG_SHIFT = 25;      // round tag above 25 bits of weight
-constexpr uint32_t VAL_MASK = (1u << TAG_SHIFT) - 1;
+constexpr int OM_W = MAX_T / 64;        // 64-bit words of a token mask
 
 enum : uint8_t { ST_OVER = 1, ST_PLACED = 2, ST_SERE = 4 };
 
@@ -204,8 +203,8 @@ struct Lds {
   uint32_t s_tot[MAX_N];
   int32_t s_cap[MAX_N];        // capacity, clamped to 2^30
   uint32_t s_load0[MAX_N];
-  uint32_t s_U[(MAX_R + 1) * MAX_N];
-  uint32_t s_tab[2 * 4 * MAX_N];
+  uint32_t s_U[MAX_N];          // weight placed by the fallback rounds
+  unsigned long long s_om[2 * MAX_N * OM_W];  // offer masks, by round parity
   unsigned long long s_load_off[MAX_N];
   int32_t s_off[MAX_N + 1];
   unsigned long long s_sum[4];  // W, W_vis, dropped, re-routed
@@ -234,7 +233,7 @@ __device__ __forceinline__ void run(const Args& a, unsigned char* dyn, Lds& L) {
   auto& s_cap = L.s_cap;
   auto& s_load0 = L.s_load0;
   auto& s_U = L.s_U;
-  auto& s_tab = L.s_tab;
+  auto& s_om = L.s_om;
   auto& s_load_off = L.s_load_off;
   auto& s_off = L.s_off;
   auto& s_sum = L.s_sum;
@@ -344,13 +343,13 @@ __device__ __forceinline__ void run(const Args& a, unsigned char* dyn, Lds& L) {
     s_run[i] = 0u;
     s_drun[i] = 0u;
   }
-  for (int i = tid; i < (MAX_R + 1) * MAX_N; i += NT) s_U[i] = 0u;
-  for (int i = tid; i < 2 * 4 * MAX_N; i += NT) s_tab[i] = 0u;
+  for (int i = tid; i < 2 * MAX_N * OM_W; i += NT) s_om[i] = 0ull;
   if (tid < MAX_N) {
     s_inp[tid] = 0;
     s_sec[tid] = 0;
     s_active[tid] = 0;
     s_load0[tid] = 0u;
+    s_U[tid] = 0u;
     s_load_off[tid] = 0ull;
   }
   if (tid < 4) s_sum[tid] = 0ull;
@@ -580,9 +579,20 @@ __device__ __forceinline__ void run(const Args& a, unsigned char* dyn, Lds& L) {
         if (q < R && ((aw >> (c & 63)) & 1u) && !held) cand |= 1u << q;
       }
     }
+    // Admission of a round's offers to expert c: in token order, while the
+    // running weight stays within the capacity left.  Weights are
+    // non-negative, so the running weight never falls: the admitted offers
+    // are the ones before the first refusal, and lane c of the walker waves
+    // (threads below N) takes the set bits of c's offer mask lowest first
+    // and stops there.  It keeps c's capacity left in a register across
+    // rounds, writes the admitted bits back over the mask and clears the
+    // other parity's mask for the next round.
+    int32_t rem = 0;
+    uint32_t placed_w = 0;
+    if (tid < N) rem = s_cap[tid] - static_cast<int32_t>(s_load0[tid]);
     // ONE: every expert in one group (no group test, no division).  The
     // rounds are unrolled, so the candidate of round r and the earlier
-    // rounds' admissions are static register and LDS indices.
+    // rounds' admissions are static register indices.
     auto rounds = [&](auto one_tag) {
       constexpr bool ONE = decltype(one_tag)::value;
       int fbg[MR], cg[MK];  // expert groups, up front
@@ -598,10 +608,8 @@ __device__ __forceinline__ void run(const Args& a, unsigned char* dyn, Lds& L) {
         bool offer = false;
         const int c = fbr[r - 1];
         int s0 = 0;
-        uint32_t* tab = s_tab + (r & 1) * 4 * MAX_N;
-        const uint32_t tag = static_cast<uint32_t>(r) << TAG_SHIFT;
-        uint32_t local = 0;
-        if (wave < tw) {  // uniform: waves without tokens only meet the barrier
+        unsigned long long* om = s_om + (r & 1) * MAX_N * OM_W;
+        if (wave < tw) {  // uniform: waves without tokens only meet the barriers
           if (tok && over && ((cand >> (r - 1)) & 1u)) {
             s0 = __builtin_ctz(over);
             bool held = false;
@@ -617,31 +625,12 @@ __device__ __forceinline__ void run(const Args& a, unsigned char* dyn, Lds& L) {
             }
             offer = !held && same_group;
           }
-          // running weight of this wave's offers to each expert, in token
-          // order, and the last offering lane of each expert
-          const uint64_t om = __ballot(offer);
-          bool last = false;
-          if (om != 0ull && __popcll(om) <= 8) {
-            // few offers: one step per offering lane
-            for (uint64_t m = om; m; m &= m - 1) {
-              const int j = __builtin_ctzll(m);
-              const int cj = __builtin_amdgcn_readlane(c, j);
-              const uint32_t wj = static_cast<uint32_t>(__builtin_amdgcn_readlane(wq, j));
-              const bool same = offer && c == cj;
-              if (same && j <= lane) local += wj;
-              if (same) last = j == lane;
-            }
-          } else if (om != 0ull) {
-            const uint64_t peers = match_any(c, offer, a.nbits);
-            local = peer_prefix(peers, offer, static_cast<uint32_t>(wq));
-            last = lane == 63 - __clzll(static_cast<long long>(peers));
-          }
-          if (offer && last) tab[wave * MAX_N + c] = tag | local;
+          if (offer) atomicOr(&om[c * OM_W + (tid >> 6)], 1ull << (tid & 63));
           // this wave's pending flag for round r (parity slot)
           const bool pend = __ballot(over != 0u && (cand >> (r - 1)) != 0u) != 0ull;
           if (lane == 0) s_pend[(r & 1) * 4 + wave] = pend;
         }
-        // publishes the table and the flags: stop once no token has an
+        // publishes the masks and the flags: stop once no token has an
         // unplaced overflowed slot (no later round could offer anything)
         __syncthreads();
         bool any = false;
@@ -653,35 +642,48 @@ __device__ __forceinline__ void run(const Args& a, unsigned char* dyn, Lds& L) {
           for (int v = 0; v < 4; ++v) any |= v < tw && pv[v] != 0;
         }
         if (!any) break;
-        if (offer) {
-          // every read of the round at once: the other token waves' totals,
-          // the capacity, round 0's load and the earlier rounds' admissions
-          uint32_t x[3], u[MR];
+        if (tid < N) {
+          unsigned long long m[OM_W];
 #pragma unroll
-          for (int v = 0; v < 3; ++v) x[v] = tab[v * MAX_N + c];
-          const int32_t cap = s_cap[c], l0 = static_cast<int32_t>(s_load0[c]);
+          for (int w = 0; w < OM_W; ++w) m[w] = om[tid * OM_W + w];
 #pragma unroll
-          for (int q = 1; q < MR; ++q)
-            if (q < r) u[q] = s_U[q * MAX_N + c];
-          uint32_t base = 0;
-#pragma unroll
-          for (int v = 0; v < 3; ++v)
-            if (v < wave && v < tw && (x[v] & ~VAL_MASK) == tag) base += x[v] & VAL_MASK;
-          int32_t rem = cap - l0;
-#pragma unroll
-          for (int q = 1; q < MR; ++q)
-            if (q < r) rem -= static_cast<int32_t>(u[q]);
-          if (static_cast<int32_t>(base + local) <= rem) {
-#pragma unroll
-            for (int s = 0; s < MK; ++s)
-              if (s == s0) {
-                cur[s] = c;
-                if constexpr (!ONE) cg[s] = fbg[r - 1];
-              }
-            over &= ~(1u << s0);
-            placed |= 1u << s0;
-            atomicAdd(&s_U[r * MAX_N + c], static_cast<uint32_t>(wq));
+          for (int w = 0; w < OM_W; ++w) {  // both halves held, as pin() does
+            uint32_t lo = static_cast<uint32_t>(m[w]), hi = static_cast<uint32_t>(m[w] >> 32);
+            asm volatile("" : "+v"(lo), "+v"(hi));
+            m[w] = (static_cast<unsigned long long>(hi) << 32) | lo;
           }
+          uint32_t run = 0;
+          bool stop = false;
+#pragma unroll
+          for (int w = 0; w < OM_W; ++w) {
+            unsigned long long left = m[w], adm = 0ull;
+            while (left != 0ull && !stop) {
+              const int b = __builtin_ctzll(left);
+              const uint32_t x = static_cast<uint32_t>(s_wq[w * 64 + b]);
+              if (static_cast<int32_t>(run + x) <= rem) {
+                run += x;
+                adm |= 1ull << b;
+              } else {
+                stop = true;
+              }
+              left &= left - 1;
+            }
+            om[tid * OM_W + w] = adm;
+            s_om[((r + 1) & 1) * MAX_N * OM_W + tid * OM_W + w] = 0ull;
+          }
+          rem -= static_cast<int32_t>(run);
+          placed_w += run;
+        }
+        __syncthreads();  // the admitted bits
+        if (offer && ((om[c * OM_W + (tid >> 6)] >> (tid & 63)) & 1ull)) {
+#pragma unroll
+          for (int s = 0; s < MK; ++s)
+            if (s == s0) {
+              cur[s] = c;
+              if constexpr (!ONE) cg[s] = fbg[r - 1];
+            }
+          over &= ~(1u << s0);
+          placed |= 1u << s0;
         }
       }
     };
@@ -689,6 +691,7 @@ __device__ __forceinline__ void run(const Args& a, unsigned char* dyn, Lds& L) {
       rounds(std::true_type{});
     else
       rounds(std::false_type{});
+    if (tid < N) s_U[tid] = placed_w;
     if (tok) {
 #pragma unroll
       for (int s = 0; s < MK; ++s)
@@ -733,8 +736,7 @@ __device__ __forceinline__ void run(const Args& a, unsigned char* dyn, Lds& L) {
     if (tid < N) {
       int64_t l;
       if (a.cap_on) {
-        l = s_load0[tid];
-        for (int q = 1; q <= R; ++q) l += s_U[q * MAX_N + tid];
+        l = static_cast<int64_t>(s_load0[tid]) + s_U[tid];
       } else {
         l = static_cast<int64_t>(s_load_off[tid]);
       }
